@@ -1,0 +1,210 @@
+"""Attention as the pages define it, in float64 (test infrastructure only).
+
+The definition (``attention``) materialises the whole score matrix, exactly
+like the "standard attention" the [KVFA] HBM/SRAM section describes: scores
+S = Q K^T, a softmax over each row, then P V.  We add the two things the
+source pages state elsewhere: the 1/sqrt(d_head) score scale ([KPF], code in
+"Following one new token through the cache", which divides by the square root
+of the head size) and the causal mask (a query at absolute position p may see
+keys 0..p).
+
+The other functions restate the page's own algorithms so that tests can show
+they reach the definition: the single-pass online softmax ([KVFA], online
+softmax section; [KPF] worked example in "Flash attention: stop carrying
+everything back and forth"), the tiled flash loop ([KVFA], Flash Attention
+section) and the split-context merge of (m, l, O) partials, which is the same
+rescale by exp(m_old - m_new) applied across splits instead of tiles
+([KVFA], Flash Attention section; [DF], FlashAttention paragraphs).
+"""
+import math
+
+import numpy as np
+
+
+def softmax_rows(S):
+    """Row softmax of a float64 matrix: exp(S - rowmax) / rowsum.
+
+    Subtracting the row maximum before exponentiating is the standard guard
+    against overflow that [KPF] mentions in its worked example; masked entries
+    are -inf and contribute exp(-inf) = 0.
+    """
+    S = np.asarray(S, dtype=np.float64)
+    mx = np.max(S, axis=-1, keepdims=True)
+    E = np.exp(S - mx)
+    return E / np.sum(E, axis=-1, keepdims=True)
+
+
+def attention(q, k, v, scale, q_pos=None):
+    """Causal softmax attention of one head, fully materialised, float64.
+
+    q: [Tq, d] queries; k, v: [L, d] keys and values in logical order.
+    q_pos: absolute position of each query row (default: the last Tq
+    positions, i.e. L - Tq .. L - 1, which is the bottom-right alignment a
+    decode step or a whole-prompt prefill both use).  Key j is visible to a
+    query at position p iff j <= p.
+    Returns O = softmax(q k^T * scale + mask) v, shape [Tq, d].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    Tq, L = q.shape[0], k.shape[0]
+    if q_pos is None:
+        q_pos = np.arange(L - Tq, L)
+    q_pos = np.asarray(q_pos)
+    S = (q @ k.T) * scale
+    visible = np.arange(L)[None, :] <= q_pos[:, None]
+    S = np.where(visible, S, -np.inf)
+    P = softmax_rows(S)
+    return P @ v
+
+
+def gqa_attention(q, k, v, scale, q_pos=None):
+    """Grouped-query attention over all heads, float64.
+
+    q: [Tq, n_q, d]; k, v: [L, n_kv, d] with n_q a multiple of n_kv.  Query
+    head h reads key/value head h // (n_q / n_kv): the pages say only that
+    several query heads share one key/value head ([KVFA] memory-cost section;
+    [DF] architecture paragraph; [KPF] "Opening the hood"), and contiguous
+    groups are the plain reading.  Returns [Tq, n_q, d].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    n_q, n_kv = q.shape[1], k.shape[1]
+    assert n_q % n_kv == 0
+    G = n_q // n_kv
+    out = np.empty(q.shape, dtype=np.float64)
+    for h in range(n_q):
+        g = h // G
+        out[:, h, :] = attention(q[:, h, :], k[:, g, :], v[:, g, :], scale, q_pos)
+    return out
+
+
+def online_softmax_trace(scores, tile):
+    """Single pass over a row of scores in tiles, keeping (m, l).
+
+    After each tile the running maximum m grows to cover the tile and the
+    running sum l, which was measured against the old maximum, is multiplied
+    by exp(m_old - m_new) before the tile's own exp(x - m_new) terms are added
+    ([KVFA] online softmax section; [DF] running-summary paragraph).  Before
+    any tile m is -inf and l is 0, and the rescale factor of that empty state
+    is taken as 0.  Returns the list of (m, l) after each tile.
+    """
+    m, l = -math.inf, 0.0
+    trace = []
+    for s in range(0, len(scores), tile):
+        block = [float(x) for x in scores[s:s + tile]]
+        m_new = max([m] + block)
+        rescale = math.exp(m - m_new) if m != -math.inf else 0.0
+        l = l * rescale + sum(math.exp(x - m_new) for x in block)
+        m = m_new
+        trace.append((m, l))
+    return trace
+
+
+def online_softmax(scores, tile):
+    """Probabilities from the single-pass (m, l): exp(x - m) / l."""
+    m, l = online_softmax_trace(scores, tile)[-1]
+    return np.array([math.exp(float(x) - m) / l for x in scores])
+
+
+def flash_attention_tiled(q, k, v, scale, tile_q, tile_k, q_pos=None):
+    """The page's tiled flash loop for one head, with scale and causal mask.
+
+    Outer loop over query tiles, inner loop over key/value tiles; each query
+    row carries (m, l, O) and every new tile rescales l and O by
+    exp(m_old - m_new) before adding its own contribution; one division by l
+    at the end of the row tile ([KVFA], Flash Attention section).  A masked
+    score is -inf; a row whose tile is fully masked so far keeps m = -inf and
+    its rescale factor is taken as 0, the guard the online softmax section
+    uses.  Float64 throughout.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    Tq, d = q.shape
+    L = k.shape[0]
+    if q_pos is None:
+        q_pos = np.arange(L - Tq, L)
+    q_pos = np.asarray(q_pos)
+    O = np.zeros((Tq, v.shape[1]))
+    for i in range(0, Tq, tile_q):
+        Qi = q[i:i + tile_q]
+        pos_i = q_pos[i:i + tile_q]
+        m_i = np.full(Qi.shape[0], -np.inf)
+        l_i = np.zeros(Qi.shape[0])
+        O_i = np.zeros((Qi.shape[0], v.shape[1]))
+        for j in range(0, L, tile_k):
+            Kj, Vj = k[j:j + tile_k], v[j:j + tile_k]
+            S = (Qi @ Kj.T) * scale
+            cols = np.arange(j, j + Kj.shape[0])
+            S = np.where(cols[None, :] <= pos_i[:, None], S, -np.inf)
+            m_new = np.maximum(m_i, S.max(axis=1))
+            live = m_new > -np.inf
+            safe_m = np.where(live, m_new, 0.0)
+            P = np.where(live[:, None], np.exp(S - safe_m[:, None]), 0.0)
+            alpha = np.where(m_i > -np.inf, np.exp(m_i - safe_m), 0.0)
+            l_i = alpha * l_i + P.sum(axis=1)
+            O_i = alpha[:, None] * O_i + P @ Vj
+            m_i = m_new
+        O[i:i + tile_q] = O_i / l_i[:, None]
+    return O
+
+
+def split_partials(q, k, v, scale, split_len):
+    """Per-split (m, l, O) of one decode query row over its whole context.
+
+    q: [d]; k, v: [L, d].  Split s covers keys [s*split_len, (s+1)*split_len).
+    For each split: m_s = max of its scores, l_s = sum exp(score - m_s) and
+    O_s = sum exp(score - m_s) v (unnormalised), i.e. the running state the
+    online softmax holds after sweeping that split alone.
+    Returns arrays m [S], l [S], O [S, d].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    L = k.shape[0]
+    n_split = -(-L // split_len)
+    ms, ls, Os = [], [], []
+    for s in range(n_split):
+        sl = slice(s * split_len, min((s + 1) * split_len, L))
+        sc = (k[sl] @ q) * scale
+        m_s = sc.max()
+        p = np.exp(sc - m_s)
+        ms.append(m_s)
+        ls.append(p.sum())
+        Os.append(p @ v[sl])
+    return np.array(ms), np.array(ls), np.array(Os)
+
+
+def merge_partials(m, l, O):
+    """Merge split partials: M = max m_s, w_s = exp(m_s - M),
+    result = sum_s w_s O_s / sum_s w_s l_s.
+
+    Each split's state is brought to the common maximum by the same
+    exp(m_old - m_new) rescale the online softmax applies tile by tile.
+    """
+    m = np.asarray(m, dtype=np.float64)
+    M = m.max()
+    w = np.exp(m - M)
+    return (w[:, None] * np.asarray(O)).sum(axis=0) / (w * np.asarray(l)).sum()
+
+
+def decode_attention(q, k, v, scale):
+    """One decode step of one sequence: every cached row is visible.
+
+    q: [n_q, d] (the new token's queries), k, v: [L, n_kv, d] with the new
+    token's own row already appended (the cache appends before the query
+    attends, [KPF] "Following one new token through the cache").
+    Returns [n_q, d].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    return gqa_attention(q[None], k, v, scale, q_pos=[k.shape[0] - 1])[0]
+
+
+def prefill_attention(q, k, v, scale):
+    """Causal attention of a whole prompt on an empty cache.
+
+    q: [T, n_q, d]; k, v: [T, n_kv, d]; query t sees keys 0..t.
+    Returns [T, n_q, d].
+    """
+    T = np.asarray(q).shape[0]
+    return gqa_attention(q, k, v, scale, q_pos=np.arange(T))

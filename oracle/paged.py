@@ -1,0 +1,150 @@
+"""Host model of the paged KV cache, byte for byte (test infrastructure only).
+
+Allocation follows the paged-cache data structure of [KVFA] (PagedAttention
+section): HBM is cut into fixed blocks of 16 token rows; each sequence owns a
+page table listing its blocks in logical order; a new block is taken from the
+free list only when the sequence's length is a multiple of 16 before the new
+token, i.e. when its last block is full; releasing a sequence puts all of its
+blocks back on the free list; the physical place of logical position p is
+(table[p // 16], p % 16).  [KPF] ("Paged attention: stop reserving empty
+tables") describes the same block table.  The free list is the page's plain
+Python list: initially 0 .. n_blocks-1, ``pop()`` takes from the end and a
+release appends the sequence's blocks in table order.
+
+Physical layout of one layer's pools (the library's documented layout):
+  K[block][kv_head][slot 0..15][d]      (a token's d values contiguous)
+  V[block][kv_head][d][slot 0..15]      (a d-column's 16 tokens contiguous)
+  Kscale, Vscale[block][kv_head]        float32, fp8 caches only
+Stored elements are raw storage-format bit patterns.  Unwritten slots keep
+whatever was there (tests fill the pools with a poison pattern first), and
+this model keeps the same poison so whole pools can be compared.
+"""
+import numpy as np
+
+from .codecs import (bf16_bits_to_f64, e4m3_decode, f16_bits_to_f64,
+                     fp8_slab_write)
+
+BLOCK = 16
+STORAGE = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8}
+POISON = {"f32": 0xFFFFFFFF, "f16": 0xFFFF, "bf16": 0xFFFF, "fp8": 0xFF}
+
+
+class PagedCacheModel:
+    def __init__(self, n_layers, n_kv, d, dtype, n_blocks, max_seqs, max_blocks_per_seq,
+                 poison=True):
+        assert dtype in STORAGE
+        self.n_layers, self.n_kv, self.d, self.dtype = n_layers, n_kv, d, dtype
+        self.n_blocks, self.max_seqs, self.max_bps = n_blocks, max_seqs, max_blocks_per_seq
+        st = STORAGE[dtype]
+        fill = POISON[dtype] if poison else 0
+        self.K = np.full((n_layers, n_blocks, n_kv, BLOCK, d), fill, dtype=st)
+        self.V = np.full((n_layers, n_blocks, n_kv, d, BLOCK), fill, dtype=st)
+        if dtype == "fp8":
+            nanbits = np.uint32(0xFFFFFFFF) if poison else np.uint32(0)
+            self.Ks = np.full((n_layers, n_blocks, n_kv), nanbits, dtype=np.uint32).view(np.float32)
+            self.Vs = np.full((n_layers, n_blocks, n_kv), nanbits, dtype=np.uint32).view(np.float32)
+        self.free = list(range(n_blocks))
+        self.table = {}
+        self.length = {}
+
+    # ------------------------------------------------------------ allocation
+    def alloc(self, seq, n_tokens):
+        n = -(-n_tokens // BLOCK)                      # ceil-div
+        if n > len(self.free):
+            raise MemoryError("no free blocks")
+        self.table[seq] = [self.free.pop() for _ in range(n)]
+        self.length[seq] = n_tokens
+
+    def grow(self, seqs):
+        need = sum(1 for s in seqs if self.length[s] % BLOCK == 0)
+        if need > len(self.free):
+            raise MemoryError("no free blocks")
+        for s in seqs:
+            if self.length[s] % BLOCK == 0:
+                self.table[s].append(self.free.pop())
+            self.length[s] += 1
+
+    def release(self, seq):
+        self.free.extend(self.table.pop(seq))
+        del self.length[seq]
+
+    def set_table(self, seq, blocks, length):
+        """Install an explicit block list (tests use shuffled tables)."""
+        blocks = [int(b) for b in blocks]
+        assert len(blocks) == -(-length // BLOCK)
+        for b in blocks:
+            self.free.remove(b)
+        self.table[seq] = blocks
+        self.length[seq] = length
+
+    def physical(self, seq, pos):
+        return self.table[seq][pos // BLOCK], pos % BLOCK
+
+    # ---------------------------------------------------------------- writes
+    def write_rows(self, layer, seq, start, k_rows, v_rows):
+        """Store rows for positions start .. start+T-1 of one sequence.
+
+        k_rows, v_rows: [T, n_kv, d].  For 16/32-bit caches they are the
+        storage bit patterns (uint16 / uint32) and are copied bit for bit; for
+        an fp8 cache they are float32 values (bf16 inputs widened exactly) and
+        go through the per-slab scale rule, one slab write per (block, head)
+        covering all of the new rows that land in that block.
+        """
+        T = k_rows.shape[0]
+        assert start + T <= self.length[seq]
+        if self.dtype != "fp8":
+            st = STORAGE[self.dtype]
+            for i in range(T):
+                b, r = self.physical(seq, start + i)
+                self.K[layer, b, :, r, :] = np.asarray(k_rows[i]).view(st)
+                self.V[layer, b, :, :, r] = np.asarray(v_rows[i]).view(st)
+            return
+        p = start
+        while p < start + T:
+            b, r0 = self.physical(seq, p)
+            n = min(BLOCK - r0, start + T - p)
+            i0 = p - start
+            for h in range(self.n_kv):
+                kc, ks = fp8_slab_write(self.K[layer, b, h], self.Ks[layer, b, h], r0,
+                                        k_rows[i0:i0 + n, h, :])
+                self.K[layer, b, h] = kc
+                self.Ks[layer, b, h] = ks
+                vc, vs = fp8_slab_write(self.V[layer, b, h].T, self.Vs[layer, b, h], r0,
+                                        v_rows[i0:i0 + n, h, :])
+                self.V[layer, b, h] = vc.T
+                self.Vs[layer, b, h] = vs
+            p += n
+
+    # ----------------------------------------------------------------- reads
+    def _widen(self, raw):
+        if self.dtype == "f32":
+            return raw.view(np.float32).astype(np.float64)
+        if self.dtype == "f16":
+            return f16_bits_to_f64(raw)
+        if self.dtype == "bf16":
+            return bf16_bits_to_f64(raw)
+        return e4m3_decode(raw)
+
+    def logical_raw(self, layer, seq, start=0, count=None):
+        """Stored bit patterns of rows start..start+count-1: K, V [count, n_kv, d]."""
+        L = self.length[seq]
+        count = L - start if count is None else count
+        Kr = np.empty((count, self.n_kv, self.d), dtype=self.K.dtype)
+        Vr = np.empty((count, self.n_kv, self.d), dtype=self.V.dtype)
+        for i in range(count):
+            b, r = self.physical(seq, start + i)
+            Kr[i] = self.K[layer, b, :, r, :]
+            Vr[i] = self.V[layer, b, :, :, r]
+        return Kr, Vr
+
+    def logical_values(self, layer, seq):
+        """Dequantised K, V of the whole sequence as exact float64 [L, n_kv, d]."""
+        L = self.length[seq]
+        Kr, Vr = self.logical_raw(layer, seq)
+        K, V = self._widen(Kr), self._widen(Vr)
+        if self.dtype == "fp8":
+            for i in range(L):
+                b, _ = self.physical(seq, i)
+                K[i] *= self.Ks[layer, b, :].astype(np.float64)[:, None]
+                V[i] *= self.Vs[layer, b, :].astype(np.float64)[:, None]
+        return K, V

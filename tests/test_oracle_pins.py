@@ -1,0 +1,243 @@
+"""The oracle against what the pages and the mathematics fix (CPU only)."""
+import math
+
+import numpy as np
+import pytest
+
+import pins
+from oracle import attention as A
+from oracle import codecs as C
+from oracle import sizes as Z
+from oracle.paged import PagedCacheModel
+from workloads import GPT2Small
+
+
+# ------------------------------------------------------------ online softmax
+def test_worked_example_printed_values():
+    assert pins.check_worked_example(A.online_softmax_trace)
+
+
+def test_online_softmax_every_split_point():
+    assert pins.check_online_every_split(A.online_softmax)
+
+
+# ------------------------------------------------------------ attention
+def test_prefill_matches_torch_sdpa_float64():
+    assert pins.check_prefill_vs_sdpa(A.prefill_attention)
+
+
+def test_decode_matches_torch_sdpa_float64():
+    assert pins.check_decode_vs_sdpa(A.decode_attention)
+
+
+def test_tiled_flash_loop_reaches_definition():
+    assert pins.check_tiled_equals_definition(A.flash_attention_tiled, A.attention)
+
+
+def test_split_merge_reaches_definition():
+    assert pins.check_merge_equals_definition(A.split_partials, A.merge_partials, A.attention)
+
+
+def test_cache_demo_same_outputs_and_row_counts():
+    assert pins.check_cache_demo(A.attention)
+
+
+def test_invariants():
+    assert pins.check_invariants(A.attention)
+
+
+def test_gqa_is_mha_with_repeated_kv_heads():
+    assert pins.check_gqa_is_repeated_mha(A.gqa_attention)
+
+
+def test_gpt2_small_cached_decode_equals_recompute():
+    """GPT-2-small shape, one layer: prefill 261 rows, then at every decode
+    step the cached one-row decode equals the last row of a full causal
+    recompute over the whole prefix (float64)."""
+    w = GPT2Small(n_new=12)
+    scale = 1 / math.sqrt(w.d)
+    K, V, Q = [w.k_prompt], [w.v_prompt], [w.q_prompt]
+    for (k, v, q) in w.steps:
+        K.append(k[None]); V.append(v[None]); Q.append(q[None])
+        Kc, Vc, Qc = np.concatenate(K), np.concatenate(V), np.concatenate(Q)
+        cached = A.decode_attention(q, Kc, Vc, scale)
+        recompute = A.prefill_attention(Qc, Kc, Vc, scale)[-1]
+        assert np.allclose(cached, recompute, rtol=0, atol=1e-12)
+    n_total = w.prompt_len + len(w.steps)
+    assert Z.naive_prefix_rows(w.prompt_len + 1, len(w.steps)) == sum(range(262, n_total + 1))
+
+
+def test_gpt2_small_operation_counts():
+    """Full recompute over 200 decode steps after a 261-token prompt touches
+    262 + ... + 461 rows; the cache touches one row per step."""
+    assert Z.naive_prefix_rows(262, 200) == 72300
+    assert Z.cached_prefix_rows(261, 200) == 461
+
+
+# ------------------------------------------------------------ closed forms
+def test_bytes_per_token_closed_form():
+    g = pins.golden("closed_forms.json")
+    for case in g["bytes_per_token"]:
+        assert Z.kv_bytes_per_token(case["n_layers"], case["n_kv_heads"], case["d_head"],
+                                    case["bytes"]) == case["expected"], case["source"]
+
+
+def test_gb_table_at_32000_tokens():
+    g = pins.golden("closed_forms.json")["gb_at_32000_tokens"]
+    for row in g["gqa"]:
+        gib = Z.gqa_kv_bytes(32_000, row["n_layers"], row["n_kv_heads"], row["d_head"]) / 1024 ** 3
+        if "formula_gives" in row:
+            assert round(gib, 2) == row["formula_gives"] and row["printed"] != row["formula_gives"]
+        else:
+            assert round(gib, 2) == row["printed"], row["model"]
+    for row in g["mla"]:
+        gib = Z.mla_kv_bytes(32_000, row["n_layers"], row["kv_lora_rank"], row["qk_rope_dim"]) / 1024 ** 3
+        # the printed 2.10 is the formula's 2.094 rounded up; the formula is pinned
+        assert round(gib, 2) == 2.09 and abs(gib - row["printed"]) < 0.01
+
+
+def test_triangular_counts():
+    for case in pins.golden("closed_forms.json")["triangular"]:
+        n = Z.naive_attention_rows(case["n"])
+        if "expected" in case:
+            assert n == case["expected"]
+        elif "at_least" in case:
+            assert n > case["at_least"] and n == 8_390_656
+        else:
+            assert abs(n - case["about"]) <= case["rel_tol"] * case["about"]
+
+
+def test_prefix_row_counts():
+    g = pins.golden("closed_forms.json")["prefix_rows"]
+    naive = Z.naive_prefix_rows(g["prompt"], g["n_new"])
+    cached = Z.cached_prefix_rows(g["prompt"], g["n_new"])
+    assert naive == 219_900 and abs(naive - g["naive_about"]) / g["naive_about"] < 0.01
+    assert cached == g["cached"]
+    assert abs(naive / cached - g["ratio_about"]) / g["ratio_about"] < 0.05
+
+
+def test_other_printed_sizes():
+    cases = pins.golden("closed_forms.json")["other_sizes"]
+    conv = cases[0]
+    assert abs(conv["tokens"] * conv["bytes_per_token"] / 2 ** 20 - conv["about_mb"]) \
+        <= conv["rel_tol"] * conv["about_mb"]
+    res = cases[1]
+    assert res["tokens"] * res["bytes_per_token"] == res["gib"] * 2 ** 30
+    fit = cases[2]
+    assert int(fit["budget_gib"] * 1e9 // (fit["tokens"] * fit["bytes_per_token"])) == fit["about_count"]
+    big = cases[3]
+    bpt = Z.kv_bytes_per_token(big["n_layers"], big["n_kv_heads"], big["d_head"], big["bytes"])
+    for c in big["cases"]:
+        assert bpt * c["tokens"] / 2 ** 30 == c["about_gib"]
+    assert Z.kv_bytes_per_token(80, 8, 128, 2) == cases[4]["ratio"] * Z.kv_bytes_per_token(80, 8, 128, 1)
+    grid = cases[5]
+    assert abs(grid["n"] ** 2 * grid["bytes"] / 1e9 - grid["about_gb"]) < 0.05
+
+
+# ------------------------------------------------------------ codecs
+def test_e4m3_table():
+    assert pins.check_e4m3_table(C.E4M3_TABLE)
+
+
+def test_e4m3_encode_equals_brute_force_nearest():
+    assert pins.check_e4m3_encode_brute(C.e4m3_encode, C.E4M3_TABLE)
+
+
+def test_e4m3_encode_equals_torch_cast_within_range():
+    assert pins.check_e4m3_encode_torch(C.e4m3_encode, C.E4M3_TABLE)
+
+
+def test_e4m3_roundtrip_every_code():
+    assert pins.check_e4m3_roundtrip(C.e4m3_encode, C.E4M3_TABLE)
+
+
+def test_e4m3_saturates():
+    assert list(C.e4m3_encode([448.0, 449.0, 1e30, -1e30])) == [0x7E, 0x7E, 0x7E, 0xFE]
+
+
+def test_bf16_rounding_equals_torch():
+    assert pins.check_bf16_vs_torch(C.bf16_bits_from_f32)
+
+
+def test_f16_rounding_equals_torch():
+    import torch
+    x = np.random.default_rng(9).standard_normal(5000).astype(np.float32) * 100
+    t = torch.from_numpy(x).half().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(C.f16_bits_from_f32(x), t)
+
+
+def _slab_error_ok(codes, scale, rows, n_requant):
+    """Every decoded element is within (n_requant + 1) fp8 roundings of its
+    source value: half a unit in the last place is 2^-4 of the magnitude for
+    normal codes and 2^-10 of the scale for subnormal ones."""
+    dec = C.e4m3_decode(codes[:rows.shape[0]]) * float(scale)
+    bound = (n_requant + 1) * (2.0 ** -4 * np.abs(rows) + 2.0 ** -10 * float(scale)) * (1 + 1e-6)
+    return bool(np.all(np.abs(dec - rows) <= bound + 1e-30))
+
+
+def test_fp8_slab_rule_scale_invariant_and_error_bound():
+    rng = np.random.default_rng(10)
+    d = 32
+    for trial in range(20):
+        rows = (rng.standard_normal((16, d)) * rng.choice([0.01, 1, 50], size=(16, 1))).astype(np.float32)
+        codes = np.full((16, d), 0xFF, dtype=np.uint8)
+        scale = np.float32(np.nan)
+        n_req = 0
+        for r in range(16):
+            old = scale
+            codes, scale = C.fp8_slab_write(codes, scale, r, rows[r:r + 1])
+            if r > 0 and scale > old:
+                n_req += 1
+            amax = np.float32(np.abs(rows[:r + 1]).max())
+            assert scale == np.float32(amax / np.float32(448))
+            assert np.all(codes[r + 1:] == 0xFF)          # untouched rows keep their bytes
+            assert _slab_error_ok(codes, scale, rows[:r + 1].astype(np.float64), n_req)
+
+
+def test_fp8_slab_bulk_equals_single_encode():
+    rows = np.random.default_rng(11).standard_normal((16, 8)).astype(np.float32)
+    codes, s = C.fp8_slab_write(np.zeros((16, 8), np.uint8), np.float32(0), 0, rows)
+    assert s == np.float32(np.abs(rows).max() / np.float32(448))
+    assert np.array_equal(codes, C.e4m3_encode((rows / s).astype(np.float32)))
+
+
+def test_fp8_slab_all_zero_rows():
+    codes, s = C.fp8_slab_write(np.zeros((16, 4), np.uint8), np.float32(5), 0,
+                                np.array([[0.0, -0.0, 0.0, 0.0]], np.float32))
+    assert s == 0 and list(codes[0]) == [0x00, 0x80, 0x00, 0x00]
+    codes, s = C.fp8_slab_write(codes, s, 1, np.array([[1.0, 2.0, -448.0, 0.0]], np.float32))
+    assert s == np.float32(1.0) and list(codes[0]) == [0x00, 0x80, 0x00, 0x00]
+
+
+# ------------------------------------------------------------ paged model
+def test_paged_allocation_follows_the_page_listing():
+    m = PagedCacheModel(1, 1, 4, "bf16", n_blocks=10, max_seqs=4, max_blocks_per_seq=8)
+    m.alloc(0, 17)                                  # ceil(17/16) = 2 blocks, popped from the end
+    assert m.table[0] == [9, 8] and m.length[0] == 17
+    m.alloc(1, 16)
+    assert m.table[1] == [7]
+    m.grow([1])                                     # 16 % 16 == 0: a new block
+    assert m.table[1] == [7, 6] and m.length[1] == 17
+    m.grow([0, 1])                                  # neither crosses a boundary
+    assert m.table[0] == [9, 8] and m.table[1] == [7, 6]
+    assert m.physical(0, 17) == (8, 1) and m.physical(1, 0) == (7, 0)
+    m.release(0)
+    assert m.free == [0, 1, 2, 3, 4, 5, 9, 8]
+    owned = set(b for t in m.table.values() for b in t)
+    assert not owned & set(m.free) and len(owned) + len(m.free) == 10
+    with pytest.raises(MemoryError):
+        m.alloc(2, 16 * 9)
+    assert len(m.free) == 8                         # a failed allocation changes nothing
+
+
+def test_paged_model_bit_copy_and_layout():
+    m = PagedCacheModel(2, 2, 4, "bf16", n_blocks=4, max_seqs=2, max_blocks_per_seq=4)
+    m.set_table(0, [3, 1], 20)
+    k = np.arange(20 * 2 * 4, dtype=np.uint16).reshape(20, 2, 4)
+    v = k + 1000
+    m.write_rows(1, 0, 0, k, v)
+    assert np.array_equal(m.K[1, 1, 1, 3, :], k[19, 1])     # position 19 -> block 1, slot 3
+    assert np.array_equal(m.V[1, 3, 0, :, 5], v[5, 0])      # V slabs are [d][slot]
+    kr, vr = m.logical_raw(1, 0)
+    assert np.array_equal(kr, k) and np.array_equal(vr, v)
+    assert np.all(m.K[0] == 0xFFFF) and np.all(m.K[1, 1, :, 4:] == 0xFFFF)
