@@ -1,0 +1,318 @@
+"""Benchmark of the paged-KV-cache attention path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+Default workload: the Llama-3-8B-shaped decode step -- 40 sequences, 32 query
+and 8 kv heads of 128, bf16 cache in 16-token blocks behind shuffled block
+tables, context lengths uniform in [512, 4096].  One step is one pass of the
+decode hot path over that batch: grow every sequence by one token (host
+allocator + table update), kv_append of the new K/V rows, then attn_decode
+(split-context partials and their (m, l) merge).  The headline `value` is
+the decode's algorithmic HBM bytes per step (K/V rows read through the
+tables, queries, outputs, table entries) divided by the wall-clock time per
+step.  The same JSON line carries a `prefill` object for the causal-prefill
+workload (4 x 8,192 tokens, 32/8 heads of 128, bf16), whose metric is
+algorithmic TFLOP/s.
+
+`roofline` is measured for the dominant call of each workload with HIP
+events recorded on the stream the library launches on, over the timed
+launches; `cpu_baseline` times the float64 oracle on a bounded sample of the
+same workload on this host's cores.  Inputs are synthetic and seeded.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2516.6
+METRIC = "decode attn HBM GB/s (% of peak) + prefill attn TFLOP/s (% MFMA peak)"
+
+
+def cpu_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count()
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 0) for p in threadpool_info()] or [0])
+    except Exception:
+        return None
+
+
+# ---------------------------------------------------------------- decode
+def build_decode(name, torch, kv):
+    from workloads import decode_workload
+    w = decode_workload(name)
+    dt = {"bf16": "bf16", "fp16": "f16", "fp8": "fp8"}[w.kv_dtype]
+    io = kv.IO_TORCH[dt]
+    spare = w.batch * 8                                     # room to grow during the run
+    max_bps = int(w.blocks_per_seq.max()) + 8
+    c = kv.KvCache(1, w.n_q, w.n_kv, w.d, w.n_blocks + spare, w.batch, max_bps, dt)
+    tables = w.block_tables()
+    for b in range(w.batch):
+        c.set_block_table(b, tables[b], int(w.lengths[b]))
+    for b in range(w.batch):
+        L = int(w.lengths[b])
+        sel = torch.tensor([b], dtype=torch.int32, device="cuda")
+        for s0 in range(0, L, 8192):
+            n = min(8192, L - s0)
+            k, v = w.kv_rows(b, s0, n)
+            c.write(0, sel, s0, torch.from_numpy(k).to(io).cuda()[None],
+                    torch.from_numpy(v).to(io).cuda()[None])
+    torch.cuda.synchronize()
+    return w, c, io
+
+
+def decode_bytes(w, lengths, kv_elem):
+    """Algorithmic HBM bytes of one decode call: every valid K and V row once
+    (per kv head), the query and output rows, one table entry per block, and
+    for fp8 the two scales per block and kv head."""
+    rows = int(np.sum(lengths))
+    kvb = 2 * rows * w.n_kv * w.d * kv_elem
+    qo = 2 * w.batch * w.n_q * w.d * 2
+    blocks = int(np.sum(-(-np.asarray(lengths) // 16)))
+    tab = blocks * 4
+    sc = 2 * blocks * w.n_kv * 4 if kv_elem == 1 else 0
+    return kvb + qo + tab + sc
+
+
+def bench_decode(name, steps, warmup, torch, kv, with_cpu):
+    w, c, io = build_decode(name, torch, kv)
+    kv_elem = 1 if w.kv_dtype == "fp8" else 2
+    seqs_host = list(range(w.batch))
+    seqs = torch.arange(w.batch, dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(123)
+    q = torch.from_numpy(w.q()).to(io).cuda()
+    knew = torch.from_numpy(rng.standard_normal((w.batch, w.n_kv, w.d), dtype=np.float32)).to(io).cuda()
+    vnew = torch.from_numpy(rng.standard_normal((w.batch, w.n_kv, w.d), dtype=np.float32)).to(io).cuda()
+    out = torch.empty((w.batch, w.n_q, w.d), dtype=io, device="cuda")
+    max_len = int(w.lengths.max()) + warmup + steps + 1
+    # workspace for the longest context the run reaches
+    ws_bytes = w.batch * w.n_q * (max_len // 64 + 2) * (w.d + 2) * 4
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        c.seq_grow(seqs_host)
+        c.append(0, seqs, knew, vnew)
+        if ev is not None:
+            ev[0].record(stream)
+        c.attn_decode(0, seqs, q, out=out, ws=ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    lens0 = np.array([c.seq_len(b) for b in range(w.batch)])
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # algorithmic bytes of each timed decode: lengths lens0+1 .. lens0+steps
+    total_bytes = sum(decode_bytes(w, lens0 + i + 1, kv_elem) for i in range(steps))
+    kern_ms = [a.elapsed_time(b) for a, b in events]
+    kern_avg_s = float(np.mean(kern_ms)) / 1e3
+    per_call = total_bytes / steps
+    achieved = per_call / kern_avg_s / 1e9
+    res = {
+        "workload": name,
+        "value": total_bytes / wall / 1e9,
+        "ms_per_step": wall / steps * 1e3,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "kvc_attn_decode (split partial + merge)",
+                     "avg_call_us": kern_avg_s * 1e6, "bytes_per_call": per_call},
+        "shape": {"batch": w.batch, "n_q": w.n_q, "n_kv": w.n_kv, "d": w.d,
+                  "kv_dtype": w.kv_dtype, "mean_len": float(np.mean(lens0 + 1))},
+    }
+    if with_cpu:
+        res["cpu_baseline"] = cpu_decode(w, q, kv_elem, torch)
+    return res
+
+
+def cpu_decode(w, q, kv_elem, torch, budget_s=12.0):
+    """Time the float64 oracle's decode on whole sequences of the workload
+    until the budget is used; report the same algorithmic bytes per second.
+    Inputs (the cached rows rounded to the storage type, widened to float64)
+    are prepared outside the timed region."""
+    from oracle import attention as A
+    io = q.dtype
+    scale = 1.0 / math.sqrt(w.d)
+    qd = q.detach().cpu().double().numpy()
+    done_bytes, spent, nseq = 0, 0.0, 0
+    for b in range(w.batch):
+        L = int(w.lengths[b])
+        k, v = w.kv_rows(b, 0, L)
+        K = torch.from_numpy(k).to(io).double().numpy()
+        V = torch.from_numpy(v).to(io).double().numpy()
+        t0 = time.perf_counter()
+        A.decode_attention(qd[b], K, V, scale)
+        spent += time.perf_counter() - t0
+        rows = L
+        done_bytes += 2 * rows * w.n_kv * w.d * kv_elem + 2 * w.n_q * w.d * 2 + (-(-L // 16)) * 4
+        nseq += 1
+        if spent >= budget_s:
+            break
+    return {"value": done_bytes / spent / 1e9, "unit": "GB/s", "cores": cpu_cores(),
+            "blas_threads": blas_threads(), "kind": "oracle",
+            "sample": f"float64 oracle decode of {nseq} of {w.batch} sequences "
+                      f"({spent:.1f} s)"}
+
+
+# ---------------------------------------------------------------- prefill
+def prefill_flops(batch, T, n_q, d):
+    """Causal attention FLOPs: per (sequence, head) 2*d multiply-adds for QK^T
+    and 2*d for PV over the T(T+1)/2 visible (query, key) pairs."""
+    return batch * n_q * 4 * d * T * (T + 1) // 2
+
+
+def bench_prefill(steps, warmup, torch, kv, with_cpu, small=False):
+    from workloads import prefill_workload
+    w = prefill_workload(small=small)
+    qn, kn, vn = w.qkv()
+    q, k, v = (torch.from_numpy(a).to(torch.bfloat16).cuda() for a in (qn, kn, vn))
+    del qn, kn, vn
+    nb = -(-w.T // 16)
+    c = kv.KvCache(1, w.n_q, w.n_kv, w.d, w.batch * nb, w.batch, nb, "bf16")
+    seqs = torch.arange(w.batch, dtype=torch.int32, device="cuda")
+    for b in range(w.batch):
+        c.seq_alloc(b, w.T)
+    out = torch.empty((w.batch, w.T, w.n_q, w.d), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        c.attn_prefill(0, q, k, v, seqs=seqs, out=out)
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        events[i][0].record(stream)
+        c.attn_prefill(0, q, k, v, seqs=seqs, out=out)
+        events[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    flops = prefill_flops(w.batch, w.T, w.n_q, w.d)
+    call_s = float(np.mean([a.elapsed_time(b) for a, b in events])) / 1e3
+    achieved = flops / call_s / 1e12
+    res = {
+        "workload": "llama8b_prefill" if not small else "llama8b_prefill_small",
+        "value": flops * steps / wall / 1e12, "unit": "TFLOP/s",
+        "ms_per_step": wall / steps * 1e3,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "kvc_attn_prefill (K/V append + causal attention)",
+                     "avg_call_us": call_s * 1e6, "flops_per_call": flops},
+        "shape": {"batch": w.batch, "T": w.T, "n_q": w.n_q, "n_kv": w.n_kv, "d": w.d},
+    }
+    if with_cpu:
+        res["cpu_baseline"] = cpu_prefill(w, q, k, v, torch)
+    return res
+
+
+def cpu_prefill(w, q, k, v, torch, budget_s=12.0):
+    """The float64 oracle's causal attention, one (sequence, query head) at a
+    time, until the budget is used; reported as algorithmic TFLOP/s."""
+    from oracle import attention as A
+    scale = 1.0 / math.sqrt(w.d)
+    G = w.n_q // w.n_kv
+    spent, heads = 0.0, 0
+    for b in range(w.batch):
+        for h in range(w.n_q):
+            qh = q[b, :, h].double().cpu().numpy()
+            kh = k[b, :, h // G].double().cpu().numpy()
+            vh = v[b, :, h // G].double().cpu().numpy()
+            t0 = time.perf_counter()
+            A.attention(qh, kh, vh, scale, q_pos=np.arange(w.T))
+            spent += time.perf_counter() - t0
+            heads += 1
+            if spent >= budget_s:
+                break
+        if spent >= budget_s:
+            break
+    flops = heads * 4 * w.d * w.T * (w.T + 1) // 2
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": cpu_cores(),
+            "blas_threads": blas_threads(), "kind": "oracle",
+            "sample": f"float64 oracle causal attention of {heads} of {w.batch * w.n_q} "
+                      f"(sequence, head) pairs ({spent:.1f} s)"}
+
+
+DECODE_WORKLOADS = {
+    "llama8b_decode": "40 sequences, 32 q / 8 kv heads, d 128, bf16 cache, 16-token blocks, "
+                      "shuffled tables, lengths uniform in [512, 4096]; grow + kv_append + decode",
+    "llama70b_decode_bf16": "8 x 32,768-token contexts, 64 q / 8 kv heads, d 128, bf16 cache, "
+                            "1% outliers x8",
+    "llama70b_decode_fp8": "8 x 32,768-token contexts, 64 q / 8 kv heads, d 128, fp8-e4m3 cache "
+                           "with per-block scales, 1% outliers x8",
+    "long_mha_decode": "1 x 128,000-token context, 32 / 32 heads, d 128, fp16 cache, "
+                       "split-context decode",
+}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama8b_decode",
+                    choices=sorted(DECODE_WORKLOADS) + ["llama8b_prefill"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="headline decode only (no prefill section)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(the work shards into independent per-GPU units; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kv_cache_flashattention_amd as kv
+    kv.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    with_cpu = not args.no_cpu
+
+    if args.workload == "llama8b_prefill":
+        pf = bench_prefill(args.steps, args.warmup, torch, kv, with_cpu)
+        line = {"metric": METRIC, "value": pf["value"], "unit": "TFLOP/s", "n_gpus": 1,
+                "steps": args.steps, "warmup": args.warmup, "ms_per_step": pf["ms_per_step"],
+                "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                "dtype": "bf16", "data": "synthetic (seeded N(0,1))",
+                "config": {"workload": "llama8b_prefill: 4 x 8,192 tokens, 32 q / 8 kv heads, "
+                                       "d 128, bf16, causal, K/V appended to the paged cache"},
+                "roofline": pf["roofline"], "cpu_baseline": pf.get("cpu_baseline")}
+        print(json.dumps(line))
+        return
+
+    dec = bench_decode(args.workload, args.steps, args.warmup, torch, kv, with_cpu)
+    dtype = {"bf16": "bf16", "fp16": "f16", "fp8": "fp8-e4m3 (bf16 q/o)"}[dec["shape"]["kv_dtype"]]
+    line = {"metric": METRIC, "value": dec["value"], "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": dec["ms_per_step"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": dtype, "data": "synthetic (seeded N(0,1))",
+            "config": {"workload": f"{args.workload}: {DECODE_WORKLOADS[args.workload]}",
+                       "mean_context": dec["shape"]["mean_len"]},
+            "roofline": dec["roofline"], "cpu_baseline": dec.get("cpu_baseline")}
+    if args.workload == "llama8b_decode" and not args.no_prefill:
+        line["prefill"] = bench_prefill(max(3, args.steps // 4), 1, torch, kv, with_cpu)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

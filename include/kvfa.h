@@ -1,0 +1,218 @@
+/*
+ * kvfa -- paged KV cache and exact causal softmax attention for AMD MI355X
+ * (gfx950).  C ABI.
+ *
+ * What is computed.  Decoder attention against a growing key/value cache:
+ * each layer keeps one K row and one V row per kv head for every token seen
+ * so far, a new token appends its own rows, and its query then attends over
+ * all rows of its sequence ("KV Cache & Flash Attention." (kvcache-7e2),
+ * KV cache section; "KV Cache & FlashAttention" (deepforge), first section;
+ * "KV cache, paged, flash and sparse attention" (abhishekpatel), "Following
+ * one new token through the cache").  The attention is the exact
+ * softmax(q K^T * scale) V with a causal mask, evaluated tile by tile with the
+ * online softmax (running max m, running sum l, rescale by exp(m_old-m_new))
+ * so the score matrix never reaches device memory (kvcache-7e2, Flash
+ * Attention and online softmax sections).  Query head h reads kv head
+ * h / (n_q_heads / n_kv_heads) (grouped-query attention, kvcache-7e2
+ * memory-cost section).
+ *
+ * Paged storage (kvcache-7e2, PagedAttention section; abhishekpatel, "Paged
+ * attention: stop reserving empty tables").  Each layer's K and V live in
+ * pools of fixed 16-token blocks; every sequence has a block table listing
+ * its blocks in logical order, so logical position p lives in block
+ * table[p / 16], slot p % 16.  Blocks come from a free list and go back to
+ * it when a sequence is released.  Physical layout of the caller-owned pools
+ * (elements of the storage type, row-major, innermost last):
+ *
+ *   k_pool  [n_layers][n_blocks][n_kv_heads][16][d_head]
+ *   v_pool  [n_layers][n_blocks][n_kv_heads][d_head][16]   (slot innermost)
+ *   k_scale, v_scale [n_layers][n_blocks][n_kv_heads]  float, fp8 only
+ *   block_table [max_seqs][max_blocks_per_seq]  int32, -1 where unused
+ *   seq_len     [max_seqs]                       int32 tokens stored
+ *
+ * Storage types.  f32, f16, bf16: K/V rows are stored bit for bit.  fp8: the
+ * OCP E4M3FN format (max 448, round to nearest even, saturating), one float
+ * scale per (layer, block, kv head) for K and one for V, equal to
+ * absmax/448 over the rows written so far to that block (0 for an all-zero
+ * block); a code holds round(x / scale); when a new row raises the absmax of
+ * a partly filled block, the rows already there are re-encoded as
+ * encode(fl(decode(code) * s_old) / s_new), all in IEEE float32.  Queries and
+ * outputs use the storage type, except that an fp8 cache takes bf16 queries,
+ * keys, values and outputs ("io type").
+ *
+ * Conventions.  Every function returns KVC_OK (0) or a negative status and
+ * never throws; kvc_last_error() gives a message for the calling thread.
+ * The caller owns all device memory (pools, tables, inputs, outputs,
+ * workspace) and all streams; a handle owns only host metadata.  Pointers
+ * named *_dev are device pointers, *_host host pointers.  Work is enqueued
+ * asynchronously on the given stream (0 = the default stream); argument
+ * errors are detected before anything is enqueued, launch failures give
+ * KVC_E_HIP, and faults inside kernels surface at the caller's next
+ * synchronisation.  A handle is not thread-safe.  Sequence ids passed in
+ * device arrays are checked by the kernels themselves: an id outside
+ * [0, max_seqs), a length of zero or beyond the table, or a block id outside
+ * the pool makes the kernel skip that entry (attention rows come back NaN,
+ * cache writes are not made); the kernels never read or write outside the
+ * buffers they are given.
+ */
+#ifndef KVFA_H
+#define KVFA_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status */
+#define KVC_OK             0
+#define KVC_E_INVAL       -1  /* null or out-of-range argument                         */
+#define KVC_E_UNSUPPORTED -2  /* d_head not 64/128, n_q % n_kv != 0, block != 16, ...  */
+#define KVC_E_NO_BLOCKS   -3  /* free list too short; nothing was changed               */
+#define KVC_E_STATE       -4  /* unknown/released/live sequence, host-only handle, ...  */
+#define KVC_E_WORKSPACE   -5  /* workspace smaller than kvc_decode_workspace_bytes      */
+#define KVC_E_HIP         -6  /* a HIP launch or runtime call failed                    */
+
+typedef enum kvc_dtype {
+  KVC_F32 = 0,
+  KVC_F16 = 1,
+  KVC_BF16 = 2,
+  KVC_FP8_E4M3FN = 3
+} kvc_dtype;
+
+typedef struct kvc_config {
+  int32_t n_layers;           /* >= 1                                              */
+  int32_t n_q_heads;          /* multiple of n_kv_heads                            */
+  int32_t n_kv_heads;         /* >= 1 (1 = multi-query attention)                  */
+  int32_t d_head;             /* 64 or 128                                         */
+  int32_t block_size;         /* tokens per block; must be 16                      */
+  int32_t n_blocks;           /* blocks per layer pool                             */
+  int32_t max_seqs;           /* sequence ids are 0 .. max_seqs-1                  */
+  int32_t max_blocks_per_seq; /* table width; a sequence holds <= 16x this tokens  */
+  int32_t kv_dtype;           /* a kvc_dtype                                       */
+} kvc_config;
+
+typedef struct kvc_sizes {    /* bytes the caller must allocate on the device      */
+  uint64_t k_pool, v_pool, k_scale, v_scale, block_table, seq_len;
+} kvc_sizes;
+
+typedef struct kvc_buffers {  /* caller-owned device buffers, sized by kvc_sizes   */
+  void* k_pool;
+  void* v_pool;
+  float* k_scale;             /* NULL unless kv_dtype is fp8                       */
+  float* v_scale;
+  int32_t* block_table;
+  int32_t* seq_len;
+} kvc_buffers;
+
+typedef struct kvc_cache kvc_cache;
+
+/* Cache bytes per token over all layers: 2 (K and V) x n_layers x n_kv_heads
+ * x d_head x element bytes (kvcache-7e2 memory-cost section; deepforge
+ * cache-size formula; abhishekpatel "Opening the hood").  fp8 counts one
+ * byte per element; the per-block scales are not included. */
+int kvc_bytes_per_token(const kvc_config* cfg, uint64_t* out);
+
+/* Device bytes for every buffer of a cache with this configuration. */
+int kvc_required_sizes(const kvc_config* cfg, kvc_sizes* out);
+
+/* Create a cache handle over caller-allocated device buffers (kv_cache_create).
+ * All n_blocks blocks start on the free list, which is the list 0..n_blocks-1
+ * used as a stack (kvcache-7e2 PagedAttention section).  Enqueues on `stream`
+ * a fill of block_table with -1 and seq_len with 0.  dev == NULL creates a
+ * host-only handle: the allocator works, and every call that needs the device
+ * returns KVC_E_STATE. */
+int kvc_create(const kvc_config* cfg, const kvc_buffers* dev, hipStream_t stream,
+               kvc_cache** out);
+int kvc_destroy(kvc_cache* cache);
+
+/* Make `seq` live with n_tokens tokens: ceil(n_tokens / 16) blocks popped from
+ * the free list (the page's allocate).  The rows themselves are written later
+ * (kvc_write, kvc_attn_prefill).  KVC_E_STATE if seq is already live,
+ * KVC_E_NO_BLOCKS if the free list is too short (state unchanged). */
+int kvc_seq_alloc(kvc_cache* cache, int32_t seq, int32_t n_tokens, hipStream_t stream);
+
+/* Grow each of n live sequences by one token (the page's append_token): a
+ * sequence whose length is a multiple of 16 first takes one block from the
+ * free list.  Ids must be distinct.  All-or-nothing: KVC_E_NO_BLOCKS leaves
+ * every sequence as it was.  The device copy of the table and lengths is
+ * updated on `stream`. */
+int kvc_seq_grow(kvc_cache* cache, int32_t n, const int32_t* seqs_host, hipStream_t stream);
+
+/* Return all blocks of `seq` to the free list, in table order (the page's
+ * release), and mark it not live (device length 0, table entries -1). */
+int kvc_seq_release(kvc_cache* cache, int32_t seq, hipStream_t stream);
+
+/* Make `seq` live with an explicit block list (each block must be free) and
+ * length `len` (nblk must equal ceil(len/16)).  For tests and callers that
+ * manage placement themselves. */
+int kvc_set_block_table(kvc_cache* cache, int32_t seq, const int32_t* blocks_host,
+                        int32_t nblk, int32_t len, hipStream_t stream);
+
+/* Host-side queries of the handle's own state. */
+int kvc_seq_len(const kvc_cache* cache, int32_t seq, int32_t* out);
+int kvc_seq_blocks(const kvc_cache* cache, int32_t seq, int32_t* blocks_host, int32_t cap,
+                   int32_t* n_out);
+int kvc_free_blocks(const kvc_cache* cache, int32_t* out);
+
+/* kv_append: store the newest token's K and V rows of one layer for each of n
+ * sequences, at position seq_len[seq] - 1 (call kvc_seq_grow first).
+ * k_dev, v_dev: [n][n_kv_heads][d_head] in the io type.  16/32-bit caches
+ * store the bits unchanged; fp8 caches apply the scale rule above. */
+int kvc_append(kvc_cache* cache, int32_t layer, int32_t n, const int32_t* seqs_dev,
+               const void* k_dev, const void* v_dev, hipStream_t stream);
+
+/* Bulk store of T consecutive rows per sequence (prefill, population):
+ * positions start .. start+T-1 of each of n sequences, which must all lie
+ * below the sequence's length.  k_dev, v_dev: [n][T][n_kv_heads][d_head] in
+ * the io type.  For fp8 each (block, kv head) is written once with all of
+ * its new rows (the scale rule applied to the rows together). */
+int kvc_write(kvc_cache* cache, int32_t layer, int32_t n, const int32_t* seqs_dev,
+              int32_t start, int32_t T, const void* k_dev, const void* v_dev,
+              hipStream_t stream);
+
+/* attn_prefill: causal attention of whole prompts, query t seeing keys
+ * 0..t, computed tile by tile with the online softmax (kvcache-7e2 Flash
+ * Attention section; deepforge: a prompt is processed all at once and the
+ * score table never leaves on-chip memory).  q_dev [n][T][n_q_heads][d_head],
+ * k_dev, v_dev [n][T][n_kv_heads][d_head], out_dev [n][T][n_q_heads][d_head],
+ * all in the io type.  When seqs_dev is not NULL the prompt's K/V rows are
+ * also stored as positions 0..T-1 of those sequences (as kvc_write with
+ * start 0; each sequence needs length >= T).  seqs_dev == NULL: attention
+ * only.  scale is the score multiplier (1/sqrt(d_head) in the pages). */
+int kvc_attn_prefill(kvc_cache* cache, int32_t layer, int32_t n, const int32_t* seqs_dev,
+                     int32_t T, const void* q_dev, const void* k_dev, const void* v_dev,
+                     void* out_dev, float scale, hipStream_t stream);
+
+/* Workspace bytes kvc_attn_decode needs for a batch of n sequences with this
+ * num_splits (0 = automatic), given the longest live sequence of the cache
+ * at the time of the call.  0 when the plan needs no workspace. */
+int kvc_decode_workspace_bytes(const kvc_cache* cache, int32_t n, int32_t num_splits,
+                               uint64_t* out);
+
+/* attn_decode: one query row per sequence against all of its cached rows
+ * (every row visible: the newest token's own row was appended first).
+ * q_dev, out_dev: [n][n_q_heads][d_head] in the io type.  Long contexts are
+ * cut into splits swept in parallel, each keeping its own (m, l, O), and
+ * merged afterwards with weights exp(m_s - max m) -- the online softmax's
+ * rescale applied across splits.  num_splits: 0 = automatic, else the
+ * number of splits of the longest sequence.  ws_dev: caller-owned workspace
+ * of at least kvc_decode_workspace_bytes bytes (may be NULL if that is 0). */
+int kvc_attn_decode(kvc_cache* cache, int32_t layer, int32_t n, const int32_t* seqs_dev,
+                    const void* q_dev, void* out_dev, float scale, int32_t num_splits,
+                    void* ws_dev, uint64_t ws_bytes, hipStream_t stream);
+
+/* Block-table gather: copy the stored bit patterns of positions start ..
+ * start+count-1 of `seq` in logical order into k_out_dev, v_out_dev, each
+ * [count][n_kv_heads][d_head] of the storage type (fp8: raw codes). */
+int kvc_gather(const kvc_cache* cache, int32_t layer, int32_t seq, int32_t start, int32_t count,
+               void* k_out_dev, void* v_out_dev, hipStream_t stream);
+
+/* Message describing the last failure on the calling thread ("" if none). */
+const char* kvc_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVFA_H */

@@ -1,0 +1,348 @@
+// Cache maintenance kernels: table fills and updates, kv_append (one row per
+// sequence), bulk row writes (prefill / population) and the block-table
+// gather.
+//
+// Addressing follows the paged layout: logical position p of a sequence is
+// slot p % 16 of block table[p / 16] ("KV Cache & Flash Attention."
+// (kvcache-7e2), PagedAttention section).  K slabs are [16][d] (a token's
+// row contiguous), V slabs are [d][16] (one head-dimension column of the
+// block's 16 tokens contiguous), which is the order the attention kernels'
+// matrix-core operands consume.
+#include <algorithm>
+
+#include "kvfa_internal.h"
+#include "fp8_e4m3.h"
+
+namespace kvfa {
+namespace {
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+// Validates a device-side sequence entry; returns its length or -1.
+__device__ __forceinline__ int seq_length(const CacheView& cv, int seq) {
+  if (seq < 0 || seq >= cv.max_seqs) return -1;
+  int L = cv.len[seq];
+  if (L <= 0 || L > cv.max_bps * kBlock) return -1;
+  return L;
+}
+
+__device__ __forceinline__ int block_of(const CacheView& cv, int seq, int pos) {
+  int b = cv.bt[(int64_t)seq * cv.max_bps + pos / kBlock];
+  return (b < 0 || b >= cv.n_blocks) ? -1 : b;
+}
+
+// Element offset of slab (layer, block, head) in a pool.
+__device__ __forceinline__ int64_t slab_elems(const CacheView& cv, int layer, int blk, int h) {
+  return (((int64_t)layer * cv.n_blocks + blk) * cv.n_kv + h) * (int64_t)(kBlock * cv.d);
+}
+
+__device__ __forceinline__ int64_t scale_idx(const CacheView& cv, int layer, int blk, int h) {
+  return ((int64_t)layer * cv.n_blocks + blk) * cv.n_kv + h;
+}
+
+// ---------------------------------------------------------------- tables
+__global__ void k_fill_tables(CacheView cv) {
+  int64_t nbt = (int64_t)cv.max_seqs * cv.max_bps;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nbt;
+       i += (int64_t)gridDim.x * blockDim.x)
+    cv.bt[i] = -1;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < cv.max_seqs;
+       i += (int64_t)gridDim.x * blockDim.x)
+    cv.len[i] = 0;
+}
+
+__global__ void k_table_update(CacheView cv, TableUpdate u) {
+  int i = threadIdx.x;
+  if (i >= u.n) return;
+  int32_t idx = u.idx[i];
+  if (idx >= 0) {
+    if ((int64_t)idx < (int64_t)cv.max_seqs * cv.max_bps) cv.bt[idx] = u.val[i];
+  } else {
+    int32_t s = -idx - 1;
+    if (s < cv.max_seqs) cv.len[s] = u.val[i];
+  }
+}
+
+// ---------------------------------------------------------------- append
+// One wave per (sequence, kv head): the new row goes to slot (L-1) % 16 of
+// block table[(L-1) / 16].  16/32-bit storage copies the bits.
+template <typename E>
+__global__ __launch_bounds__(64) void k_append_copy(CacheView cv, int layer, const int32_t* seqs,
+                                                    const E* knew, const E* vnew) {
+  const int b = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const int seq = seqs[b];
+  const int L = seq_length(cv, seq);
+  if (L < 0) return;
+  const int pos = L - 1, slot = pos % kBlock;
+  const int blk = block_of(cv, seq, pos);
+  if (blk < 0) return;
+  const int d = cv.d;
+  const int64_t base = slab_elems(cv, layer, blk, h);
+  E* K = (E*)cv.k + base;
+  E* V = (E*)cv.v + base;
+  const E* kr = knew + ((int64_t)b * cv.n_kv + h) * d;
+  const E* vr = vnew + ((int64_t)b * cv.n_kv + h) * d;
+  for (int j = lane; j < d; j += 64) {
+    K[slot * d + j] = kr[j];
+    V[j * kBlock + slot] = vr[j];
+  }
+}
+
+// fp8 append of one slab column set.  Every lane owns the head-dimension
+// indices lane, lane+64; the slab's scale is kept equal to absmax/448 over the
+// rows written so far; when it grows, rows 0..slot-1 are re-encoded from
+// their decoded values.  `row_stride` / `col_stride` place element (r, j)
+// of the slab at r*row_stride + j*col_stride (K: d, 1; V: 1, 16).
+__device__ void fp8_append_slab(uint8_t* slab, float* scale, int slot, int d, int row_stride,
+                                int col_stride, const uint16_t* row_bf16) {
+  const int lane = threadIdx.x;
+  float x[2] = {0.f, 0.f};
+  float amax = 0.f;
+  for (int t = 0, j = lane; j < d; j += 64, ++t) {
+    x[t] = bf16_to_f32(row_bf16[j]);
+    amax = fmaxf(amax, fabsf(x[t]));
+  }
+  amax = wave_max(amax);
+  const float s_new = amax / 448.0f;
+  float s = s_new;
+  if (slot > 0) {
+    const float s_old = *scale;
+    s = fmaxf(s_old, s_new);
+    if (s > s_old) {
+      for (int r = 0; r < slot; ++r)
+        for (int j = lane; j < d; j += 64) {
+          uint8_t* p = slab + r * row_stride + j * col_stride;
+          float y = e4m3_decode(*p) * s_old;
+          *p = (uint8_t)e4m3_encode(y / s);
+        }
+    }
+  }
+  for (int t = 0, j = lane; j < d; j += 64, ++t) {
+    float y = s > 0.f ? x[t] / s : x[t];
+    slab[slot * row_stride + j * col_stride] = (uint8_t)e4m3_encode(y);
+  }
+  if (lane == 0) *scale = s;
+}
+
+__global__ __launch_bounds__(64) void k_append_fp8(CacheView cv, int layer, const int32_t* seqs,
+                                                   const uint16_t* knew, const uint16_t* vnew) {
+  const int b = blockIdx.x, h = blockIdx.y;
+  const int seq = seqs[b];
+  const int L = seq_length(cv, seq);
+  if (L < 0) return;
+  const int pos = L - 1, slot = pos % kBlock;
+  const int blk = block_of(cv, seq, pos);
+  if (blk < 0) return;
+  const int d = cv.d;
+  const int64_t base = slab_elems(cv, layer, blk, h);
+  const int64_t si = scale_idx(cv, layer, blk, h);
+  const int64_t row = ((int64_t)b * cv.n_kv + h) * d;
+  fp8_append_slab((uint8_t*)cv.k + base, cv.ks + si, slot, d, d, 1, knew + row);
+  fp8_append_slab((uint8_t*)cv.v + base, cv.vs + si, slot, d, 1, kBlock, vnew + row);
+}
+
+// ---------------------------------------------------------------- bulk write
+// One workgroup per (logical block touched, kv head, sequence) writes the
+// block's rows that fall in [start, start+T).  Input rows are
+// [n][T][n_kv][d].  The block's rows are staged in LDS so that V can be
+// written column by column in the [d][16] order.
+template <typename E>
+__global__ __launch_bounds__(256) void k_write_copy(CacheView cv, int layer, const int32_t* seqs,
+                                                    int start, int T, const E* kin, const E* vin) {
+  __shared__ E vt[kBlock * 128];
+  const int lb = start / kBlock + blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int seq = seqs[b];
+  const int L = seq_length(cv, seq);
+  if (L < 0 || start + T > L) return;
+  const int blk = block_of(cv, seq, lb * kBlock);
+  if (blk < 0) return;
+  const int d = cv.d;
+  const int p0 = max(start, lb * kBlock), p1 = min(start + T, lb * kBlock + kBlock);
+  const int64_t base = slab_elems(cv, layer, blk, h);
+  E* K = (E*)cv.k + base;
+  E* V = (E*)cv.v + base;
+  for (int i = threadIdx.x; i < (p1 - p0) * d; i += blockDim.x) {
+    const int p = p0 + i / d, j = i % d;
+    const int64_t src = (((int64_t)b * T + (p - start)) * cv.n_kv + h) * d + j;
+    K[(p % kBlock) * d + j] = kin[src];
+    vt[(p % kBlock) * d + j] = vin[src];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < d * kBlock; i += blockDim.x) {
+    const int j = i / kBlock, r = i % kBlock, p = lb * kBlock + r;
+    if (p >= p0 && p < p1) V[j * kBlock + r] = vt[r * d + j];
+  }
+}
+
+// fp8 bulk write: the new rows of a slab are encoded together with one scale
+// update (absmax over all of them), after re-encoding older rows if the
+// scale grew.
+__global__ __launch_bounds__(256) void k_write_fp8(CacheView cv, int layer, const int32_t* seqs,
+                                                   int start, int T, const uint16_t* kin,
+                                                   const uint16_t* vin) {
+  __shared__ float red[2][4];
+  const int lb = start / kBlock + blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int seq = seqs[b];
+  const int L = seq_length(cv, seq);
+  if (L < 0 || start + T > L) return;
+  const int blk = block_of(cv, seq, lb * kBlock);
+  if (blk < 0) return;
+  const int d = cv.d;
+  const int p0 = max(start, lb * kBlock), p1 = min(start + T, lb * kBlock + kBlock);
+  const int r0 = p0 - lb * kBlock, nnew = p1 - p0;
+  const int64_t base = slab_elems(cv, layer, blk, h);
+  const int64_t si = scale_idx(cv, layer, blk, h);
+  uint8_t* K = (uint8_t*)cv.k + base;
+  uint8_t* V = (uint8_t*)cv.v + base;
+  // Old scales are read by every thread before the barrier below; thread 0
+  // overwrites them only after it.
+  const float sk_old = r0 > 0 ? cv.ks[si] : 0.f, sv_old = r0 > 0 ? cv.vs[si] : 0.f;
+  float ka = 0.f, va = 0.f;
+  for (int i = threadIdx.x; i < nnew * d; i += blockDim.x) {
+    const int64_t src = (((int64_t)b * T + (p0 - start + i / d)) * cv.n_kv + h) * d + i % d;
+    ka = fmaxf(ka, fabsf(bf16_to_f32(kin[src])));
+    va = fmaxf(va, fabsf(bf16_to_f32(vin[src])));
+  }
+  ka = wave_max(ka);
+  va = wave_max(va);
+  const int w = threadIdx.x / 64;
+  if ((threadIdx.x & 63) == 0) {
+    red[0][w] = ka;
+    red[1][w] = va;
+  }
+  __syncthreads();
+  ka = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+  va = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+  float sk = ka / 448.0f, sv = va / 448.0f;
+  if (r0 > 0) {
+    const float skn = fmaxf(sk_old, sk), svn = fmaxf(sv_old, sv);
+    for (int i = threadIdx.x; i < r0 * d; i += blockDim.x) {
+      const int r = i / d, j = i % d;
+      if (skn > sk_old) {
+        uint8_t* p = K + r * d + j;
+        *p = (uint8_t)e4m3_encode((e4m3_decode(*p) * sk_old) / skn);
+      }
+      if (svn > sv_old) {
+        uint8_t* p = V + j * kBlock + r;
+        *p = (uint8_t)e4m3_encode((e4m3_decode(*p) * sv_old) / svn);
+      }
+    }
+    sk = skn;
+    sv = svn;
+  }
+  for (int i = threadIdx.x; i < nnew * d; i += blockDim.x) {
+    const int r = r0 + i / d, j = i % d;
+    const int64_t src = (((int64_t)b * T + (p0 - start + i / d)) * cv.n_kv + h) * d + j;
+    const float xk = bf16_to_f32(kin[src]), xv = bf16_to_f32(vin[src]);
+    K[r * d + j] = (uint8_t)e4m3_encode(sk > 0.f ? xk / sk : xk);
+    V[j * kBlock + r] = (uint8_t)e4m3_encode(sv > 0.f ? xv / sv : xv);
+  }
+  if (threadIdx.x == 0) {
+    cv.ks[si] = sk;
+    cv.vs[si] = sv;
+  }
+}
+
+// ---------------------------------------------------------------- gather
+template <typename E>
+__global__ __launch_bounds__(256) void k_gather(CacheView cv, int layer, int seq, int start,
+                                                int count, E* kout, E* vout) {
+  const int d = cv.d;
+  const int64_t total = (int64_t)count * cv.n_kv * d;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int j = (int)(i % d);
+    const int h = (int)((i / d) % cv.n_kv);
+    const int p = start + (int)(i / ((int64_t)d * cv.n_kv));
+    const int blk = block_of(cv, seq, p);
+    if (blk < 0) continue;
+    const int64_t base = slab_elems(cv, layer, blk, h);
+    kout[i] = ((const E*)cv.k)[base + (p % kBlock) * d + j];
+    vout[i] = ((const E*)cv.v)[base + j * kBlock + (p % kBlock)];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fill_tables(const CacheView& cv, hipStream_t s) {
+  int64_t nbt = (int64_t)cv.max_seqs * cv.max_bps;
+  int grid = (int)std::min<int64_t>((nbt + 255) / 256 + 1, 4096);
+  hipLaunchKernelGGL(k_fill_tables, dim3(grid), dim3(256), 0, s, cv);
+  return hipGetLastError();
+}
+
+hipError_t launch_table_update(const CacheView& cv, const TableUpdate& u, hipStream_t s) {
+  hipLaunchKernelGGL(k_table_update, dim3(1), dim3(256), 0, s, cv, u);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const CacheView& cv, int layer, int n, const int32_t* seqs,
+                         const void* k, const void* v, hipStream_t s) {
+  dim3 grid(n, cv.n_kv);
+  switch (cv.dtype) {
+    case KVC_F32:
+      hipLaunchKernelGGL(k_append_copy<uint32_t>, grid, dim3(64), 0, s, cv, layer, seqs,
+                         (const uint32_t*)k, (const uint32_t*)v);
+      break;
+    case KVC_F16:
+    case KVC_BF16:
+      hipLaunchKernelGGL(k_append_copy<uint16_t>, grid, dim3(64), 0, s, cv, layer, seqs,
+                         (const uint16_t*)k, (const uint16_t*)v);
+      break;
+    default:
+      hipLaunchKernelGGL(k_append_fp8, grid, dim3(64), 0, s, cv, layer, seqs,
+                         (const uint16_t*)k, (const uint16_t*)v);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_write(const CacheView& cv, int layer, int n, const int32_t* seqs, int start,
+                        int T, const void* k, const void* v, hipStream_t s) {
+  const int nlb = (start + T - 1) / kBlock - start / kBlock + 1;
+  dim3 grid(nlb, cv.n_kv, n);
+  switch (cv.dtype) {
+    case KVC_F32:
+      hipLaunchKernelGGL(k_write_copy<uint32_t>, grid, dim3(256), 0, s, cv, layer, seqs, start, T,
+                         (const uint32_t*)k, (const uint32_t*)v);
+      break;
+    case KVC_F16:
+    case KVC_BF16:
+      hipLaunchKernelGGL(k_write_copy<uint16_t>, grid, dim3(256), 0, s, cv, layer, seqs, start, T,
+                         (const uint16_t*)k, (const uint16_t*)v);
+      break;
+    default:
+      hipLaunchKernelGGL(k_write_fp8, grid, dim3(256), 0, s, cv, layer, seqs, start, T,
+                         (const uint16_t*)k, (const uint16_t*)v);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const CacheView& cv, int layer, int seq, int start, int count,
+                         void* k_out, void* v_out, hipStream_t s) {
+  int64_t total = (int64_t)count * cv.n_kv * cv.d;
+  int grid = (int)std::min<int64_t>((total + 255) / 256, 8192);
+  switch (elem_bytes(cv.dtype)) {
+    case 4:
+      hipLaunchKernelGGL(k_gather<uint32_t>, dim3(grid), dim3(256), 0, s, cv, layer, seq, start,
+                         count, (uint32_t*)k_out, (uint32_t*)v_out);
+      break;
+    case 2:
+      hipLaunchKernelGGL(k_gather<uint16_t>, dim3(grid), dim3(256), 0, s, cv, layer, seq, start,
+                         count, (uint16_t*)k_out, (uint16_t*)v_out);
+      break;
+    default:
+      hipLaunchKernelGGL(k_gather<uint8_t>, dim3(grid), dim3(256), 0, s, cv, layer, seq, start,
+                         count, (uint8_t*)k_out, (uint8_t*)v_out);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvfa

@@ -1,0 +1,439 @@
+// C ABI and host-side cache manager.
+//
+// The manager keeps the authoritative host copy of the paged cache's
+// metadata: a free list used as a stack (initially 0..n_blocks-1, blocks are
+// popped from the end and released blocks are pushed back in table order),
+// one block table per sequence and its length ("KV Cache & Flash Attention."
+// (kvcache-7e2), PagedAttention section: fixed 16-token blocks, a per-sequence
+// table, a new block only when the last one is full, release returns every
+// block).  Every change is mirrored to the caller's device tables by a small
+// kernel whose arguments carry the changed entries, enqueued on the caller's
+// stream, so attention kernels later on that stream see it.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kvfa_internal.h"
+
+using namespace kvfa;
+
+struct kvc_cache {
+  kvc_config cfg;
+  bool has_dev = false;
+  kvc_buffers dev{};
+  std::vector<int32_t> free_list;               // stack: back() is popped first
+  std::vector<std::vector<int32_t>> table;      // per sequence
+  std::vector<int32_t> len;                     // per sequence
+  std::vector<uint8_t> live;                    // per sequence
+  std::vector<uint8_t> owned;                   // per block: 1 if some sequence holds it
+  CacheView view() const {
+    CacheView v{};
+    v.k = dev.k_pool;
+    v.v = dev.v_pool;
+    v.ks = dev.k_scale;
+    v.vs = dev.v_scale;
+    v.bt = dev.block_table;
+    v.len = dev.seq_len;
+    v.n_layers = cfg.n_layers;
+    v.n_q = cfg.n_q_heads;
+    v.n_kv = cfg.n_kv_heads;
+    v.d = cfg.d_head;
+    v.n_blocks = cfg.n_blocks;
+    v.max_seqs = cfg.max_seqs;
+    v.max_bps = cfg.max_blocks_per_seq;
+    v.dtype = cfg.kv_dtype;
+    return v;
+  }
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(KVC_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int check_config(const kvc_config* c) {
+  if (!c) return fail(KVC_E_INVAL, "config is NULL");
+  if (c->n_layers < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->n_blocks < 1 ||
+      c->max_seqs < 1 || c->max_blocks_per_seq < 1)
+    return fail(KVC_E_INVAL, "config counts must be positive");
+  if (c->kv_dtype < KVC_F32 || c->kv_dtype > KVC_FP8_E4M3FN)
+    return fail(KVC_E_INVAL, "unknown kv_dtype");
+  if (c->block_size != kBlock) return fail(KVC_E_UNSUPPORTED, "block_size must be 16");
+  if (c->d_head != 64 && c->d_head != 128) return fail(KVC_E_UNSUPPORTED, "d_head must be 64 or 128");
+  if (c->n_q_heads % c->n_kv_heads != 0)
+    return fail(KVC_E_UNSUPPORTED, "n_q_heads must be a multiple of n_kv_heads");
+  if ((int64_t)c->max_blocks_per_seq * kBlock > INT32_MAX)
+    return fail(KVC_E_UNSUPPORTED, "max_blocks_per_seq too large");
+  return KVC_OK;
+}
+
+uint64_t pool_bytes(const kvc_config* c) {
+  return (uint64_t)c->n_layers * c->n_blocks * c->n_kv_heads * kBlock * c->d_head *
+         elem_bytes(c->kv_dtype);
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Collects (index, value) writes and flushes them in launches of at most
+// kTableUpdateMax entries each.
+struct Uploader {
+  kvc_cache* c;
+  hipStream_t s;
+  TableUpdate u{};
+  hipError_t err = hipSuccess;
+  Uploader(kvc_cache* c_, hipStream_t s_) : c(c_), s(s_) {}
+  void put(int32_t idx, int32_t val) {
+    if (!c->has_dev) return;
+    u.idx[u.n] = idx;
+    u.val[u.n] = val;
+    if (++u.n == kTableUpdateMax) flush();
+  }
+  void bt(int32_t seq, int32_t i, int32_t blk) { put(seq * c->cfg.max_blocks_per_seq + i, blk); }
+  void len(int32_t seq, int32_t l) { put(-seq - 1, l); }
+  void flush() {
+    if (u.n == 0) return;
+    hipError_t e = launch_table_update(c->view(), u, s);
+    if (e != hipSuccess && err == hipSuccess) err = e;
+    u.n = 0;
+  }
+  int finish() {
+    flush();
+    return err == hipSuccess ? KVC_OK : hip_fail(err, "table update launch");
+  }
+};
+
+int check_seq(const kvc_cache* c, int32_t seq) {
+  if (seq < 0 || seq >= c->cfg.max_seqs) return fail(KVC_E_INVAL, "sequence id out of range");
+  return KVC_OK;
+}
+
+int need_dev(const kvc_cache* c) {
+  if (!c->has_dev) return fail(KVC_E_STATE, "host-only handle has no device buffers");
+  return KVC_OK;
+}
+
+int32_t live_max_len(const kvc_cache* c) {
+  int32_t m = 0;
+  for (int32_t s = 0; s < c->cfg.max_seqs; ++s)
+    if (c->live[s]) m = std::max(m, c->len[s]);
+  return m;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvc_last_error(void) { return g_err.c_str(); }
+
+int kvc_bytes_per_token(const kvc_config* cfg, uint64_t* out) {
+  int r = check_config(cfg);
+  if (r) return r;
+  if (!out) return fail(KVC_E_INVAL, "out is NULL");
+  *out = 2ull * cfg->n_layers * cfg->n_kv_heads * cfg->d_head * elem_bytes(cfg->kv_dtype);
+  return KVC_OK;
+}
+
+int kvc_required_sizes(const kvc_config* cfg, kvc_sizes* out) {
+  int r = check_config(cfg);
+  if (r) return r;
+  if (!out) return fail(KVC_E_INVAL, "out is NULL");
+  out->k_pool = out->v_pool = pool_bytes(cfg);
+  uint64_t sc = (uint64_t)cfg->n_layers * cfg->n_blocks * cfg->n_kv_heads * sizeof(float);
+  out->k_scale = out->v_scale = cfg->kv_dtype == KVC_FP8_E4M3FN ? sc : 0;
+  out->block_table = (uint64_t)cfg->max_seqs * cfg->max_blocks_per_seq * sizeof(int32_t);
+  out->seq_len = (uint64_t)cfg->max_seqs * sizeof(int32_t);
+  return KVC_OK;
+}
+
+int kvc_create(const kvc_config* cfg, const kvc_buffers* dev, hipStream_t stream,
+               kvc_cache** out) {
+  int r = check_config(cfg);
+  if (r) return r;
+  if (!out) return fail(KVC_E_INVAL, "out is NULL");
+  if (dev) {
+    if (!dev->k_pool || !dev->v_pool || !dev->block_table || !dev->seq_len)
+      return fail(KVC_E_INVAL, "device buffer is NULL");
+    if (cfg->kv_dtype == KVC_FP8_E4M3FN && (!dev->k_scale || !dev->v_scale))
+      return fail(KVC_E_INVAL, "fp8 cache needs k_scale and v_scale");
+    if (!aligned16(dev->k_pool) || !aligned16(dev->v_pool))
+      return fail(KVC_E_INVAL, "pools must be 16-byte aligned");
+  }
+  kvc_cache* c = new (std::nothrow) kvc_cache();
+  if (!c) return fail(KVC_E_INVAL, "out of host memory");
+  c->cfg = *cfg;
+  c->free_list.resize(cfg->n_blocks);
+  for (int32_t i = 0; i < cfg->n_blocks; ++i) c->free_list[i] = i;
+  c->table.resize(cfg->max_seqs);
+  c->len.assign(cfg->max_seqs, 0);
+  c->live.assign(cfg->max_seqs, 0);
+  c->owned.assign(cfg->n_blocks, 0);
+  if (dev) {
+    c->has_dev = true;
+    c->dev = *dev;
+    hipError_t e = launch_fill_tables(c->view(), stream);
+    if (e != hipSuccess) {
+      delete c;
+      return hip_fail(e, "table fill launch");
+    }
+  }
+  *out = c;
+  return KVC_OK;
+}
+
+int kvc_destroy(kvc_cache* cache) {
+  delete cache;
+  return KVC_OK;
+}
+
+int kvc_seq_alloc(kvc_cache* c, int32_t seq, int32_t n_tokens, hipStream_t stream) {
+  if (!c) return fail(KVC_E_INVAL, "cache is NULL");
+  int r = check_seq(c, seq);
+  if (r) return r;
+  if (c->live[seq]) return fail(KVC_E_STATE, "sequence is already live");
+  if (n_tokens < 0) return fail(KVC_E_INVAL, "n_tokens < 0");
+  int64_t nb = ((int64_t)n_tokens + kBlock - 1) / kBlock;
+  if (nb > c->cfg.max_blocks_per_seq) return fail(KVC_E_INVAL, "n_tokens exceeds the table width");
+  if (nb > (int64_t)c->free_list.size()) return fail(KVC_E_NO_BLOCKS, "free list exhausted");
+  Uploader up(c, stream);
+  auto& t = c->table[seq];
+  t.clear();
+  for (int64_t i = 0; i < nb; ++i) {
+    int32_t b = c->free_list.back();
+    c->free_list.pop_back();
+    c->owned[b] = 1;
+    t.push_back(b);
+    up.bt(seq, (int32_t)i, b);
+  }
+  c->len[seq] = n_tokens;
+  c->live[seq] = 1;
+  up.len(seq, n_tokens);
+  return up.finish();
+}
+
+int kvc_seq_grow(kvc_cache* c, int32_t n, const int32_t* seqs, hipStream_t stream) {
+  if (!c) return fail(KVC_E_INVAL, "cache is NULL");
+  if (n < 0 || (n > 0 && !seqs)) return fail(KVC_E_INVAL, "bad sequence list");
+  std::vector<uint8_t> seen(c->cfg.max_seqs, 0);
+  int64_t need = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    int r = check_seq(c, seqs[i]);
+    if (r) return r;
+    int32_t s = seqs[i];
+    if (!c->live[s]) return fail(KVC_E_STATE, "sequence is not live");
+    if (seen[s]) return fail(KVC_E_INVAL, "duplicate sequence id");
+    seen[s] = 1;
+    if ((int64_t)c->len[s] + 1 > (int64_t)c->cfg.max_blocks_per_seq * kBlock)
+      return fail(KVC_E_INVAL, "sequence would exceed its table width");
+    if (c->len[s] % kBlock == 0) ++need;
+  }
+  if (need > (int64_t)c->free_list.size()) return fail(KVC_E_NO_BLOCKS, "free list exhausted");
+  Uploader up(c, stream);
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t s = seqs[i];
+    if (c->len[s] % kBlock == 0) {
+      int32_t b = c->free_list.back();
+      c->free_list.pop_back();
+      c->owned[b] = 1;
+      up.bt(s, (int32_t)c->table[s].size(), b);
+      c->table[s].push_back(b);
+    }
+    c->len[s] += 1;
+    up.len(s, c->len[s]);
+  }
+  return up.finish();
+}
+
+int kvc_seq_release(kvc_cache* c, int32_t seq, hipStream_t stream) {
+  if (!c) return fail(KVC_E_INVAL, "cache is NULL");
+  int r = check_seq(c, seq);
+  if (r) return r;
+  if (!c->live[seq]) return fail(KVC_E_STATE, "sequence is not live");
+  Uploader up(c, stream);
+  auto& t = c->table[seq];
+  for (size_t i = 0; i < t.size(); ++i) {
+    c->free_list.push_back(t[i]);
+    c->owned[t[i]] = 0;
+    up.bt(seq, (int32_t)i, -1);
+  }
+  t.clear();
+  c->len[seq] = 0;
+  c->live[seq] = 0;
+  up.len(seq, 0);
+  return up.finish();
+}
+
+int kvc_set_block_table(kvc_cache* c, int32_t seq, const int32_t* blocks, int32_t nblk,
+                        int32_t len, hipStream_t stream) {
+  if (!c) return fail(KVC_E_INVAL, "cache is NULL");
+  int r = check_seq(c, seq);
+  if (r) return r;
+  if (c->live[seq]) return fail(KVC_E_STATE, "sequence is already live");
+  if (len < 0 || nblk != (len + kBlock - 1) / kBlock || (nblk > 0 && !blocks))
+    return fail(KVC_E_INVAL, "nblk must equal ceil(len / 16)");
+  if (nblk > c->cfg.max_blocks_per_seq) return fail(KVC_E_INVAL, "table too long");
+  std::vector<uint8_t> seen(c->cfg.n_blocks, 0);
+  for (int32_t i = 0; i < nblk; ++i) {
+    int32_t b = blocks[i];
+    if (b < 0 || b >= c->cfg.n_blocks) return fail(KVC_E_INVAL, "block id out of range");
+    if (c->owned[b] || seen[b]) return fail(KVC_E_STATE, "block is not free");
+    seen[b] = 1;
+  }
+  // Remove the chosen blocks from the free list, keeping the order of the rest.
+  std::vector<int32_t> rest;
+  rest.reserve(c->free_list.size());
+  for (int32_t b : c->free_list)
+    if (!seen[b]) rest.push_back(b);
+  c->free_list.swap(rest);
+  Uploader up(c, stream);
+  auto& t = c->table[seq];
+  t.assign(blocks, blocks + nblk);
+  for (int32_t i = 0; i < nblk; ++i) {
+    c->owned[blocks[i]] = 1;
+    up.bt(seq, i, blocks[i]);
+  }
+  c->len[seq] = len;
+  c->live[seq] = 1;
+  up.len(seq, len);
+  return up.finish();
+}
+
+int kvc_seq_len(const kvc_cache* c, int32_t seq, int32_t* out) {
+  if (!c || !out) return fail(KVC_E_INVAL, "NULL argument");
+  int r = check_seq(c, seq);
+  if (r) return r;
+  if (!c->live[seq]) return fail(KVC_E_STATE, "sequence is not live");
+  *out = c->len[seq];
+  return KVC_OK;
+}
+
+int kvc_seq_blocks(const kvc_cache* c, int32_t seq, int32_t* blocks, int32_t cap,
+                   int32_t* n_out) {
+  if (!c || !n_out) return fail(KVC_E_INVAL, "NULL argument");
+  int r = check_seq(c, seq);
+  if (r) return r;
+  if (!c->live[seq]) return fail(KVC_E_STATE, "sequence is not live");
+  const auto& t = c->table[seq];
+  *n_out = (int32_t)t.size();
+  if (blocks) {
+    if (cap < (int32_t)t.size()) return fail(KVC_E_INVAL, "cap too small");
+    std::copy(t.begin(), t.end(), blocks);
+  }
+  return KVC_OK;
+}
+
+int kvc_free_blocks(const kvc_cache* c, int32_t* out) {
+  if (!c || !out) return fail(KVC_E_INVAL, "NULL argument");
+  *out = (int32_t)c->free_list.size();
+  return KVC_OK;
+}
+
+int kvc_append(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs, const void* k,
+               const void* v, hipStream_t stream) {
+  if (!c) return fail(KVC_E_INVAL, "cache is NULL");
+  int r = need_dev(c);
+  if (r) return r;
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(KVC_E_STATE, "layer out of range");
+  if (n < 0) return fail(KVC_E_INVAL, "n < 0");
+  if (n == 0) return KVC_OK;
+  if (!seqs || !k || !v) return fail(KVC_E_INVAL, "NULL device pointer");
+  hipError_t e = launch_append(c->view(), layer, n, seqs, k, v, stream);
+  return e == hipSuccess ? KVC_OK : hip_fail(e, "append launch");
+}
+
+int kvc_write(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs, int32_t start,
+              int32_t T, const void* k, const void* v, hipStream_t stream) {
+  if (!c) return fail(KVC_E_INVAL, "cache is NULL");
+  int r = need_dev(c);
+  if (r) return r;
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(KVC_E_STATE, "layer out of range");
+  if (n < 0 || T < 0 || start < 0) return fail(KVC_E_INVAL, "negative size");
+  if ((int64_t)start + T > (int64_t)c->cfg.max_blocks_per_seq * kBlock)
+    return fail(KVC_E_INVAL, "rows beyond the table width");
+  if (n == 0 || T == 0) return KVC_OK;
+  if (!seqs || !k || !v) return fail(KVC_E_INVAL, "NULL device pointer");
+  if (!aligned16(k) || !aligned16(v)) return fail(KVC_E_INVAL, "k/v must be 16-byte aligned");
+  hipError_t e = launch_write(c->view(), layer, n, seqs, start, T, k, v, stream);
+  return e == hipSuccess ? KVC_OK : hip_fail(e, "write launch");
+}
+
+int kvc_attn_prefill(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs, int32_t T,
+                     const void* q, const void* k, const void* v, void* out, float scale,
+                     hipStream_t stream) {
+  if (!c) return fail(KVC_E_INVAL, "cache is NULL");
+  int r = need_dev(c);
+  if (r) return r;
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(KVC_E_STATE, "layer out of range");
+  if (n < 0 || T < 0) return fail(KVC_E_INVAL, "negative size");
+  if (!std::isfinite(scale)) return fail(KVC_E_INVAL, "scale must be finite");
+  if (n == 0 || T == 0) return KVC_OK;
+  if (!q || !k || !v || !out) return fail(KVC_E_INVAL, "NULL device pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(KVC_E_INVAL, "q/k/v/out must be 16-byte aligned");
+  if (seqs && (int64_t)T > (int64_t)c->cfg.max_blocks_per_seq * kBlock)
+    return fail(KVC_E_INVAL, "prompt longer than the table width");
+  hipError_t e = hipSuccess;
+  if (seqs) e = launch_write(c->view(), layer, n, seqs, 0, T, k, v, stream);
+  if (e == hipSuccess) e = launch_prefill(c->view(), n, T, q, k, v, out, scale, stream);
+  return e == hipSuccess ? KVC_OK : hip_fail(e, "prefill launch");
+}
+
+int kvc_decode_workspace_bytes(const kvc_cache* c, int32_t n, int32_t num_splits, uint64_t* out) {
+  if (!c || !out) return fail(KVC_E_INVAL, "NULL argument");
+  if (n < 0 || num_splits < 0) return fail(KVC_E_INVAL, "negative size");
+  DecodePlan p = make_decode_plan(c->view(), n, live_max_len(c), num_splits);
+  *out = p.ws_bytes;
+  return KVC_OK;
+}
+
+int kvc_attn_decode(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs, const void* q,
+                    void* out, float scale, int32_t num_splits, void* ws, uint64_t ws_bytes,
+                    hipStream_t stream) {
+  if (!c) return fail(KVC_E_INVAL, "cache is NULL");
+  int r = need_dev(c);
+  if (r) return r;
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(KVC_E_STATE, "layer out of range");
+  if (n < 0 || num_splits < 0) return fail(KVC_E_INVAL, "negative size");
+  if (!std::isfinite(scale)) return fail(KVC_E_INVAL, "scale must be finite");
+  if (n == 0) return KVC_OK;
+  if (!seqs || !q || !out) return fail(KVC_E_INVAL, "NULL device pointer");
+  if (!aligned16(q) || !aligned16(out)) return fail(KVC_E_INVAL, "q/out must be 16-byte aligned");
+  int32_t max_len = live_max_len(c);
+  if (max_len <= 0) return fail(KVC_E_STATE, "no live sequence holds any token");
+  DecodePlan p = make_decode_plan(c->view(), n, max_len, num_splits);
+  if (p.ws_bytes > 0 && (!ws || ws_bytes < p.ws_bytes))
+    return fail(KVC_E_WORKSPACE, "workspace too small: need " + std::to_string(p.ws_bytes) +
+                                     " bytes");
+  if (p.ws_bytes > 0 && !aligned16(ws)) return fail(KVC_E_INVAL, "workspace must be 16-byte aligned");
+  hipError_t e = launch_decode(c->view(), layer, n, seqs, q, out, scale, p, ws, stream);
+  return e == hipSuccess ? KVC_OK : hip_fail(e, "decode launch");
+}
+
+int kvc_gather(const kvc_cache* c, int32_t layer, int32_t seq, int32_t start, int32_t count,
+               void* k_out, void* v_out, hipStream_t stream) {
+  if (!c) return fail(KVC_E_INVAL, "cache is NULL");
+  int r = need_dev(c);
+  if (r) return r;
+  r = check_seq(c, seq);
+  if (r) return r;
+  if (!c->live[seq]) return fail(KVC_E_STATE, "sequence is not live");
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(KVC_E_STATE, "layer out of range");
+  if (start < 0 || count < 0 || (int64_t)start + count > c->len[seq])
+    return fail(KVC_E_INVAL, "rows outside the sequence");
+  if (count == 0) return KVC_OK;
+  if (!k_out || !v_out) return fail(KVC_E_INVAL, "NULL device pointer");
+  hipError_t e = launch_gather(c->view(), layer, seq, start, count, k_out, v_out, stream);
+  return e == hipSuccess ? KVC_OK : hip_fail(e, "gather launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// Internal declarations shared by the host manager and the kernel launchers.
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+#include "kvfa.h"
+
+namespace kvfa {
+
+constexpr int kBlock = 16;          // tokens per physical block
+constexpr int kTableUpdateMax = 240; // (index, value) pairs carried per update launch
+
+// Everything a kernel needs to address the cache, passed by value.
+struct CacheView {
+  void* k;            // k_pool
+  void* v;            // v_pool
+  float* ks;          // k_scale (fp8 only)
+  float* vs;          // v_scale (fp8 only)
+  int32_t* bt;        // block_table [max_seqs][max_bps]
+  int32_t* len;       // seq_len [max_seqs]
+  int32_t n_layers, n_q, n_kv, d, n_blocks, max_seqs, max_bps;
+  int32_t dtype;      // kvc_dtype of the storage
+};
+
+// Table/length writes enqueued as kernel arguments (no host staging buffer
+// whose lifetime would have to outlive the copy).  idx >= 0 addresses
+// block_table[idx]; idx < 0 addresses seq_len[-idx - 1].
+struct TableUpdate {
+  int32_t n;
+  int32_t idx[kTableUpdateMax];
+  int32_t val[kTableUpdateMax];
+};
+
+// How one decode call cuts the longest context into splits.
+struct DecodePlan {
+  int32_t splits;     // splits per (sequence, kv head)
+  int32_t split_len;  // tokens per split, a multiple of 64
+  uint64_t ws_bytes;  // workspace for partial (m, l, O); 0 if splits == 1
+};
+
+inline int elem_bytes(int dtype) {
+  return dtype == KVC_F32 ? 4 : dtype == KVC_FP8_E4M3FN ? 1 : 2;
+}
+inline int io_dtype(int dtype) { return dtype == KVC_FP8_E4M3FN ? KVC_BF16 : dtype; }
+
+DecodePlan make_decode_plan(const CacheView& cv, int32_t n, int32_t max_len, int32_t num_splits);
+
+// Launchers: return hipSuccess or the launch error.
+hipError_t launch_fill_tables(const CacheView& cv, hipStream_t s);
+hipError_t launch_table_update(const CacheView& cv, const TableUpdate& u, hipStream_t s);
+hipError_t launch_append(const CacheView& cv, int layer, int n, const int32_t* seqs,
+                         const void* k, const void* v, hipStream_t s);
+hipError_t launch_write(const CacheView& cv, int layer, int n, const int32_t* seqs, int start,
+                        int T, const void* k, const void* v, hipStream_t s);
+hipError_t launch_gather(const CacheView& cv, int layer, int seq, int start, int count,
+                         void* k_out, void* v_out, hipStream_t s);
+hipError_t launch_decode(const CacheView& cv, int layer, int n, const int32_t* seqs,
+                         const void* q, void* out, float scale, const DecodePlan& plan,
+                         void* ws, hipStream_t s);
+hipError_t launch_prefill(const CacheView& cv, int n, int T, const void* q, const void* k,
+                          const void* v, void* out, float scale, hipStream_t s);
+
+}  // namespace kvfa

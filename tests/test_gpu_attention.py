@@ -1,0 +1,185 @@
+"""Attention on the GPU against the float64 oracle: decode (paged, split,
+GQA, all storage types), causal prefill, and the GPT-2-small fp32 path."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_flashattention_amd as kv
+from harness import (ABS_TOL, FP8_ABS_TOL, REL_TOL, Built, assert_close, errors, f64)
+from oracle import attention as A
+from workloads import DecodeWorkload, GPT2Small, decode_workload, prefill_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _q(w, io):
+    return torch.from_numpy(w.q()).to(io).cuda()
+
+
+@pytest.mark.parametrize("name", ["llama8b_decode", "llama70b_decode_bf16", "long_mha_decode",
+                                  "llama70b_decode_fp8"])
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_decode_small_workloads(name, splits):
+    w = decode_workload(name, small=True)
+    b = Built(w)
+    q = _q(w, b.io)
+    out = b.c.attn_decode(0, b.seqs, q, num_splits=splits)
+    torch.cuda.synchronize()
+    y = f64(out)
+    if w.kv_dtype == "fp8":
+        assert_close(y, b.oracle_decode(q), what="fp8 vs dequantised oracle", io=b.io_name)
+        a, _ = errors(y, b.oracle_decode_source(q), b.io_name)
+        assert a <= FP8_ABS_TOL, f"fp8 vs bf16 source oracle: abs {a:.3e}"
+    else:
+        assert_close(y, b.oracle_decode(q), what=name, io=b.io_name)
+
+
+@pytest.mark.parametrize("dtype,n_q,n_kv,d", [("bf16", 16, 16, 64), ("fp16", 12, 4, 64),
+                                              ("bf16", 32, 1, 128), ("fp8", 20, 4, 64),
+                                              ("f32", 8, 2, 128)])
+def test_decode_shapes(dtype, n_q, n_kv, d):
+    w = DecodeWorkload("shape" + dtype, 4, n_q, n_kv, d, dtype, (1, 200), outliers=True)
+    b = Built(w)
+    q = _q(w, b.io)
+    for splits in (0, 2, 7):
+        y = f64(b.c.attn_decode(0, b.seqs, q, num_splits=splits))
+        assert_close(y, b.oracle_decode(q), what=f"{dtype} splits={splits}", io=b.io_name)
+
+
+def test_decode_deterministic_and_table_order_independent():
+    w = decode_workload("llama8b_decode", small=True)
+    a = Built(w)
+    b = Built(w, identity_tables=True)
+    q = _q(w, a.io)
+    ya = a.c.attn_decode(0, a.seqs, q).clone()
+    ya2 = a.c.attn_decode(0, a.seqs, q).clone()
+    yb = b.c.attn_decode(0, b.seqs, q).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(ya.view(torch.int16), ya2.view(torch.int16))
+    assert torch.equal(ya.view(torch.int16), yb.view(torch.int16))
+
+
+def test_decode_unpoisoned_equals_poisoned():
+    w = decode_workload("llama8b_decode", small=True)
+    a = Built(w, poison=True)
+    b = Built(w, poison=False)
+    q = _q(w, a.io)
+    ya = a.c.attn_decode(0, a.seqs, q, num_splits=2)
+    yb = b.c.attn_decode(0, b.seqs, q, num_splits=2)
+    torch.cuda.synchronize()
+    assert torch.equal(ya.view(torch.int16), yb.view(torch.int16))
+
+
+def test_decode_single_row_returns_value_exactly():
+    """L = 1: the only row gets weight 1, so the output is v itself."""
+    w = DecodeWorkload("one", 3, 8, 2, 128, "bf16", 1)
+    b = Built(w)
+    q = _q(w, b.io)
+    y = b.c.attn_decode(0, b.seqs, q).float().cpu()
+    for s in range(3):
+        v = b.src_v[s][0].float().cpu()
+        for h in range(8):
+            assert torch.equal(y[s, h], v[h // 4])
+
+
+def test_fp8_decode_reproduces_every_code_exactly():
+    """A one-row fp8 cache whose row holds every finite E4M3FN value (scale
+    448/448 = 1): decode returns the stored values exactly, so the
+    widening of codes inside the decode kernel is exact for all 254 codes."""
+    from oracle.codecs import E4M3_TABLE
+    vals = np.array([x for x in E4M3_TABLE if np.isfinite(x)], dtype=np.float32)
+    vals = np.concatenate([vals, np.zeros(256 - len(vals), np.float32)])   # 256 = 2 heads x 128
+    row = vals.reshape(1, 2, 128)
+    c = kv.KvCache(1, 2, 2, 128, 2, 1, 2, "fp8", poison=True)
+    c.seq_alloc(0, 0)
+    c.seq_grow([0])
+    seqs = torch.zeros(1, dtype=torch.int32, device="cuda")
+    k = torch.from_numpy(row).to(torch.bfloat16).cuda()
+    c.append(0, seqs, k, k)
+    q = torch.ones(1, 2, 128, dtype=torch.bfloat16, device="cuda")
+    y = c.attn_decode(0, seqs, q).float().cpu().numpy()
+    assert np.array_equal(y.reshape(-1), vals), "decoded fp8 values differ"
+    assert float(c.v_scale[0, c.seq_blocks(0)[0], 0]) == 1.0
+
+
+def _prefill_case(dtype, batch, T, n_q, n_kv, d, seed=0):
+    w = prefill_workload(small=True, seed=seed)
+    rng = np.random.default_rng([seed, T, n_q, n_kv, d])
+    io = kv.IO_TORCH[dtype]
+    q = torch.from_numpy(rng.standard_normal((batch, T, n_q, d), dtype=np.float32)).to(io).cuda()
+    k = torch.from_numpy(rng.standard_normal((batch, T, n_kv, d), dtype=np.float32)).to(io).cuda()
+    v = torch.from_numpy(rng.standard_normal((batch, T, n_kv, d), dtype=np.float32)).to(io).cuda()
+    return q, k, v
+
+
+@pytest.mark.parametrize("dtype,batch,T,n_q,n_kv,d", [
+    ("bf16", 2, 333, 32, 8, 128), ("bf16", 1, 1, 8, 8, 128), ("f16", 2, 130, 8, 2, 64),
+    ("bf16", 1, 257, 4, 1, 64), ("f32", 1, 100, 4, 2, 128)])
+def test_prefill_vs_oracle(dtype, batch, T, n_q, n_kv, d):
+    q, k, v = _prefill_case(dtype, batch, T, n_q, n_kv, d)
+    c = kv.KvCache(1, n_q, n_kv, d, 4, 1, 4, dtype)
+    out = c.attn_prefill(0, q, k, v)
+    torch.cuda.synchronize()
+    scale = 1 / math.sqrt(d)
+    for s in range(batch):
+        ref = A.prefill_attention(f64(q[s]), f64(k[s]), f64(v[s]), scale)
+        assert_close(f64(out[s]), ref, what=f"prefill {dtype} T={T} seq {s}", io=dtype)
+
+
+def test_prefill_small_workload_writes_cache():
+    """Prefill with sequences: outputs match the oracle and the prompt's
+    K/V rows land in the cache bit for bit (gather)."""
+    w = prefill_workload(small=True)
+    qn, kn, vn = w.qkv()
+    q, k, v = (torch.from_numpy(a).to(torch.bfloat16).cuda() for a in (qn, kn, vn))
+    nb = -(-w.T // 16)
+    c = kv.KvCache(1, w.n_q, w.n_kv, w.d, w.batch * nb + 3, w.batch, nb, "bf16", poison=True)
+    for s in range(w.batch):
+        c.seq_alloc(s, w.T)
+    seqs = torch.arange(w.batch, dtype=torch.int32, device="cuda")
+    out = c.attn_prefill(0, q, k, v, seqs=seqs)
+    torch.cuda.synchronize()
+    for s in range(w.batch):
+        ref = A.prefill_attention(f64(q[s]), f64(k[s]), f64(v[s]), 1 / math.sqrt(w.d))
+        assert_close(f64(out[s]), ref, what=f"prefill seq {s}")
+        gk, gv = c.gather(0, s, 0, w.T)
+        assert torch.equal(gk.view(torch.int16), k[s].view(torch.int16))
+        assert torch.equal(gv.view(torch.int16), v[s].view(torch.int16))
+
+
+def test_gpt2_small_fp32_cached_decode_equals_recompute():
+    """GPT-2-small shape in fp32: prefill the 261-token prompt into the cache,
+    then 200 steps of (grow, append, decode).  At every step the cached
+    decode row equals the last row of a full causal recompute on the GPU and
+    the float64 oracle."""
+    w = GPT2Small()
+    H, d = w.n_heads, w.d
+    total = w.prompt_len + w.n_new
+    c = kv.KvCache(1, H, H, d, -(-total // 16) + 1, 1, -(-total // 16) + 1, "f32", poison=True)
+    c.seq_alloc(0, w.prompt_len)
+    seqs = torch.zeros(1, dtype=torch.int32, device="cuda")
+    Q = torch.from_numpy(w.q_prompt).cuda()[None]
+    K = torch.from_numpy(w.k_prompt).cuda()[None]
+    V = torch.from_numpy(w.v_prompt).cuda()[None]
+    out = c.attn_prefill(0, Q, K, V, seqs=seqs)
+    scale = 1 / math.sqrt(d)
+    ref = A.prefill_attention(f64(Q[0]), f64(K[0]), f64(V[0]), scale)
+    assert_close(f64(out[0]), ref, abs_tol=1e-4, rel_tol=1e-4, what="fp32 prefill", io="f32")
+    Kall, Vall, Qall = [K[0]], [V[0]], [Q[0]]
+    for t, (k, v, q) in enumerate(w.steps):
+        kt, vt, qt = (torch.from_numpy(a).cuda() for a in (k, v, q))
+        c.seq_grow([0])
+        c.append(0, seqs, kt[None].contiguous(), vt[None].contiguous())
+        dec = c.attn_decode(0, seqs, qt[None].contiguous())
+        Kall.append(kt[None]); Vall.append(vt[None]); Qall.append(qt[None])
+        if t % 20 == 0 or t == w.n_new - 1:
+            Kc, Vc, Qc = torch.cat(Kall), torch.cat(Vall), torch.cat(Qall)
+            full = c.attn_prefill(0, Qc[None].contiguous(), Kc[None].contiguous(),
+                                  Vc[None].contiguous())
+            torch.cuda.synchronize()
+            assert torch.allclose(dec[0], full[0, -1], atol=1e-5, rtol=0)
+            r = A.decode_attention(f64(qt), f64(Kc), f64(Vc), scale)
+            assert_close(f64(dec[0]), r, abs_tol=1e-4, rel_tol=1e-4, what=f"fp32 step {t}",
+                         io="f32")

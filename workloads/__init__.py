@@ -22,6 +22,8 @@ its seed and, for the large caches, from the chunk it lives in):
   consecutive runs of ceil(L/16) blocks per sequence, so that no kernel can
   rely on a sequence's blocks being adjacent.
 """
+import zlib
+
 import numpy as np
 
 CHUNK = 1024
@@ -29,7 +31,9 @@ BLOCK = 16
 
 
 def _rng(*key):
-    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(key))))
+    """Generator seeded by a tuple of ints and strings (strings by CRC-32)."""
+    ints = [zlib.crc32(k.encode()) if isinstance(k, str) else int(k) for k in key]
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(ints)))
 
 
 # ------------------------------------------------------------------ GPT-2 small
