@@ -29,10 +29,13 @@ hipError_t launch_decode_mfma(const CacheView& cv, int layer, int n, const int32
 DecodePlan make_decode_plan(const CacheView& cv, int32_t n, int32_t max_len, int32_t num_splits) {
   DecodePlan p{1, 64, 0};
   if (max_len <= 0 || n <= 0) return p;
+  // Splits are whole multiples of 256 tokens (four waves x 64-token chunks)
+  // when chosen automatically, of 64 tokens when the caller fixes the count.
   const int64_t chunks = (max_len + 63) / 64;               // 64-token units
-  int64_t splits;
+  int64_t splits, unit;
   if (num_splits > 0) {
     splits = std::min<int64_t>(num_splits, chunks);
+    unit = 1;
   } else {
     // Enough workgroups to cover the chip a few times over, but no split
     // shorter than 256 tokens.
@@ -40,8 +43,10 @@ DecodePlan make_decode_plan(const CacheView& cv, int32_t n, int32_t max_len, int
     const int64_t target = 2048;
     splits = std::max<int64_t>(1, std::min<int64_t>((target + groups - 1) / groups,
                                                     (chunks + 3) / 4));
+    unit = 4;
   }
-  const int64_t per = (chunks + splits - 1) / splits;
+  int64_t per = (chunks + splits - 1) / splits;
+  per = (per + unit - 1) / unit * unit;
   p.split_len = (int32_t)(per * 64);
   p.splits = (int32_t)((max_len + p.split_len - 1) / p.split_len);
   if (p.splits > 1)

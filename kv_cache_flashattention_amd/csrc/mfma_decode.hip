@@ -160,67 +160,88 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(CacheView cv, int layer,
   const int64_t slab_bytes = (int64_t)kBlock * D * EB;
   const int64_t layer_blocks = (int64_t)layer * cv.n_blocks;
   const int nchunks = (t1 - t0 + 63) / 64;
+  const int last_blk = (L - 1) / kBlock;             // last table entry of the sequence
+  const int wu = __builtin_amdgcn_readfirstlane(w);   // wave index as a scalar
 
-  for (int ci = w; ci < nchunks; ci += 4) {
+  for (int ci = wu; ci < nchunks; ci += 4) {
     const int c = t0 + ci * 64;
     const int nvalid = min(64, t1 - c);
-    const int nb = (nvalid + 15) >> 4;
-    int bid[4];
+    const bool tail = nvalid < 64;
+    // Table entries of the chunk's four blocks (entries past the sequence's
+    // end are clamped to its last block; their tokens are masked below).
+    int64_t sbase[4];
+    int64_t sidx[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int x = i < nb ? btrow[c / kBlock + i] : 0;
+      int x = btrow[min(c / kBlock + i, last_blk)];
       if (x < 0 || x >= cv.n_blocks) {
         bad = true;
         x = 0;
       }
-      bid[i] = x;
+      sidx[i] = (layer_blocks + x) * cv.n_kv + kvh;
+      sbase[i] = sidx[i] * slab_bytes;
     }
-    // byte offset of slab (layer, block, kvh)
-    auto slab = [&](int blk) -> int64_t {
-      return ((layer_blocks + blk) * cv.n_kv + kvh) * slab_bytes;
+    auto pick = [&](const int64_t* a, int i) -> int64_t {
+      return i == 0 ? a[0] : i == 1 ? a[1] : i == 2 ? a[2] : a[3];
     };
+
+    // ---- issue every K and V load of the chunk before using any
+    constexpr int KL = KV == KV_FP8 ? KS / 2 : KS;      // 16-byte K loads per tile
+    constexpr int VL = KV == KV_FP8 ? DT : 2 * DT;      // 16-byte V loads per chunk
+    uint4 kraw[4][KL];
+    uint4 vraw[VL];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint8_t* krow = kpool + pick(sbase, tok_block<KV>(t, r16)) +
+                            (int64_t)tok_slot<KV>(t, r16) * D * EB;
+#pragma unroll
+      for (int a = 0; a < KL; ++a) {
+        const int off = KV == KV_FP8 ? 64 * a + 16 * g : 2 * dmap<KV>(a, g);
+        kraw[t][a] = *(const uint4*)(krow + off);
+      }
+    }
+    if (KV == KV_FP8) {
+      const uint8_t* vslab = vpool + pick(sbase, g);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) vraw[dt] = *(const uint4*)(vslab + (16 * dt + r16) * kBlock);
+    } else {
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const uint8_t* vslab = vpool + pick(sbase, 2 * st + (g >> 1));
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          vraw[st * DT + dt] =
+              *(const uint4*)(vslab + 2 * ((16 * dt + r16) * kBlock + 8 * (g & 1)));
+      }
+    }
 
     // ---- S^T = K Q^T for four 16-token tiles
     f32x4 sacc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int bi = tok_block<KV>(t, r16);
-      const int sl = tok_slot<KV>(t, r16);
-      const bool live = bi < nb;
-      const int blk = bi == 0 ? bid[0] : bi == 1 ? bid[1] : bi == 2 ? bid[2] : bid[3];
-      const uint8_t* krow = kpool + slab(blk) + (int64_t)sl * D * EB;
-      if (KV == KV_FP8) {
 #pragma unroll
-        for (int a = 0; a < KS / 2; ++a) {
-          uint4 raw = live ? *(const uint4*)(krow + 64 * a + 16 * g) : make_uint4(0, 0, 0, 0);
-          OpT k0 = __builtin_bit_cast(OpT, fp8x8_to_bf16(raw.x, raw.y));
-          OpT k1 = __builtin_bit_cast(OpT, fp8x8_to_bf16(raw.z, raw.w));
-          sacc[t] = mfma(k0, qop[2 * a], sacc[t]);
-          sacc[t] = mfma(k1, qop[2 * a + 1], sacc[t]);
-        }
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          uint4 raw = live ? *(const uint4*)(krow + 2 * dmap<KV>(ks, g)) : make_uint4(0, 0, 0, 0);
-          sacc[t] = mfma(__builtin_bit_cast(OpT, raw), qop[ks], sacc[t]);
+      for (int a = 0; a < KL; ++a) {
+        if (KV == KV_FP8) {
+          sacc[t] = mfma(__builtin_bit_cast(OpT, fp8x8_to_bf16(kraw[t][a].x, kraw[t][a].y)),
+                         qop[2 * a], sacc[t]);
+          sacc[t] = mfma(__builtin_bit_cast(OpT, fp8x8_to_bf16(kraw[t][a].z, kraw[t][a].w)),
+                         qop[2 * a + 1], sacc[t]);
+        } else {
+          sacc[t] = mfma(__builtin_bit_cast(OpT, kraw[t][a]), qop[a], sacc[t]);
         }
       }
     }
 
-    // ---- online softmax over the chunk (rows of S^T held by this lane: query r16)
+    // ---- online softmax over the chunk (this lane's S^T column: query r16)
     float ksc = 1.f, vsc = 1.f;
     if (KV == KV_FP8) {
-      const int blk = g == 0 ? bid[0] : g == 1 ? bid[1] : g == 2 ? bid[2] : bid[3];
-      const int64_t si = (layer_blocks + blk) * cv.n_kv + kvh;
-      if (g < nb) {
-        ksc = cv.ks[si];
-        vsc = cv.vs[si];
-      }
+      const int64_t si = pick(sidx, g);
+      ksc = cv.ks[si];
+      vsc = cv.vs[si];
     }
     float p[4][4];
     float cmax = -INFINITY;
-    const bool tail = nvalid < 64;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -258,43 +279,36 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(CacheView cv, int layer,
 #pragma unroll
       for (int j = 0; j < 8; ++j) pv[j] = p[2 * st + (j >> 2)][j & 3] * vsc;
       const OpT pop = pack8<OpT>(pv);
-      // V operand: 8 tokens of one head-dimension column d = 16*dt + r16.
-      int bi, s0;
-      if (KV == KV_FP8) {
-        bi = g;
-        s0 = 8 * st;
-      } else {
-        bi = 2 * st + (g >> 1);
-        s0 = 8 * (g & 1);
+      // This lane's V operand covers block bi, slots s0..s0+7 of the chunk;
+      // in the chunk holding the split's end, slots past it are zeroed (they
+      // may hold stale or poisoned bytes, and 0 * NaN would poison O).
+      const int bi = KV == KV_FP8 ? g : 2 * st + (g >> 1);
+      const int s0 = KV == KV_FP8 ? 8 * st : 8 * (g & 1);
+      const int nok = tail ? nvalid - 16 * bi - s0 : 8;  // valid slots among the 8
+      uint32_t keep[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (KV == KV_FP8) {        // 4 one-byte slots per dword, dwords 0..1 used
+          const int base = 4 * e;
+          uint32_t mk = 0;
+#pragma unroll
+          for (int y = 0; y < 4; ++y) mk |= (base + y < nok ? 0xFFu : 0u) << (8 * y);
+          keep[e] = mk;
+        } else {                   // 2 two-byte slots per dword
+          keep[e] = (2 * e < nok ? 0xFFFFu : 0u) | (2 * e + 1 < nok ? 0xFFFF0000u : 0u);
+        }
       }
-      const bool live = bi < nb;
-      const int blk = bi == 0 ? bid[0] : bi == 1 ? bid[1] : bi == 2 ? bid[2] : bid[3];
-      const int nok = nvalid - 16 * bi - s0;              // valid tokens among the 8
-      const uint8_t* vslab = vpool + slab(blk);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const int d = 16 * dt + r16;
         OpT vop;
         if (KV == KV_FP8) {
-          uint2 raw = live ? *(const uint2*)(vslab + d * kBlock + s0) : make_uint2(0, 0);
-          if (tail && nok < 8) {
-            const uint64_t keep = nok <= 0 ? 0ull : (~0ull >> (64 - 8 * nok));
-            uint64_t v64 = ((uint64_t)raw.y << 32 | raw.x) & keep;
-            raw = make_uint2((uint32_t)v64, (uint32_t)(v64 >> 32));
-          }
-          vop = __builtin_bit_cast(OpT, fp8x8_to_bf16(raw.x, raw.y));
+          const uint32_t lo = (st == 0 ? vraw[dt].x : vraw[dt].z) & keep[0];
+          const uint32_t hi = (st == 0 ? vraw[dt].y : vraw[dt].w) & keep[1];
+          vop = __builtin_bit_cast(OpT, fp8x8_to_bf16(lo, hi));
         } else {
-          uint4 raw = live ? *(const uint4*)(vslab + 2 * (d * kBlock + s0)) : make_uint4(0, 0, 0, 0);
-          if (tail && nok < 8) {
-            uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const uint32_t lo = 2 * k < nok ? 0xFFFFu : 0u, hi = 2 * k + 1 < nok ? 0xFFFF0000u : 0u;
-              wds[k] &= (lo | hi);
-            }
-            raw = make_uint4(wds[0], wds[1], wds[2], wds[3]);
-          }
-          vop = __builtin_bit_cast(OpT, raw);
+          const uint4 raw = vraw[st * DT + dt];
+          vop = __builtin_bit_cast(OpT, make_uint4(raw.x & keep[0], raw.y & keep[1],
+                                                   raw.z & keep[2], raw.w & keep[3]));
         }
         o[dt] = mfma(vop, pop, o[dt]);
       }

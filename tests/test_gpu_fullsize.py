@@ -1,0 +1,172 @@
+"""Parity at the workloads' full sizes, in the launch configuration the bench
+times (automatic split plan), on outputs the oracle computes one sequence or
+one head at a time."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_flashattention_amd as kv
+from harness import FP8_ABS_TOL, assert_close, errors, f64
+from oracle import attention as A
+from oracle.paged import PagedCacheModel
+from workloads import decode_workload, prefill_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def populate(w, append_from=None):
+    """Cache holding workload w: rows 0..L-2 by bulk writes (block-aligned
+    chunks), then one grow + kv_append of row L-1 for every sequence.  With
+    append_from=P, rows P..L-2 are added one token at a time (grow +
+    kv_append), the way a decode loop fills the cache."""
+    dt = {"bf16": "bf16", "fp16": "f16", "fp8": "fp8"}[w.kv_dtype]
+    io = kv.IO_TORCH[dt]
+    max_bps = int(w.blocks_per_seq.max()) + 1
+    c = kv.KvCache(1, w.n_q, w.n_kv, w.d, w.n_blocks + w.batch, w.batch, max_bps, dt)
+    tables = w.block_tables()
+    last_k, last_v = [], []
+    for b in range(w.batch):
+        L = int(w.lengths[b])
+        pre = L - 1 if append_from is None else append_from
+        c.set_block_table(b, tables[b][:-(-pre // 16)], pre)
+        sel = torch.tensor([b], dtype=torch.int32, device="cuda")
+        for s0 in range(0, pre, 8192):
+            n = min(8192, pre - s0)
+            k, v = w.kv_rows(b, s0, n)
+            c.write(0, sel, s0, torch.from_numpy(k).to(io).cuda()[None],
+                    torch.from_numpy(v).to(io).cuda()[None])
+        if append_from is not None:
+            k, v = w.kv_rows(b, pre, L - 1 - pre)
+            kt = torch.from_numpy(k).to(io).cuda()
+            vt = torch.from_numpy(v).to(io).cuda()
+            for i in range(L - 1 - pre):
+                c.seq_grow([b])
+                c.append(0, sel, kt[i:i + 1], vt[i:i + 1])
+        k, v = w.kv_rows(b, L - 1, 1)
+        last_k.append(torch.from_numpy(k).to(io).cuda()[0])
+        last_v.append(torch.from_numpy(v).to(io).cuda()[0])
+    c.seq_grow(list(range(w.batch)))
+    seqs = torch.arange(w.batch, dtype=torch.int32, device="cuda")
+    c.append(0, seqs, torch.stack(last_k).contiguous(), torch.stack(last_v).contiguous())
+    torch.cuda.synchronize()
+    return c, seqs, io
+
+
+def source_rows(w, b, io, head=None):
+    """The rows exactly as stored for 16-bit caches (rounded to the io type),
+    widened to float64: [L, n_kv, d] or [L, d] for one kv head."""
+    k, v = w.kv_rows(b, 0, int(w.lengths[b]))
+    if head is not None:
+        k, v = k[:, head], v[:, head]
+    return (torch.from_numpy(np.ascontiguousarray(k)).to(io).double().numpy(),
+            torch.from_numpy(np.ascontiguousarray(v)).to(io).double().numpy())
+
+
+def test_llama8b_decode_full_all_outputs():
+    w = decode_workload("llama8b_decode")
+    c, seqs, io = populate(w)
+    q = torch.from_numpy(w.q()).to(io).cuda()
+    y = f64(c.attn_decode(0, seqs, q))
+    scale = 1 / math.sqrt(w.d)
+    qd = f64(q)
+    worst = (0.0, 0.0)
+    for b in range(w.batch):
+        K, V = source_rows(w, b, io)
+        r = A.decode_attention(qd[b], K, V, scale)
+        a, rel = assert_close(y[b], r, what=f"seq {b} (L={w.lengths[b]})")
+        worst = (max(worst[0], a), max(worst[1], rel))
+    print(f"llama8b decode: worst abs {worst[0]:.2e} rel {worst[1]:.2e}")
+
+
+def test_long_mha_decode_full_sampled_heads():
+    """One 128,000-token fp16 sequence: 2,000 rows written in bulk, then
+    125,999 single-token grow + kv_append steps, then the new token."""
+    w = decode_workload("long_mha_decode")
+    c, seqs, io = populate(w, append_from=2000)
+    assert c.seq_len(0) == 128000
+    q = torch.from_numpy(w.q()).to(io).cuda()
+    y = f64(c.attn_decode(0, seqs, q))
+    qd = f64(q)
+    scale = 1 / math.sqrt(w.d)
+    for h in (0, 7, 19, 31):
+        K, V = source_rows(w, 0, io, head=h)
+        r = A.attention(qd[0, h][None], K, V, scale)[0]
+        assert_close(y[0, h][None], r[None], what=f"head {h}", io="f16")
+    # the single-token path wrote the same bytes as a bulk write would
+    k, _ = c.gather(0, 0, 64000, 3)
+    kk, _ = w.kv_rows(0, 64000, 3)
+    assert torch.equal(k.view(torch.int16).cpu(),
+                       torch.from_numpy(kk).to(io).view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["llama70b_decode_bf16", "llama70b_decode_fp8"])
+def test_llama70b_decode_full_sampled(name):
+    w = decode_workload(name)
+    c, seqs, io = populate(w)
+    q = torch.from_numpy(w.q()).to(io).cuda()
+    y = f64(c.attn_decode(0, seqs, q))
+    qd = f64(q)
+    scale = 1 / math.sqrt(w.d)
+    G = w.n_q // w.n_kv
+    for b in (0, w.batch - 1):
+        for g in (0, 5):
+            Ks, Vs = source_rows(w, b, io, head=g)
+            heads = list(range(g * G, (g + 1) * G))
+            ref_src = np.array([A.attention(qd[b, h][None], Ks, Vs, scale)[0] for h in heads])
+            if w.kv_dtype == "fp8":
+                L = int(w.lengths[b])
+                m = PagedCacheModel(1, 1, w.d, "fp8", -(-L // 16) + 1, 1, -(-L // 16) + 1,
+                                    poison=False)
+                m.alloc(0, L - 1)
+                m.write_rows(0, 0, 0, Ks[:L - 1, None].astype(np.float32),
+                             Vs[:L - 1, None].astype(np.float32))
+                m.grow([0])
+                m.write_rows(0, 0, L - 1, Ks[L - 1:, None].astype(np.float32),
+                             Vs[L - 1:, None].astype(np.float32))
+                Kq, Vq = m.logical_values(0, 0)
+                ref_q = np.array([A.attention(qd[b, h][None], Kq[:, 0], Vq[:, 0], scale)[0]
+                                  for h in heads])
+                # kernel error: against the oracle on the values the cache holds
+                a, _ = errors(y[b, heads], ref_q, "bf16")
+                assert a <= FP8_ABS_TOL, f"fp8 kernel seq {b} kv {g}: abs {a:.3e}"
+                assert_close(y[b, heads], ref_q, what=f"fp8 kernel seq {b} kv {g}")
+                # end to end: never further from the unquantised rows than the
+                # format itself (the oracle on dequantised rows) plus 2e-2
+                fmt = np.abs(ref_q - ref_src)
+                dev = np.abs(y[b, heads] - ref_src)
+                assert np.all(dev <= fmt + 2e-2 + np.abs(ref_src) * 2.0 ** -8), \
+                    f"fp8 end-to-end seq {b} kv {g}: {dev.max():.3e} vs format {fmt.max():.3e}"
+            else:
+                assert_close(y[b, heads], ref_src, what=f"seq {b} kv {g}")
+
+
+def test_llama8b_prefill_full_sampled_rows():
+    """4 x 8,192-token causal prefill (the benched call, K/V appended to the
+    cache): sampled rows of sampled heads against the oracle, and the cache
+    rows bit for bit."""
+    w = prefill_workload()
+    qn, kn, vn = w.qkv()
+    q, k, v = (torch.from_numpy(a).to(torch.bfloat16).cuda() for a in (qn, kn, vn))
+    del qn, kn, vn
+    nb = -(-w.T // 16)
+    c = kv.KvCache(1, w.n_q, w.n_kv, w.d, w.batch * nb, w.batch, nb, "bf16")
+    for b in range(w.batch):
+        c.seq_alloc(b, w.T)
+    seqs = torch.arange(w.batch, dtype=torch.int32, device="cuda")
+    out = c.attn_prefill(0, q, k, v, seqs=seqs)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 63, 64, 127, 128, 129, 1000, 4095, 4096, 8000, 8191])
+    scale = 1 / math.sqrt(w.d)
+    G = w.n_q // w.n_kv
+    for b in (0, 3):
+        for h in (0, 13, 31):
+            Kh = f64(k[b, :, h // G])
+            Vh = f64(v[b, :, h // G])
+            Qh = f64(q[b, rows, h])
+            ref = A.attention(Qh, Kh, Vh, scale, q_pos=rows)
+            assert_close(f64(out[b, rows, h]), ref, what=f"prefill seq {b} head {h}")
+    gk, gv = c.gather(0, 2, 0, w.T)
+    assert torch.equal(gk.view(torch.int16), k[2].view(torch.int16))
+    assert torch.equal(gv.view(torch.int16), v[2].view(torch.int16))
