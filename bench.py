@@ -275,6 +275,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-prefill", action="store_true",
                     help="headline decode only (no prefill section)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device-to-device 5 times (calibrates the HBM "
+                         "byte counters read by rocprofv3 --pmc) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -283,6 +286,16 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_probe:
+        nbytes = args.copy_probe << 20
+        x = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+        y = torch.empty_like(x)
+        for _ in range(5):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": nbytes, "copy_probe_bytes_written": nbytes,
+                          "repeats": 5}))
+        return
     import kv_cache_flashattention_amd as kv
     kv.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"

@@ -13,8 +13,9 @@
 // Scores are kept in the base-2 domain: s2 = (q . k) * scale * log2(e), so
 // exp(s - m) = exp2(s2 - m2) and the hardware exp2 is used directly.
 //
-// This file holds the plan, the merge, and the portable VALU kernel used for
-// f32 caches (and for any shape the matrix-core kernel does not cover).
+// This file holds the plan and the portable VALU kernel (with its merge) used
+// for f32 caches; the matrix-core path for 16-bit and fp8 caches lives in
+// mfma_decode.hip.
 #include <algorithm>
 
 #include "common.h"
@@ -26,27 +27,34 @@ hipError_t launch_decode_mfma(const CacheView& cv, int layer, int n, const int32
                               const void* q, void* out, float scale_log2, const DecodePlan& plan,
                               void* ws, hipStream_t s, bool* handled);
 
-DecodePlan make_decode_plan(const CacheView& cv, int32_t n, int32_t max_len, int32_t num_splits) {
-  DecodePlan p{1, 64, 0};
+DecodePlan make_decode_plan(const CacheView& cv, int32_t n, int32_t max_len, int32_t num_splits,
+                            int32_t cu_count) {
+  DecodePlan p{0, 1, 64, 0, 0};
   if (max_len <= 0 || n <= 0) return p;
-  // Splits are whole multiples of 256 tokens (four waves x 64-token chunks)
-  // when chosen automatically, of 64 tokens when the caller fixes the count.
-  const int64_t chunks = (max_len + 63) / 64;               // 64-token units
-  int64_t splits, unit;
+  if (cv.dtype != KVC_F32) {
+    // Work list: every wave of a full chip gets an equal share; with an
+    // explicit num_splits, about that many pieces per (sequence, group).
+    const int nb = n < kMaxBatch ? n : kMaxBatch;
+    const int64_t groups = (int64_t)nb * cv.n_kv * ((cv.n_q / cv.n_kv + 15) / 16);
+    int64_t waves = num_splits > 0
+                        ? groups * num_splits
+                        : (int64_t)std::max(cu_count, 1) * work_list_waves_per_cu(cv);
+    waves = std::max<int64_t>(4, std::min<int64_t>(waves, (int64_t)1 << 24));
+    p.work_list = 1;
+    p.waves = (int32_t)waves;
+    p.ws_bytes = work_list_ws_bytes(cv, nb, p.waves);
+    return p;
+  }
+  // VALU splits: whole multiples of 64 tokens.
+  const int64_t chunks = (max_len + 63) / 64;
+  int64_t splits;
   if (num_splits > 0) {
     splits = std::min<int64_t>(num_splits, chunks);
-    unit = 1;
   } else {
-    // Enough workgroups to cover the chip a few times over, but no split
-    // shorter than 256 tokens.
-    const int64_t groups = (int64_t)n * cv.n_kv * ((cv.n_q / cv.n_kv + 15) / 16);
-    const int64_t target = 2048;
-    splits = std::max<int64_t>(1, std::min<int64_t>((target + groups - 1) / groups,
-                                                    (chunks + 3) / 4));
-    unit = 4;
+    const int64_t heads = (int64_t)n * cv.n_q;
+    splits = std::max<int64_t>(1, std::min<int64_t>((2048 + heads - 1) / heads, chunks));
   }
-  int64_t per = (chunks + splits - 1) / splits;
-  per = (per + unit - 1) / unit * unit;
+  const int64_t per = (chunks + splits - 1) / splits;
   p.split_len = (int32_t)(per * 64);
   p.splits = (int32_t)((max_len + p.split_len - 1) / p.split_len);
   if (p.splits > 1)
@@ -231,27 +239,6 @@ hipError_t run_valu_d(const CacheView& cv, int layer, int n, const int32_t* seqs
 }
 
 }  // namespace
-
-// Merge launcher shared with the matrix-core kernels.
-hipError_t launch_decode_merge(const CacheView& cv, int n, const int32_t* seqs, void* out,
-                               const DecodePlan& p, const void* ws, hipStream_t st) {
-  const int io = io_dtype(cv.dtype);
-  dim3 grid(cv.n_q, n);
-#define KVFA_MERGE(IO, D) \
-  hipLaunchKernelGGL((k_decode_merge<IO, D>), grid, dim3(64), 0, st, cv, seqs, (IO*)out, ws, n, \
-                     p.splits, p.split_len)
-  if (cv.d == 128) {
-    if (io == KVC_F32) KVFA_MERGE(float, 128);
-    else if (io == KVC_F16) KVFA_MERGE(_Float16, 128);
-    else KVFA_MERGE(BF16, 128);
-  } else {
-    if (io == KVC_F32) KVFA_MERGE(float, 64);
-    else if (io == KVC_F16) KVFA_MERGE(_Float16, 64);
-    else KVFA_MERGE(BF16, 64);
-  }
-#undef KVFA_MERGE
-  return hipGetLastError();
-}
 
 hipError_t launch_decode(const CacheView& cv, int layer, int n, const int32_t* seqs,
                          const void* q, void* out, float scale, const DecodePlan& plan,

@@ -29,6 +29,7 @@ struct kvc_cache {
   std::vector<int32_t> len;                     // per sequence
   std::vector<uint8_t> live;                    // per sequence
   std::vector<uint8_t> owned;                   // per block: 1 if some sequence holds it
+  int32_t cu_count = 256;                       // compute units of the device (decode plan)
   CacheView view() const {
     CacheView v{};
     v.k = dev.k_pool;
@@ -181,6 +182,11 @@ int kvc_create(const kvc_config* cfg, const kvc_buffers* dev, hipStream_t stream
   if (dev) {
     c->has_dev = true;
     c->dev = *dev;
+    int device = 0, cus = 0;
+    if (hipGetDevice(&device) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess &&
+        cus > 0)
+      c->cu_count = cus;
     hipError_t e = launch_fill_tables(c->view(), stream);
     if (e != hipSuccess) {
       delete c;
@@ -391,7 +397,7 @@ int kvc_attn_prefill(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs
 int kvc_decode_workspace_bytes(const kvc_cache* c, int32_t n, int32_t num_splits, uint64_t* out) {
   if (!c || !out) return fail(KVC_E_INVAL, "NULL argument");
   if (n < 0 || num_splits < 0) return fail(KVC_E_INVAL, "negative size");
-  DecodePlan p = make_decode_plan(c->view(), n, live_max_len(c), num_splits);
+  DecodePlan p = make_decode_plan(c->view(), n, live_max_len(c), num_splits, c->cu_count);
   *out = p.ws_bytes;
   return KVC_OK;
 }
@@ -410,7 +416,7 @@ int kvc_attn_decode(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs,
   if (!aligned16(q) || !aligned16(out)) return fail(KVC_E_INVAL, "q/out must be 16-byte aligned");
   int32_t max_len = live_max_len(c);
   if (max_len <= 0) return fail(KVC_E_STATE, "no live sequence holds any token");
-  DecodePlan p = make_decode_plan(c->view(), n, max_len, num_splits);
+  DecodePlan p = make_decode_plan(c->view(), n, max_len, num_splits, c->cu_count);
   if (p.ws_bytes > 0 && (!ws || ws_bytes < p.ws_bytes))
     return fail(KVC_E_WORKSPACE, "workspace too small: need " + std::to_string(p.ws_bytes) +
                                      " bytes");

@@ -32,11 +32,23 @@ struct TableUpdate {
   int32_t val[kTableUpdateMax];
 };
 
-// How one decode call cuts the longest context into splits.
+// How one decode call divides its work.
+//  * Matrix-core path (16-bit and fp8 caches): a work list.  The batch's
+//    32-token units, over every (sequence, kv-head group), are cut into
+//    `waves` equal contiguous ranges, one per wave; each wave leaves one
+//    (m, l, O) partial per piece of a (sequence, group) segment it covers and
+//    a merge combines the pieces.  Batches larger than kMaxBatch are run in
+//    sub-batches of at most kMaxBatch sequences.
+//  * VALU path (f32 caches): a grid of `splits` fixed-length splits per
+//    (sequence, query head), merged when splits > 1.
+constexpr int kMaxBatch = 2048;
+
 struct DecodePlan {
-  int32_t splits;     // splits per (sequence, kv head)
-  int32_t split_len;  // tokens per split, a multiple of 64
-  uint64_t ws_bytes;  // workspace for partial (m, l, O); 0 if splits == 1
+  int32_t work_list;  // 1: matrix-core work list, 0: VALU splits
+  int32_t splits;     // VALU: splits per sequence
+  int32_t split_len;  // VALU: tokens per split, a multiple of 64
+  int32_t waves;      // work list: waves sharing the work of one (sub-)batch
+  uint64_t ws_bytes;  // workspace bytes the call needs
 };
 
 inline int elem_bytes(int dtype) {
@@ -44,7 +56,10 @@ inline int elem_bytes(int dtype) {
 }
 inline int io_dtype(int dtype) { return dtype == KVC_FP8_E4M3FN ? KVC_BF16 : dtype; }
 
-DecodePlan make_decode_plan(const CacheView& cv, int32_t n, int32_t max_len, int32_t num_splits);
+DecodePlan make_decode_plan(const CacheView& cv, int32_t n, int32_t max_len, int32_t num_splits,
+                            int32_t cu_count);
+uint64_t work_list_ws_bytes(const CacheView& cv, int32_t nb, int32_t waves);
+int work_list_waves_per_cu(const CacheView& cv);
 
 // Launchers: return hipSuccess or the launch error.
 hipError_t launch_fill_tables(const CacheView& cv, hipStream_t s);

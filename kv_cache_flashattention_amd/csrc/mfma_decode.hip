@@ -1,40 +1,47 @@
 // Decode attention on the matrix cores (bf16 / fp16 / fp8 caches, d 64 or 128).
 //
-// Work unit: one workgroup of four waves per (split, kv head, group of up to
-// 16 query heads sharing that kv head, sequence), so each K/V byte of the
-// split is read once for the whole query group (grouped-query attention,
-// "KV Cache & Flash Attention." (kvcache-7e2) memory-cost section).  The
-// waves take 64-token chunks (four 16-token blocks) of the split in turn; per
-// chunk a wave
+// Work list.  The unit of work is 32 tokens (two 16-token blocks) of one
+// (sequence, kv-head group) segment, where a group is up to 16 query heads
+// sharing one kv head, so each K/V byte is read once for the whole query
+// group (grouped-query attention, "KV Cache & Flash Attention." (kvcache-7e2)
+// memory-cost section).  Every workgroup first turns the batch's lengths into
+// prefix sums of unit counts (in LDS); the W units of the batch are then cut
+// into `waves` equal contiguous ranges, one per wave, whatever the mix of
+// lengths.  A wave sweeps its range segment piece by segment piece; per unit
+// it
 //   1. computes S^T = K Q^T with 16x16x32 MFMAs: the 16 M-rows are tokens,
 //      the 16 N-columns are the query rows (padded with zeros), K = head dim;
 //   2. updates the running max m and sum l of each query row and rescales
 //      its output by exp(m_old - m_new) (kvcache-7e2, online softmax
 //      section), all in fp32;
-//   3. computes O^T += V^T P^T with MFMAs over the chunk's tokens.
-// The waves' (m, l, O) are combined through LDS at the end; with one split
-// the workgroup writes O / l, otherwise it leaves (m, l, O) for the merge.
+//   3. computes O^T += V^T P^T with MFMAs over the unit's 32 tokens.
+// Units are double-buffered in registers: the next unit's K/V loads are
+// issued before the current unit is computed, so a wave keeps HBM reads in
+// flight while it computes.  At the end of each piece the wave writes its
+// (m, l, O) to workspace slot (segment + wave), so the pieces of a segment
+// occupy consecutive slots; a merge kernel combines them with weights
+// exp(m_s - max m) -- the online softmax's rescale applied across pieces --
+// and writes O / l.
 //
 // Operand placement.  A 16x16x32 MFMA lane l holds, for its operand, row (or
 // column) l % 16 and a group of 8 reduction indices chosen by l / 16; the
 // reduction indices may be assigned in any order as long as both operands
 // agree.  K slabs are [16][d], so a lane loads 16 bytes of one token's row
 // for QK^T.  For PV the reduction runs over tokens, and the V slabs are
-// [d][16], so a lane loads 8 (or, for fp8, 16) consecutive tokens of one
-// head-dimension column.  Which token each S^T row holds is chosen so that
-// the probabilities a lane ends up with are exactly the tokens its V
-// operand covers: no data moves between lanes except the row max/sum.
+// [d][16], so a lane loads 8 consecutive tokens of one head-dimension column.
+// Which token each S^T row holds is chosen so that the probabilities a lane
+// ends up with are exactly the tokens its V operand covers: no data moves
+// between lanes except the row max/sum.
 //
 // fp8: codes are widened to bf16 exactly (every E4M3FN value is a bf16
 // value); the block's K scale multiplies its scores and its V scale the
 // probabilities before they are rounded to bf16; the running sum l uses the
 // unscaled probabilities.
+#include <hip/hip_runtime.h>
+
 #include "common.h"
 
 namespace kvfa {
-
-hipError_t launch_decode_merge(const CacheView& cv, int n, const int32_t* seqs, void* out,
-                               const DecodePlan& p, const void* ws, hipStream_t st);
 
 namespace {
 
@@ -89,212 +96,280 @@ template <int KV> __device__ __forceinline__ int dmap(int ks, int g) {
   return 32 * ks + 8 * g;
 }
 
-// Token held by row r of S^T tile t (t = 0..3) within a 64-token chunk:
-// block (0..3) and slot (0..15).  After the MFMA, lane group g holds rows
-// 4g..4g+3 of every tile; the PV k-step s takes tiles 2s and 2s+1, and its
-// operand slot j = 4u + i of lane group g is row 4g+i of tile 2s+u.
-template <int KV> __device__ __forceinline__ int tok_block(int t, int r) {
-  if (KV == KV_FP8) return r >> 2;                        // group g <-> block g
-  return 2 * (t >> 1) + (r >> 3);                         // group g <-> block 2s+(g>>1)
+// Token of a 32-token unit held by row r of S^T tile t (t = 0, 1): block
+// r >> 3 and slot 8*((r >> 2) & 1) + 4t + (r & 3).  After the MFMA, lane
+// group g holds rows 4g..4g+3 of both tiles, i.e. block g >> 1, slots
+// 8*(g & 1) + 4t + i: exactly the 8 consecutive slots its PV operand covers
+// (slot j = 4t + i of the k-step).
+__device__ __forceinline__ int tok_block(int r) { return r >> 3; }
+__device__ __forceinline__ int tok_slot(int t, int r) { return 8 * ((r >> 2) & 1) + 4 * t + (r & 3); }
+
+// One unit's loaded K/V operands (registers).
+template <int KV, int D> struct Unit {
+  static constexpr int KS = D / 32;                    // k-steps of QK^T
+  static constexpr int DT = D / 16;                    // 16-row tiles of O^T
+  static constexpr int KL = KV == KV_FP8 ? KS / 2 : KS;  // 16-byte K loads per tile
+  uint4 k[2][KL];
+  uint4 v[KV == KV_FP8 ? DT / 2 : DT];                 // fp8: 8-byte loads, two per uint4
+  int64_t sidx[2];                                     // scale index of each block
+};
+
+// Workspace of one (sub-)batch: O [slots][16][D] f32, m [slots][16],
+// l [slots][16], then the batch's unit prefix sums [nb+1] (int64) and unit
+// counts [nb] (int32) for the merge.
+struct WorkWs {
+  float* O;
+  float* m;
+  float* l;
+  int64_t* units;
+  int32_t* counts;
+};
+
+__host__ __device__ inline int64_t work_slots(int nb, int nkvg, int waves) {
+  return (int64_t)nb * nkvg + waves;
 }
-template <int KV> __device__ __forceinline__ int tok_slot(int t, int r) {
-  if (KV == KV_FP8) return 4 * t + (r & 3);               // slots 8s..8s+7 per k-step
-  return 8 * ((r >> 2) & 1) + 4 * (t & 1) + (r & 3);      // slots 8(g&1)..+7
+
+__device__ __forceinline__ WorkWs work_ws(void* ws, int64_t slots, int D, int nb) {
+  WorkWs w;
+  w.O = (float*)ws;
+  w.m = w.O + slots * 16 * D;
+  w.l = w.m + slots * 16;
+  w.units = (int64_t*)(w.l + slots * 16);   // slots*16*(D+2) floats: 8-byte aligned
+  w.counts = (int32_t*)(w.units + nb + 1);
+  return w;
 }
+
+// floor(a * W / P) without overflow: W = qP + r.
+__device__ __forceinline__ int64_t share(int64_t a, int64_t W, int64_t P) {
+  return a * (W / P) + (a * (W % P)) / P;
+}
+
+constexpr int kUnit = 32;   // tokens per work unit
 
 template <int KV, int D>
-__global__ __launch_bounds__(256, 2) void k_decode_mfma(CacheView cv, int layer,
+__global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
                                                         const int32_t* seqs, const uint16_t* q,
-                                                        uint16_t* out, void* ws, int n,
-                                                        int splits, int split_len, float sl2,
-                                                        int qgroups) {
+                                                        void* ws, int nb, int qgroups, int waves,
+                                                        float sl2) {
   typedef typename Op<KV>::T OpT;
-  constexpr int KS = D / 32;     // k-steps of QK^T
-  constexpr int DT = D / 16;     // 16-row tiles of O^T
+  typedef Unit<KV, D> U;
+  constexpr int KS = U::KS, DT = U::DT, KL = U::KL;
   constexpr int EB = KV == KV_FP8 ? 1 : 2;
-  __shared__ float sO[4][16][D + 1];
-  __shared__ float sm[4][16], sl[4][16];
+  __shared__ int64_t s_units[kMaxBatch + 1];
+  __shared__ int32_t s_counts[kMaxBatch];
+  __shared__ int64_t s_wsum[4];
 
-  const int s = blockIdx.x, kvh = blockIdx.y / qgroups, qg = blockIdx.y % qgroups;
-  const int b = blockIdx.z;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   const int G = cv.n_q / cv.n_kv;
-  const int seq = seqs[b];
-  const int L = valid_len(cv, seq);
-  if (L < 0) {
-    if (splits == 1) {
-      for (int e = threadIdx.x; e < 16 * D; e += 256) {
-        const int qi = qg * 16 + e / D;
-        if (qi < G)
-          out[((int64_t)b * cv.n_q + kvh * G + qi) * D + e % D] = 0x7FC0;   // NaN
-      }
-    }
-    return;
-  }
-  const int t0 = s * split_len;
-  if (t0 >= L) return;
-  const int t1 = min(t0 + split_len, L);
+  const int nkvg = cv.n_kv * qgroups;
+  const int64_t slots = work_slots(nb, nkvg, waves);
+  WorkWs W_ = work_ws(ws, slots, D, nb);
 
-  // Query operand (B of S^T = K Q^T): column r16 = query row qg*16 + r16.
-  const int qi = qg * 16 + r16;
-  const bool qrow = qi < G;
-  OpT qop[KS];
+  // ---- unit counts and their prefix sums (8 entries per thread, nb <= 2048)
   {
-    const uint16_t* qr = q + ((int64_t)b * cv.n_q + kvh * G + (qrow ? qi : 0)) * D;
+    int64_t loc[8], tsum = 0;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 raw = qrow ? *(const uint4*)(qr + dmap<KV>(ks, g)) : make_uint4(0, 0, 0, 0);
-      qop[ks] = __builtin_bit_cast(OpT, raw);
+    for (int i = 0; i < 8; ++i) {
+      const int b = tid * 8 + i;
+      int c = 0;
+      if (b < nb) {
+        const int L = valid_len(cv, seqs[b]);
+        c = L > 0 ? (L + kUnit - 1) / kUnit : 0;
+        s_counts[b] = c;
+      }
+      loc[i] = (int64_t)c * nkvg;
+      tsum += loc[i];
+    }
+    int64_t x = tsum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) s_wsum[tid >> 6] = x;
+    __syncthreads();
+    int64_t ex = x - tsum;
+    for (int i = 0; i < (tid >> 6); ++i) ex += s_wsum[i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int b = tid * 8 + i;
+      if (b < nb) s_units[b] = ex;
+      ex += loc[i];
+    }
+    if (tid == 0) s_units[nb] = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+    __syncthreads();
+    if (blockIdx.x == 0) {
+      for (int b = tid; b <= nb; b += 256) W_.units[b] = s_units[b];
+      for (int b = tid; b < nb; b += 256) W_.counts[b] = s_counts[b];
     }
   }
 
-  f32x4 o[DT];
-#pragma unroll
-  for (int i = 0; i < DT; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, lpart = 0.f;
-  bool bad = false;
+  const int gw = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t Wt = s_units[nb];
+  if (gw >= waves || Wt == 0) return;
+  int64_t u = share(gw, Wt, waves);
+  const int64_t u1 = share(gw + 1, Wt, waves);
 
-  const int32_t* btrow = cv.bt + (int64_t)seq * cv.max_bps;
+  // entry holding unit u: the last b with s_units[b] <= u (entries without
+  // units share their offset with the next entry and are skipped this way)
+  int b = 0;
+  {
+    int lo = 0, hi = nb - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_units[mid] <= u) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+  }
+
   const uint8_t* kpool = (const uint8_t*)cv.k;
   const uint8_t* vpool = (const uint8_t*)cv.v;
   const int64_t slab_bytes = (int64_t)kBlock * D * EB;
   const int64_t layer_blocks = (int64_t)layer * cv.n_blocks;
-  const int nchunks = (t1 - t0 + 63) / 64;
-  const int last_blk = (L - 1) / kBlock;             // last table entry of the sequence
-  const int wu = __builtin_amdgcn_readfirstlane(w);   // wave index as a scalar
 
-  for (int ci = wu; ci < nchunks; ci += 4) {
-    const int c = t0 + ci * 64;
-    const int nvalid = min(64, t1 - c);
-    const bool tail = nvalid < 64;
-    // Table entries of the chunk's four blocks (entries past the sequence's
-    // end are clamped to its last block; their tokens are masked below).
-    int64_t sbase[4];
-    int64_t sidx[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int x = btrow[min(c / kBlock + i, last_blk)];
-      if (x < 0 || x >= cv.n_blocks) {
-        bad = true;
-        x = 0;
-      }
-      sidx[i] = (layer_blocks + x) * cv.n_kv + kvh;
-      sbase[i] = sidx[i] * slab_bytes;
-    }
-    auto pick = [&](const int64_t* a, int i) -> int64_t {
-      return i == 0 ? a[0] : i == 1 ? a[1] : i == 2 ? a[2] : a[3];
-    };
+  while (u < u1) {
+    while (s_units[b + 1] <= u) ++b;                 // skip to the entry holding u
+    const int cb = s_counts[b];
+    const int64_t rem = u - s_units[b];
+    const int kvg = (int)(rem / cb);
+    const int c0 = (int)(rem % cb);
+    const int64_t segend = s_units[b] + (int64_t)(kvg + 1) * cb;
+    const int64_t pend = u1 < segend ? u1 : segend;
+    const int c1 = c0 + (int)(pend - u);
+    const int kvh = kvg / qgroups, qg = kvg % qgroups;
+    const int seq = seqs[b];
+    const int L = valid_len(cv, seq);                  // > 0: the entry has units
 
-    // ---- issue every K and V load of the chunk before using any
-    constexpr int KL = KV == KV_FP8 ? KS / 2 : KS;      // 16-byte K loads per tile
-    constexpr int VL = KV == KV_FP8 ? DT : 2 * DT;      // 16-byte V loads per chunk
-    uint4 kraw[4][KL];
-    uint4 vraw[VL];
+    // Query operand (B of S^T = K Q^T): column r16 = query row qg*16 + r16.
+    const int qi = qg * 16 + r16;
+    const bool qrow = qi < G;
+    OpT qop[KS];
+    {
+      const uint16_t* qr = q + ((int64_t)b * cv.n_q + kvh * G + (qrow ? qi : 0)) * D;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const uint8_t* krow = kpool + pick(sbase, tok_block<KV>(t, r16)) +
-                            (int64_t)tok_slot<KV>(t, r16) * D * EB;
-#pragma unroll
-      for (int a = 0; a < KL; ++a) {
-        const int off = KV == KV_FP8 ? 64 * a + 16 * g : 2 * dmap<KV>(a, g);
-        kraw[t][a] = *(const uint4*)(krow + off);
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 raw = qrow ? *(const uint4*)(qr + dmap<KV>(ks, g)) : make_uint4(0, 0, 0, 0);
+        qop[ks] = __builtin_bit_cast(OpT, raw);
       }
     }
-    if (KV == KV_FP8) {
-      const uint8_t* vslab = vpool + pick(sbase, g);
+
+    f32x4 o[DT];
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) vraw[dt] = *(const uint4*)(vslab + (16 * dt + r16) * kBlock);
-    } else {
+    for (int i = 0; i < DT; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, lpart = 0.f;
+    bool bad = false;
+    const int32_t* btrow = cv.bt + (int64_t)seq * cv.max_bps;
+    const int last_blk = (L - 1) / kBlock;
+
+    // Issue every load of unit c into buffer B (table entries past the
+    // sequence's end are clamped to its last block; their tokens are masked).
+    auto issue = [&](U& B, int c) {
+      int64_t sbase[2];
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const uint8_t* vslab = vpool + pick(sbase, 2 * st + (g >> 1));
+      for (int i = 0; i < 2; ++i) {
+        int x = btrow[min(2 * c + i, last_blk)];
+        if (x < 0 || x >= cv.n_blocks) {
+          bad = true;
+          x = 0;
+        }
+        B.sidx[i] = (layer_blocks + x) * cv.n_kv + kvh;
+        sbase[i] = B.sidx[i] * slab_bytes;
+      }
+      const uint8_t* krow = kpool + (tok_block(r16) ? sbase[1] : sbase[0]);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int a = 0; a < KL; ++a) {
+          const int off = KV == KV_FP8 ? 64 * a + 16 * g : 2 * dmap<KV>(a, g);
+          B.k[t][a] = *(const uint4*)(krow + (int64_t)tok_slot(t, r16) * D * EB + off);
+        }
+      const uint8_t* vslab = vpool + ((g >> 1) ? sbase[1] : sbase[0]) + 8 * (g & 1) * EB;
+      if (KV == KV_FP8) {
+#pragma unroll
+        for (int dt = 0; dt < DT; dt += 2) {
+          const uint2 lo = *(const uint2*)(vslab + (16 * dt + r16) * kBlock);
+          const uint2 hi = *(const uint2*)(vslab + (16 * (dt + 1) + r16) * kBlock);
+          B.v[dt / 2] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
+      } else {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          vraw[st * DT + dt] =
-              *(const uint4*)(vslab + 2 * ((16 * dt + r16) * kBlock + 8 * (g & 1)));
+          B.v[dt] = *(const uint4*)(vslab + 2 * (16 * dt + r16) * kBlock);
       }
-    }
+    };
 
-    // ---- S^T = K Q^T for four 16-token tiles
-    f32x4 sacc[4];
+    // Fold unit c (loaded in B) into (m, l, O).
+    auto compute = [&](const U& B, int c) {
+      const int nvalid = min(kUnit, L - c * kUnit);
+      const bool tail = nvalid < kUnit;
+      // ---- S^T = K Q^T, two 16-token tiles
+      f32x4 sacc[2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < 2; ++t) {
+        sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int a = 0; a < KL; ++a) {
-        if (KV == KV_FP8) {
-          sacc[t] = mfma(__builtin_bit_cast(OpT, fp8x8_to_bf16(kraw[t][a].x, kraw[t][a].y)),
-                         qop[2 * a], sacc[t]);
-          sacc[t] = mfma(__builtin_bit_cast(OpT, fp8x8_to_bf16(kraw[t][a].z, kraw[t][a].w)),
-                         qop[2 * a + 1], sacc[t]);
-        } else {
-          sacc[t] = mfma(__builtin_bit_cast(OpT, kraw[t][a]), qop[a], sacc[t]);
+        for (int a = 0; a < KL; ++a) {
+          if (KV == KV_FP8) {
+            sacc[t] = mfma(__builtin_bit_cast(OpT, fp8x8_to_bf16(B.k[t][a].x, B.k[t][a].y)),
+                           qop[2 * a], sacc[t]);
+            sacc[t] = mfma(__builtin_bit_cast(OpT, fp8x8_to_bf16(B.k[t][a].z, B.k[t][a].w)),
+                           qop[2 * a + 1], sacc[t]);
+          } else {
+            sacc[t] = mfma(__builtin_bit_cast(OpT, B.k[t][a]), qop[a], sacc[t]);
+          }
         }
       }
-    }
-
-    // ---- online softmax over the chunk (this lane's S^T column: query r16)
-    float ksc = 1.f, vsc = 1.f;
-    if (KV == KV_FP8) {
-      const int64_t si = pick(sidx, g);
-      ksc = cv.ks[si];
-      vsc = cv.vs[si];
-    }
-    float p[4][4];
-    float cmax = -INFINITY;
+      // ---- online softmax (this lane's S^T column: query r16; its values
+      // are tokens 16*(g>>1) + 8*(g&1) + 4t + i of the unit)
+      float ksc = 1.f, vsc = 1.f;
+      if (KV == KV_FP8) {
+        const int64_t si = (g >> 1) ? B.sidx[1] : B.sidx[0];
+        ksc = cv.ks[si];
+        vsc = cv.vs[si];
+      }
+      const int pos0 = 16 * (g >> 1) + 8 * (g & 1);
+      float p[2][4];
+      float cmax = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x = sacc[t][i] * (sl2 * ksc);
-        if (tail) {
-          const int r = 4 * g + i;
-          const int pos = 16 * tok_block<KV>(t, r) + tok_slot<KV>(t, r);
-          if (pos >= nvalid) x = -INFINITY;
+        for (int i = 0; i < 4; ++i) {
+          float x = sacc[t][i] * (sl2 * ksc);
+          if (tail && pos0 + 4 * t + i >= nvalid) x = -INFINITY;
+          p[t][i] = x;
+          cmax = fmaxf(cmax, x);
         }
-        p[t][i] = x;
-        cmax = fmaxf(cmax, x);
-      }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-    const float m_new = fmaxf(m, cmax);
-    const float alpha = m == -INFINITY ? 0.f : exp2f(m - m_new);
-    float psum = 0.f;
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+      const float m_new = fmaxf(m, cmax);
+      const float alpha = m == -INFINITY ? 0.f : exp2f(m - m_new);
+      float psum = 0.f, pv[8];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[t][i] = exp2f(p[t][i] - m_new);
-        psum += p[t][i];
-      }
-    lpart = lpart * alpha + psum;
-    m = m_new;
+        for (int i = 0; i < 4; ++i) {
+          const float e = exp2f(p[t][i] - m_new);
+          psum += e;
+          pv[4 * t + i] = e * vsc;
+        }
+      lpart = lpart * alpha + psum;
+      m = m_new;
 #pragma unroll
-    for (int i = 0; i < DT; ++i) o[i] *= alpha;
-
-    // ---- O^T += V^T P^T, two k-steps of 32 tokens
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      float pv[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pv[j] = p[2 * st + (j >> 2)][j & 3] * vsc;
+      for (int i = 0; i < DT; ++i) o[i] *= alpha;
+      // ---- O^T += V^T P^T over the unit's 32 tokens; in a sequence's last
+      // unit, V slots past its end are zeroed (they may hold stale or
+      // poisoned bytes, and 0 * NaN would poison O)
       const OpT pop = pack8<OpT>(pv);
-      // This lane's V operand covers block bi, slots s0..s0+7 of the chunk;
-      // in the chunk holding the split's end, slots past it are zeroed (they
-      // may hold stale or poisoned bytes, and 0 * NaN would poison O).
-      const int bi = KV == KV_FP8 ? g : 2 * st + (g >> 1);
-      const int s0 = KV == KV_FP8 ? 8 * st : 8 * (g & 1);
-      const int nok = tail ? nvalid - 16 * bi - s0 : 8;  // valid slots among the 8
+      const int nok = tail ? nvalid - pos0 : 8;       // valid slots among the lane's 8
       uint32_t keep[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if (KV == KV_FP8) {        // 4 one-byte slots per dword, dwords 0..1 used
-          const int base = 4 * e;
+        if (KV == KV_FP8) {
           uint32_t mk = 0;
 #pragma unroll
-          for (int y = 0; y < 4; ++y) mk |= (base + y < nok ? 0xFFu : 0u) << (8 * y);
+          for (int y = 0; y < 4; ++y) mk |= ((4 * (e & 1) + y) < nok ? 0xFFu : 0u) << (8 * y);
           keep[e] = mk;
-        } else {                   // 2 two-byte slots per dword
+        } else {
           keep[e] = (2 * e < nok ? 0xFFFFu : 0u) | (2 * e + 1 < nok ? 0xFFFF0000u : 0u);
         }
       }
@@ -302,62 +377,139 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(CacheView cv, int layer,
       for (int dt = 0; dt < DT; ++dt) {
         OpT vop;
         if (KV == KV_FP8) {
-          const uint32_t lo = (st == 0 ? vraw[dt].x : vraw[dt].z) & keep[0];
-          const uint32_t hi = (st == 0 ? vraw[dt].y : vraw[dt].w) & keep[1];
+          const uint4 w4 = B.v[dt / 2];
+          const uint32_t lo = ((dt & 1) ? w4.z : w4.x) & keep[0];
+          const uint32_t hi = ((dt & 1) ? w4.w : w4.y) & keep[1];
           vop = __builtin_bit_cast(OpT, fp8x8_to_bf16(lo, hi));
         } else {
-          const uint4 raw = vraw[st * DT + dt];
+          const uint4 raw = B.v[dt];
           vop = __builtin_bit_cast(OpT, make_uint4(raw.x & keep[0], raw.y & keep[1],
                                                    raw.z & keep[2], raw.w & keep[3]));
         }
         o[dt] = mfma(vop, pop, o[dt]);
       }
-    }
-  }
+    };
 
-  // ---- combine the four waves
-  float l = lpart + __shfl_xor(lpart, 16, 64);
-  l += __shfl_xor(l, 32, 64);
-  if (bad) l = __builtin_nanf("");
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sO[w][r16][16 * dt + 4 * g + i] = o[dt][i];
-  if (g == 0) {
-    sm[w][r16] = m;
-    sl[w][r16] = l;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < 16 * D; e += 256) {
-    const int qq = e / D, d = e % D;
-    const int qi2 = qg * 16 + qq;
-    if (qi2 >= G) continue;
-    float M = -INFINITY;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sm[ww][qq]);
-    float acc = 0.f, lsum = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
-      const float f = sm[ww][qq] == -INFINITY ? 0.f : exp2f(sm[ww][qq] - M);
-      acc += f * sO[ww][qq][d];
-      lsum += f * sl[ww][qq];
+    // Two buffers, alternating: unit c+1's loads go out before unit c is
+    // computed.
+    U A, Bb;
+    issue(A, c0);
+    for (int c = c0; c < c1; c += 2) {
+      if (c + 1 < c1) issue(Bb, c + 1);
+      compute(A, c);
+      if (c + 2 < c1) issue(A, c + 2);
+      if (c + 1 < c1) compute(Bb, c + 1);
     }
-    const int h = kvh * G + qi2;
-    if (splits == 1) {
-      const float y = acc / lsum;
-      out[((int64_t)b * cv.n_q + h) * D + d] =
-          KV == KV_F16 ? __builtin_bit_cast(uint16_t, (_Float16)y) : f32_to_bf16_bits(y);
-    } else {
-      float* PO = (float*)ws;
-      float* Pm = PO + (int64_t)n * cv.n_q * splits * D;
-      float* Pl = Pm + (int64_t)n * cv.n_q * splits;
-      const int64_t r = ((int64_t)b * cv.n_q + h) * splits + s;
-      PO[r * D + d] = acc;
-      if (d == 0) {
-        Pm[r] = M;
-        Pl[r] = lsum;
+
+    // ---- piece done: (m, l, O) of this wave's query rows to slot (segment + wave)
+    float l = lpart + __shfl_xor(lpart, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (bad) l = __builtin_nanf("");
+    const int64_t slot = (int64_t)b * nkvg + kvg + gw;
+    if (qrow) {
+      float* Orow = W_.O + (slot * 16 + r16) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *(float4*)(Orow + 16 * dt + 4 * g) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+      if (g == 0) {
+        W_.m[slot * 16 + r16] = m;
+        W_.l[slot * 16 + r16] = l;
       }
     }
+    u = pend;
+  }
+}
+
+// Merge of the pieces of every (sequence, query head): the pieces of segment
+// s are in slots s + w for the waves w whose ranges meet the segment.
+// M = max m, weights exp2(m - M), out = sum w O / sum w l.  One workgroup of
+// four waves per (query head, sequence): each wave folds every fourth piece
+// into its own running (M, den, acc) -- the same online rescale, four pieces
+// per step so their loads are in flight together -- and the four waves are
+// combined through LDS.  An entry without units (invalid) gets NaN.
+template <bool F16, int D>
+__global__ __launch_bounds__(256) void k_decode_work_merge(CacheView cv, const void* ws_,
+                                                           uint16_t* out, int nb, int qgroups,
+                                                           int waves) {
+  constexpr int J = D / 64;
+  constexpr int UN = 4;
+  __shared__ float sM[4], sDen[4], sAcc[4][D];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int wv = tid >> 6;
+  const int G = cv.n_q / cv.n_kv;
+  const int nkvg = cv.n_kv * qgroups;
+  const int kvh = h / G, qi = h % G, kvg = kvh * qgroups + qi / 16, r = qi % 16;
+  const int64_t slots = work_slots(nb, nkvg, waves);
+  WorkWs W_ = work_ws((void*)ws_, slots, D, nb);
+  uint16_t* orow = out + ((int64_t)b * cv.n_q + h) * D;
+  const int cb = W_.counts[b];
+  const int64_t Wt = W_.units[nb];
+  if (cb == 0 || Wt == 0) {
+    for (int j = tid; j < D; j += 256) orow[j] = F16 ? 0x7E00 : 0x7FC0;   // NaN
+    return;
+  }
+  const int64_t q_ = Wt / waves, r_ = Wt % waves;
+  auto start_of = [&](int64_t w) -> int64_t { return w * q_ + (w * r_) / waves; };
+  // wave holding unit x: the largest w with floor(w W / P) <= x, which is
+  // floor(((x + 1) P - 1) / W)
+  auto wave_of = [&](int64_t x) -> int64_t { return ((x + 1) * waves - 1) / Wt; };
+  const int64_t s0 = W_.units[b] + (int64_t)kvg * cb;             // first unit
+  const int64_t w0 = wave_of(s0), w1 = wave_of(s0 + cb - 1);
+  const bool some_empty = q_ == 0;                                 // fewer units than waves
+  const int64_t seg = (int64_t)b * nkvg + kvg;
+
+  float M = -INFINITY, den = 0.f, acc[J];
+#pragma unroll
+  for (int i = 0; i < J; ++i) acc[i] = 0.f;
+  for (int64_t w = w0 + wv; w <= w1; w += 4 * UN) {
+    float pm[UN], pl[UN], po[UN][J];
+#pragma unroll
+    for (int k = 0; k < UN; ++k) {
+      const int64_t ww = w + 4 * k;
+      // waves whose range is empty wrote nothing
+      const bool ok = ww <= w1 && (!some_empty || start_of(ww) != start_of(ww + 1));
+      const int64_t sl = ok ? seg + ww : 0;
+      pm[k] = ok ? W_.m[sl * 16 + r] : -INFINITY;
+      pl[k] = ok ? W_.l[sl * 16 + r] : 0.f;
+#pragma unroll
+      for (int i = 0; i < J; ++i) po[k][i] = ok ? W_.O[(sl * 16 + r) * D + lane + 64 * i] : 0.f;
+    }
+    float Mn = M;
+#pragma unroll
+    for (int k = 0; k < UN; ++k) Mn = fmaxf(Mn, pm[k]);
+    if (Mn == -INFINITY) continue;
+    const float a = M == -INFINITY ? 0.f : exp2f(M - Mn);
+    den *= a;
+#pragma unroll
+    for (int i = 0; i < J; ++i) acc[i] *= a;
+#pragma unroll
+    for (int k = 0; k < UN; ++k) {
+      const float f = pm[k] == -INFINITY ? 0.f : exp2f(pm[k] - Mn);
+      den += f * pl[k];
+#pragma unroll
+      for (int i = 0; i < J; ++i) acc[i] += f * po[k][i];
+    }
+    M = Mn;
+  }
+  if (lane == 0) {
+    sM[wv] = M;
+    sDen[wv] = den;
+  }
+#pragma unroll
+  for (int i = 0; i < J; ++i) sAcc[wv][lane + 64 * i] = acc[i];
+  __syncthreads();
+  const float Mt = fmaxf(fmaxf(sM[0], sM[1]), fmaxf(sM[2], sM[3]));
+  float f[4], dt = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    f[k] = sM[k] == -INFINITY ? 0.f : exp2f(sM[k] - Mt);
+    dt += f[k] * sDen[k];
+  }
+  const float inv = 1.f / dt;
+  for (int j = tid; j < D; j += 256) {
+    const float y = (f[0] * sAcc[0][j] + f[1] * sAcc[1][j] + f[2] * sAcc[2][j] +
+                     f[3] * sAcc[3][j]) * inv;
+    orow[j] = F16 ? __builtin_bit_cast(uint16_t, (_Float16)y) : f32_to_bf16_bits(y);
   }
 }
 
@@ -366,31 +518,72 @@ hipError_t run(const CacheView& cv, int layer, int n, const int32_t* seqs, const
                void* out, float sl2, const DecodePlan& p, void* ws, hipStream_t st) {
   const int G = cv.n_q / cv.n_kv;
   const int qgroups = (G + 15) / 16;
-  hipLaunchKernelGGL((k_decode_mfma<KV, D>), dim3(p.splits, cv.n_kv * qgroups, n), dim3(256), 0,
-                     st, cv, layer, seqs, (const uint16_t*)q, (uint16_t*)out, ws, n, p.splits,
-                     p.split_len, sl2, qgroups);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.splits == 1) return e;
-  return launch_decode_merge(cv, n, seqs, out, p, ws, st);
+  const int grid = (p.waves + 3) / 4;
+  for (int b0 = 0; b0 < n; b0 += kMaxBatch) {
+    const int nb = n - b0 < kMaxBatch ? n - b0 : kMaxBatch;
+    const uint16_t* qb = (const uint16_t*)q + (int64_t)b0 * cv.n_q * D;
+    uint16_t* ob = (uint16_t*)out + (int64_t)b0 * cv.n_q * D;
+    hipLaunchKernelGGL((k_decode_work<KV, D>), dim3(grid), dim3(256), 0, st, cv, layer,
+                       seqs + b0, qb, ws, nb, qgroups, p.waves, sl2);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_decode_work_merge<KV == KV_F16, D>), dim3(cv.n_q, nb), dim3(256), 0, st,
+                       cv, (const void*)ws, ob, nb, qgroups, p.waves);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int KV, int D>
+int occupancy_waves() {
+  static int waves = 0;
+  if (waves == 0) {
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, (const void*)k_decode_work<KV, D>,
+                                                     256, 0) != hipSuccess || blocks < 1)
+      blocks = 2;
+    waves = 4 * blocks;
+  }
+  return waves;
 }
 
 }  // namespace
 
+uint64_t work_list_ws_bytes(const CacheView& cv, int32_t nb, int32_t waves) {
+  const int nkvg = cv.n_kv * ((cv.n_q / cv.n_kv + 15) / 16);
+  const int64_t slots = work_slots(nb, nkvg, waves);
+  return (uint64_t)slots * 16 * (cv.d + 2) * 4 + (uint64_t)(nb + 1) * 8 + (uint64_t)nb * 4 + 16;
+}
+
+// Waves one compute unit keeps resident for this cache's decode kernel (the
+// work list is cut for a full chip).  Host-only handles have no device to
+// ask and use 8.
+int work_list_waves_per_cu(const CacheView& cv) {
+  if (cv.k == nullptr) return 8;
+  if (cv.d == 128) {
+    if (cv.dtype == KVC_BF16) return occupancy_waves<KV_BF16, 128>();
+    if (cv.dtype == KVC_F16) return occupancy_waves<KV_F16, 128>();
+    return occupancy_waves<KV_FP8, 128>();
+  }
+  if (cv.dtype == KVC_BF16) return occupancy_waves<KV_BF16, 64>();
+  if (cv.dtype == KVC_F16) return occupancy_waves<KV_F16, 64>();
+  return occupancy_waves<KV_FP8, 64>();
+}
+
 hipError_t launch_decode_mfma(const CacheView& cv, int layer, int n, const int32_t* seqs,
                               const void* q, void* out, float sl2, const DecodePlan& p, void* ws,
                               hipStream_t st, bool* handled) {
-  *handled = true;
+  *handled = p.work_list != 0;
+  if (!*handled) return hipSuccess;
   if (cv.d == 128) {
     if (cv.dtype == KVC_BF16) return run<KV_BF16, 128>(cv, layer, n, seqs, q, out, sl2, p, ws, st);
     if (cv.dtype == KVC_F16) return run<KV_F16, 128>(cv, layer, n, seqs, q, out, sl2, p, ws, st);
-    if (cv.dtype == KVC_FP8_E4M3FN) return run<KV_FP8, 128>(cv, layer, n, seqs, q, out, sl2, p, ws, st);
-  } else if (cv.d == 64) {
-    if (cv.dtype == KVC_BF16) return run<KV_BF16, 64>(cv, layer, n, seqs, q, out, sl2, p, ws, st);
-    if (cv.dtype == KVC_F16) return run<KV_F16, 64>(cv, layer, n, seqs, q, out, sl2, p, ws, st);
-    if (cv.dtype == KVC_FP8_E4M3FN) return run<KV_FP8, 64>(cv, layer, n, seqs, q, out, sl2, p, ws, st);
+    return run<KV_FP8, 128>(cv, layer, n, seqs, q, out, sl2, p, ws, st);
   }
-  *handled = false;
-  return hipSuccess;
+  if (cv.dtype == KVC_BF16) return run<KV_BF16, 64>(cv, layer, n, seqs, q, out, sl2, p, ws, st);
+  if (cv.dtype == KVC_F16) return run<KV_F16, 64>(cv, layer, n, seqs, q, out, sl2, p, ws, st);
+  return run<KV_FP8, 64>(cv, layer, n, seqs, q, out, sl2, p, ws, st);
 }
 
 }  // namespace kvfa
