@@ -180,7 +180,9 @@ int kvc_write(kvc_cache* cache, int32_t layer, int32_t n, const int32_t* seqs_de
  * all in the io type.  When seqs_dev is not NULL the prompt's K/V rows are
  * also stored as positions 0..T-1 of those sequences (as kvc_write with
  * start 0; each sequence needs length >= T).  seqs_dev == NULL: attention
- * only.  scale is the score multiplier (1/sqrt(d_head) in the pages). */
+ * only.  scale is the score multiplier (1/sqrt(d_head) in the pages); it
+ * must be finite and > 0 (KVC_E_INVAL otherwise): the kernels take each row
+ * maximum on unscaled scores. */
 int kvc_attn_prefill(kvc_cache* cache, int32_t layer, int32_t n, const int32_t* seqs_dev,
                      int32_t T, const void* q_dev, const void* k_dev, const void* v_dev,
                      void* out_dev, float scale, hipStream_t stream);
@@ -198,7 +200,8 @@ int kvc_decode_workspace_bytes(const kvc_cache* cache, int32_t n, int32_t num_sp
  * merged afterwards with weights exp(m_s - max m) -- the online softmax's
  * rescale applied across splits.  num_splits: 0 = automatic, else the
  * number of splits of the longest sequence.  ws_dev: caller-owned workspace
- * of at least kvc_decode_workspace_bytes bytes (may be NULL if that is 0). */
+ * of at least kvc_decode_workspace_bytes bytes (may be NULL if that is 0).
+ * scale: finite and > 0, as for kvc_attn_prefill. */
 int kvc_attn_decode(kvc_cache* cache, int32_t layer, int32_t n, const int32_t* seqs_dev,
                     const void* q_dev, void* out_dev, float scale, int32_t num_splits,
                     void* ws_dev, uint64_t ws_bytes, hipStream_t stream);

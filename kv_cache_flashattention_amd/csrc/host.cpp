@@ -377,11 +377,12 @@ int kvc_attn_prefill(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs
                      const void* q, const void* k, const void* v, void* out, float scale,
                      hipStream_t stream) {
   if (!c) return fail(KVC_E_INVAL, "cache is NULL");
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(KVC_E_INVAL, "scale must be finite and positive");
   int r = need_dev(c);
   if (r) return r;
   if (layer < 0 || layer >= c->cfg.n_layers) return fail(KVC_E_STATE, "layer out of range");
   if (n < 0 || T < 0) return fail(KVC_E_INVAL, "negative size");
-  if (!std::isfinite(scale)) return fail(KVC_E_INVAL, "scale must be finite");
   if (n == 0 || T == 0) return KVC_OK;
   if (!q || !k || !v || !out) return fail(KVC_E_INVAL, "NULL device pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
@@ -406,11 +407,12 @@ int kvc_attn_decode(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs,
                     void* out, float scale, int32_t num_splits, void* ws, uint64_t ws_bytes,
                     hipStream_t stream) {
   if (!c) return fail(KVC_E_INVAL, "cache is NULL");
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(KVC_E_INVAL, "scale must be finite and positive");
   int r = need_dev(c);
   if (r) return r;
   if (layer < 0 || layer >= c->cfg.n_layers) return fail(KVC_E_STATE, "layer out of range");
   if (n < 0 || num_splits < 0) return fail(KVC_E_INVAL, "negative size");
-  if (!std::isfinite(scale)) return fail(KVC_E_INVAL, "scale must be finite");
   if (n == 0) return KVC_OK;
   if (!seqs || !q || !out) return fail(KVC_E_INVAL, "NULL device pointer");
   if (!aligned16(q) || !aligned16(out)) return fail(KVC_E_INVAL, "q/out must be 16-byte aligned");

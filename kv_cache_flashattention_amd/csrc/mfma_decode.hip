@@ -342,13 +342,13 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
       cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
       cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
       const float m_new = fmaxf(m, cmax);
-      const float alpha = m == -INFINITY ? 0.f : exp2f(m - m_new);
+      const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_new);
       float psum = 0.f, pv[8];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float e = exp2f(p[t][i] - m_new);
+          const float e = __builtin_amdgcn_exp2f(p[t][i] - m_new);
           psum += e;
           pv[4 * t + i] = e * vsc;
         }
@@ -478,13 +478,13 @@ __global__ __launch_bounds__(256) void k_decode_work_merge(CacheView cv, const v
 #pragma unroll
     for (int k = 0; k < UN; ++k) Mn = fmaxf(Mn, pm[k]);
     if (Mn == -INFINITY) continue;
-    const float a = M == -INFINITY ? 0.f : exp2f(M - Mn);
+    const float a = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
     den *= a;
 #pragma unroll
     for (int i = 0; i < J; ++i) acc[i] *= a;
 #pragma unroll
     for (int k = 0; k < UN; ++k) {
-      const float f = pm[k] == -INFINITY ? 0.f : exp2f(pm[k] - Mn);
+      const float f = pm[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(pm[k] - Mn);
       den += f * pl[k];
 #pragma unroll
       for (int i = 0; i < J; ++i) acc[i] += f * po[k][i];
@@ -502,7 +502,7 @@ __global__ __launch_bounds__(256) void k_decode_work_merge(CacheView cv, const v
   float f[4], dt = 0.f;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    f[k] = sM[k] == -INFINITY ? 0.f : exp2f(sM[k] - Mt);
+    f[k] = sM[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sM[k] - Mt);
     dt += f[k] * sDen[k];
   }
   const float inv = 1.f / dt;

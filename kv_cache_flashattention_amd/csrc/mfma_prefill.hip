@@ -17,7 +17,9 @@
 // the row max has grown by more than 8 (base-2 units) since the last
 // rescale; otherwise the stale max is kept.  The result is the same exact
 // softmax -- every term and the final sum use the one max in force -- and
-// the terms stay below 2^8, far inside fp32/bf16 range.
+// the terms stay below 2^8, far inside fp32/bf16 range.  Scores stay raw
+// until the exponent: p = exp2(s * scale * log2(e) - m) is one FMA and one
+// v_exp_f32 (terms below 2^-126 of the max flush to zero).
 //
 // Layout choices.  K tiles sit in LDS as rows [key][d]; V tiles are written
 // transposed, [d][key], during staging so that the PV operand (8
@@ -39,6 +41,7 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 constexpr int BM = 128;   // query rows per workgroup
 constexpr int BN = 64;    // keys per tile
@@ -76,6 +79,16 @@ __device__ __forceinline__ int row_key(int r) {
   return (jj < 2) ? 8 * h + 4 * jj + i : 16 + 8 * h + 4 * (jj - 2) + i;
 }
 
+// LDS tiles are stored without padding, with 16-byte granules XOR-swizzled
+// per row so that the lanes of one LDS access hit distinct banks, both when
+// the tiles are written during staging and when the MFMA operands are read.
+// K tile [key][d]: granule g of row r lives at g ^ ksw(r); the operand read
+// touches rows {0..3, 8..11} (+32) at one granule, which ksw spreads over 8
+// granules.  V^T tile [d][key]: granule g of row r lives at g ^ vsw(r);
+// operand reads touch 8 consecutive rows, staging writes rows 8 apart.
+__device__ __forceinline__ int ksw(int r) { return (r & 3) | ((r >> 1) & 4); }
+__device__ __forceinline__ int vsw(int r) { return (r & 7) ^ ((r >> 3) & 7); }
+
 template <int D, bool F16>
 __global__ __launch_bounds__(256, 2) void k_prefill_mfma(int n_q, int n_kv, int T,
                                                          const uint16_t* __restrict__ q,
@@ -86,10 +99,9 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(int n_q, int n_kv, int 
   typedef typename Op<F16>::T OpT;
   constexpr int KS = D / 16;        // k-steps of QK^T
   constexpr int DT = D / 32;        // 32-row tiles of O^T
-  constexpr int KP = D + 8;         // padded K row (elements)
-  constexpr int VP = BN + 8;        // padded V^T row (elements)
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN][KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D][VP];
+  constexpr int KG = D / 8;         // 16-byte granules per K row
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * BN];
 
   // ---- work assignment
   const int bx = blockIdx.x;
@@ -106,59 +118,52 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(int n_q, int n_kv, int 
   // ---- query operand (B of S^T = K Q^T)
   OpT qop[KS];
   {
-    const bool ok = qrow < T;
-    const uint16_t* qp = q + ((int64_t)b * T + (ok ? qrow : 0)) * qstride + (int64_t)head * D;
+    const uint16_t* qp = q + ((int64_t)b * T + min(qrow, T - 1)) * qstride + (int64_t)head * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 raw = ok ? *(const uint4*)(qp + 16 * ks + 8 * half) : make_uint4(0, 0, 0, 0);
-      qop[ks] = __builtin_bit_cast(OpT, raw);
-    }
+    for (int ks = 0; ks < KS; ++ks)
+      qop[ks] = __builtin_bit_cast(OpT, *(const u32x4*)(qp + 16 * ks + 8 * half));
   }
 
-  // ---- staging of one K/V tile: global -> registers -> LDS
+  // ---- staging of one K/V tile: global -> registers -> LDS.  Rows past
+  // the prompt's end load row T-1 instead: their scores are masked (the key
+  // is after every query), so they contribute exp(-inf) * finite = 0.
   constexpr int KCH = BN * D / 8 / 256;               // 16-byte K chunks per thread
   constexpr int VBL = (BN / 4) * (D / 8);             // 4x8 V blocks per tile
-  uint4 kreg[KCH], vreg[4];
+  u32x4 kreg[KCH], vreg[4];   // plain vectors: stay in registers
   const uint16_t* kbase = k + (int64_t)b * T * kvstride + (int64_t)g * D;
   const uint16_t* vbase = v + (int64_t)b * T * kvstride + (int64_t)g * D;
   auto load_tile = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i, row = c / (D / 8), c8 = c % (D / 8);
-      const int key = k0 + row;
-      kreg[i] = key < T ? *(const uint4*)(kbase + (int64_t)key * kvstride + 8 * c8)
-                        : make_uint4(0, 0, 0, 0);
+      const int c = tid + 256 * i, row = c / KG, c8 = c % KG;
+      const int key = min(k0 + row, T - 1);
+      kreg[i] = *(const u32x4*)(kbase + (int64_t)key * kvstride + 8 * c8);
     }
     if (tid < VBL) {
       const int kg = tid / (D / 8), dg = tid % (D / 8);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = k0 + 4 * kg + r;
-        vreg[r] = key < T ? *(const uint4*)(vbase + (int64_t)key * kvstride + 8 * dg)
-                          : make_uint4(0, 0, 0, 0);
+        const int key = min(k0 + 4 * kg + r, T - 1);
+        vreg[r] = *(const u32x4*)(vbase + (int64_t)key * kvstride + 8 * dg);
       }
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i, row = c / (D / 8), c8 = c % (D / 8);
-      *(uint4*)&Ks[buf][row][8 * c8] = kreg[i];
+      const int c = tid + 256 * i, row = c / KG, c8 = c % KG;
+      *(u32x4*)&Ks[buf][row * D + 8 * (c8 ^ ksw(row))] = kreg[i];
     }
     if (tid < VBL) {
       const int kg = tid / (D / 8), dg = tid % (D / 8);
-      const uint32_t* r0 = (const uint32_t*)&vreg[0];
-      const uint32_t* r1 = (const uint32_t*)&vreg[1];
-      const uint32_t* r2 = (const uint32_t*)&vreg[2];
-      const uint32_t* r3 = (const uint32_t*)&vreg[3];
 #pragma unroll
       for (int dd = 0; dd < 8; ++dd) {
-        const int wd = dd >> 1;
+        const int wd = dd >> 1, row = 8 * dg + dd;
         const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
-        uint2 pk;
-        pk.x = __builtin_amdgcn_perm(r1[wd], r0[wd], sel);   // keys 0,1 of column dd
-        pk.y = __builtin_amdgcn_perm(r3[wd], r2[wd], sel);   // keys 2,3
-        *(uint2*)&Vt[buf][8 * dg + dd][4 * kg] = pk;
+        uint2 pk;   // keys 0..3 of column dd
+        pk.x = __builtin_amdgcn_perm(vreg[1][wd], vreg[0][wd], sel);
+        pk.y = __builtin_amdgcn_perm(vreg[3][wd], vreg[2][wd], sel);
+        *(uint2*)&Vt[buf][row * BN + 8 * ((kg >> 1) ^ vsw(row)) + 4 * (kg & 1)] = pk;
       }
     }
   };
@@ -187,49 +192,50 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(int n_q, int n_kv, int 
       for (int st = 0; st < 2; ++st) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) sacc[st][e] = 0.f;
-        const uint16_t* krow = &Ks[buf][32 * st + row_key(col)][8 * half];
+        const int row = 32 * st + row_key(col);
+        const uint16_t* krow = &Ks[buf][row * D];
+        const int sw = ksw(row);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          OpT a = __builtin_bit_cast(OpT, *(const uint4*)(krow + 16 * ks));
+          OpT a = __builtin_bit_cast(OpT, *(const u32x4*)(krow + 8 * ((2 * ks + half) ^ sw)));
           sacc[st] = mfma32(a, qop[ks], sacc[st]);
         }
       }
-      // scores -> base-2 domain, causal mask on diagonal tiles
-      const bool diag = k0 + BN - 1 > q0 + 32 * w;
-      float p[2][16];
+      // causal mask on tiles that reach past the wave's first query
+      if (k0 + BN - 1 > q0 + 32 * w) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int r = 8 * (e >> 2) + 4 * half + (e & 3);
+            if (k0 + 32 * st + row_key(r) > qrow) sacc[st][e] = -INFINITY;
+          }
+      }
       float rmax = -INFINITY;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float x = sacc[st][e] * sl2;
-          if (diag) {
-            const int r = 8 * (e >> 2) + 4 * half + (e & 3);
-            if (k0 + 32 * st + row_key(r) > qrow) x = -INFINITY;
-          }
-          p[st][e] = x;
-          rmax = fmaxf(rmax, x);
-        }
-      rmax = fmaxf(rmax, __shfl_xor(rmax, 32, 64));
+        for (int e = 0; e < 16; ++e) rmax = fmaxf(rmax, sacc[st][e]);
+      rmax = fmaxf(rmax, __shfl_xor(rmax, 32, 64)) * sl2;   // base-2 domain (sl2 > 0)
       // stale-max online softmax update
       const float m_new = fmaxf(m, rmax);
       const bool grow = m_new > m + kStale;           // also true when m = -inf and m_new finite
-      const float m_use = grow ? m_new : m;
       if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float alpha = grow ? (m == -INFINITY ? 0.f : exp2f(m - m_new)) : 1.f;
+        const float alpha = grow ? (m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_new)) : 1.f;
         lsum *= alpha;
 #pragma unroll
         for (int i = 0; i < DT; ++i)
 #pragma unroll
           for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
       }
-      m = m_use;
+      if (grow) m = m_new;
       const float msub = m == -INFINITY ? 0.f : m;   // fully masked rows so far: p = 0
+      float p[2][16];
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          p[st][e] = exp2f(p[st][e] - msub);
+          p[st][e] = __builtin_amdgcn_exp2f(fmaf(sacc[st][e], sl2, -msub));
           lsum += p[st][e];
         }
       // O^T += V^T P^T over 4 k-steps of 16 keys
@@ -238,10 +244,12 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(int n_q, int n_kv, int 
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const OpT pop = pack8<OpT>(&p[st][8 * kb]);
+          const int gr = 4 * st + 2 * kb + half;       // logical granule of the keys
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            const uint16_t* vr = &Vt[buf][32 * dt + col][32 * st + 16 * kb + 8 * half];
-            OpT a = __builtin_bit_cast(OpT, *(const uint4*)vr);
+            const int row = 32 * dt + col;
+            const uint16_t* vr = &Vt[buf][row * BN + 8 * (gr ^ vsw(row))];
+            OpT a = __builtin_bit_cast(OpT, *(const u32x4*)vr);
             o[dt] = mfma32(a, pop, o[dt]);
           }
         }
@@ -264,7 +272,8 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(int n_q, int n_kv, int 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float y = o[dt][4 * jj + i] * inv;
-        hv[i] = F16 ? __builtin_bit_cast(uint16_t, (_Float16)y) : f32_to_bf16_bits(y);
+        hv[i] = F16 ? __builtin_bit_cast(uint16_t, (_Float16)y)
+                    : __builtin_bit_cast(uint16_t, (__bf16)y);
       }
       uint2 pk = make_uint2((uint32_t)hv[0] | ((uint32_t)hv[1] << 16),
                             (uint32_t)hv[2] | ((uint32_t)hv[3] << 16));

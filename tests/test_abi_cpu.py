@@ -176,6 +176,19 @@ def test_host_only_handle_refuses_device_calls():
     assert rc == kv.KVC_E_STATE
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.125, float("nan"), float("inf")])
+def test_attention_rejects_scale_outside_positive_reals(scale):
+    """Both attention calls take the row max on unscaled scores, which is only
+    the max of the scaled scores for a positive multiplier."""
+    c = host_cache()
+    L = kv.lib()
+    p = ctypes.c_void_p(16)
+    rc = L.kvc_attn_decode(c._h, 0, 1, p, p, p, ctypes.c_float(scale), 0, None, 0, None)
+    assert rc == kv.KVC_E_INVAL
+    rc = L.kvc_attn_prefill(c._h, 0, 1, None, 4, p, p, p, p, ctypes.c_float(scale), None)
+    assert rc == kv.KVC_E_INVAL
+
+
 def test_decode_workspace_plan():
     """Matrix-core caches use a work list: (sequence x group segments + waves)
     slots of 16 rows x (d + 2) floats plus the batch's prefix sums; f32 caches
