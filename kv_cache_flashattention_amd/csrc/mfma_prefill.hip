@@ -1,17 +1,25 @@
 // Causal prefill attention on the matrix cores (bf16 / fp16, d 64 or 128).
 //
 // Tiling ("KV Cache & Flash Attention." (kvcache-7e2), Flash Attention
-// section): a workgroup owns 128 consecutive query rows of one query head
-// (four waves x 32 rows) and streams the prompt's keys/values through LDS in
-// tiles of 64 rows, double-buffered: while a tile is consumed the next one is
-// already on its way from HBM.  Per tile each wave
+// section): a workgroup owns 256 consecutive query rows of one query head
+// (eight waves x 32 rows) and streams the prompt's keys/values through LDS in
+// tiles of 64 rows.  Per tile each wave
 //   1. computes S^T = K Q^T (32 keys x 32 queries per 32x32x16 MFMA, d as
 //      the reduction), so a lane holds 16 keys of one query column;
 //   2. applies the causal mask on tiles that touch the diagonal and runs the
 //      online softmax in fp32 (kvcache-7e2, online softmax section): row max
-//      = in-lane max + one exchange with the partner lane 32 away;
+//      = in-lane max + one swap with the partner lane 32 away;
 //   3. accumulates O^T += V^T P^T with P in registers (no LDS round trip).
 // The score tile never leaves registers; only O / l is written.
+//
+// Two wave groups per SIMD, offset by half a tile ("ping-pong").  Waves w and
+// w+4 share a SIMD.  The kernel runs in slots separated by workgroup
+// barriers; in each slot one group issues its matrix-core work (the PV
+// product of tile i-1, S of tile i, and the short VALU work that needs S:
+// row max and rescale) while the other group computes the exponentials of
+// its last score tile and stages the next K or V tile into LDS.  The matrix
+// core of each SIMD stays busy while the VALU serves the other wave.  Group 1 stages K tiles, group 0 stages V tiles, each in
+// its own exponent slot, through registers (loads issued two slots ahead).
 //
 // Running max.  The rescale factor exp(m_old - m_new) is applied only when
 // the row max has grown by more than 8 (base-2 units) since the last
@@ -19,19 +27,23 @@
 // softmax -- every term and the final sum use the one max in force -- and
 // the terms stay below 2^8, far inside fp32/bf16 range.  Scores stay raw
 // until the exponent: p = exp2(s * scale * log2(e) - m) is one FMA and one
-// v_exp_f32 (terms below 2^-126 of the max flush to zero).
+// v_exp_f32 (terms below 2^-126 of the max flush to zero).  The row sum adds
+// the probabilities as rounded to the 16-bit type the PV product uses.
 //
 // Layout choices.  K tiles sit in LDS as rows [key][d]; V tiles are written
 // transposed, [d][key], during staging so that the PV operand (8
 // consecutive keys of one d) is a single 16-byte LDS read.  Which key each
 // S^T row holds is permuted so that the 8 probabilities a lane holds for a
-// PV k-step are 8 consecutive keys.
+// PV k-step are 8 consecutive keys.  Rows of both tiles are padded by 16
+// bytes, which puts the 16 rows one operand read touches on 16 different
+// bank groups and keeps every operand address a per-lane base plus an
+// immediate offset; staging writes fill whole rows.
 //
 // Scheduling.  Query tiles near the end of the prompt see the most keys;
-// the grid's slowest dimension walks the tiles from the last to the first so
-// the heaviest workgroups start first.  On 8-XCD parts consecutive
-// workgroups go to different XCDs; query heads are numbered so that the
-// heads sharing one kv head land on the same XCD (and its L2).
+// each XCD walks its (sequence, kv head) tiles from the last to the first
+// so the heaviest workgroups start first.  Consecutive workgroups go to
+// different XCDs; the work list gives each XCD a contiguous run of one kv
+// head's work, so its L2 serves the K/V tiles that its workgroups share.
 #include "common.h"
 
 namespace kvfa {
@@ -40,10 +52,12 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
-constexpr int BM = 128;   // query rows per workgroup
+constexpr int BM = 256;   // query rows per workgroup
 constexpr int BN = 64;    // keys per tile
 constexpr float kStale = 8.0f;
 
@@ -71,6 +85,61 @@ template <> __device__ __forceinline__ f16x8 pack8<f16x8>(const float* p) {
   return r;
 }
 
+// Sum of the 8 rounded probabilities of one PV operand, two per dot product.
+__device__ __forceinline__ float sum8(bf16x8 p, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    bf16x2 t = {p[2 * j], p[2 * j + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(t, one, acc, false);
+  }
+  return acc;
+}
+__device__ __forceinline__ float sum8(f16x8 p, float acc) {
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f16x2 t = {p[2 * j], p[2 * j + 1]};
+    acc = __builtin_amdgcn_fdot2(t, one, acc, false);
+  }
+  return acc;
+}
+
+// The value held by the lane 32 away: one v_permlane32_swap, no LDS.
+__device__ __forceinline__ float half_swap(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  // lanes 0-31 find the partner's value in r[1], lanes 32-63 in r[0]; the
+  // other element holds the lane's own value.
+  return __builtin_bit_cast(float, (__lane_id() < 32) ? r[1] : r[0]);
+}
+
+// Scheduling pattern for a run of N MFMAs, each fed by one 16-byte LDS
+// operand read: the reads run at most AHEAD instructions ahead of the MFMAs
+// that consume them, which bounds the registers holding operands in flight.
+template <int N, int AHEAD>
+__device__ __forceinline__ void interleave_lds_mfma() {
+#pragma unroll
+  for (int n = 0; n < AHEAD; ++n) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+  for (int n = 0; n < N - AHEAD; ++n) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+#pragma unroll
+  for (int n = 0; n < AHEAD; ++n) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+}
+
+// The thread index, hidden from the optimizer so that per-lane addresses are
+// recomputed where they are used (a few VALU ops in slots with spare VALU
+// issue) instead of being hoisted out of the tile loop into registers that
+// would stay live across it.
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 // Key (0..31 within a 32-key S^T tile) held by MFMA row r = 8*jj + 4*h + i.
 // Lane half h then holds keys 8h..8h+7 (jj = 0, 1) and 16+8h..16+8h+7
 // (jj = 2, 3).
@@ -79,41 +148,50 @@ __device__ __forceinline__ int row_key(int r) {
   return (jj < 2) ? 8 * h + 4 * jj + i : 16 + 8 * h + 4 * (jj - 2) + i;
 }
 
-// LDS tiles are stored without padding, with 16-byte granules XOR-swizzled
-// per row so that the lanes of one LDS access hit distinct banks, both when
-// the tiles are written during staging and when the MFMA operands are read.
-// K tile [key][d]: granule g of row r lives at g ^ ksw(r); the operand read
-// touches rows {0..3, 8..11} (+32) at one granule, which ksw spreads over 8
-// granules.  V^T tile [d][key]: granule g of row r lives at g ^ vsw(r);
-// operand reads touch 8 consecutive rows, staging writes rows 8 apart.
-__device__ __forceinline__ int ksw(int r) { return (r & 3) | ((r >> 1) & 4); }
-__device__ __forceinline__ int vsw(int r) { return (r & 7) ^ ((r >> 3) & 7); }
-
 template <int D, bool F16>
-__global__ __launch_bounds__(256, 2) void k_prefill_mfma(int n_q, int n_kv, int T,
+__global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int T,
                                                          const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v,
                                                          uint16_t* __restrict__ out, float sl2,
-                                                         int ntiles, int xcd_heads) {
+                                                         int ntiles, int n_seq, int n_units,
+                                                         int xcd_split) {
   typedef typename Op<F16>::T OpT;
   constexpr int KS = D / 16;        // k-steps of QK^T
   constexpr int DT = D / 32;        // 32-row tiles of O^T
   constexpr int KG = D / 8;         // 16-byte granules per K row
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * BN];
+  constexpr int KP = D + 8;         // padded row lengths (elements)
+  constexpr int VP = BN + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VP];
 
-  // ---- work assignment
-  const int bx = blockIdx.x;
-  const int head = xcd_heads ? (bx % 8) * (n_q / 8) + bx / 8 : bx;
-  const int b = blockIdx.y;
-  const int tile = ntiles - 1 - (int)blockIdx.z;
+  // ---- work assignment.  Workgroup L runs on XCD L % 8; the work list is
+  // cut into 8 contiguous parts, one per XCD, ordered (kv head, sequence,
+  // query tile from the last, query head of the group).  An XCD thus works
+  // through one (sequence, kv head) at a time and its L2 holds the K/V rows
+  // that all of its resident workgroups read.
+  const int G = n_q / n_kv;
+  int u = blockIdx.x;
+  if (xcd_split) u = (u % 8) * (n_units / 8) + u / 8;
+  const int hg = u % G;
+  int r = u / G;
+  const int tile = ntiles - 1 - r % ntiles;
+  r /= ntiles;
+  const int b = r % n_seq;
+  const int g = r / n_seq;
+  const int head = g * G + hg;
   const int q0 = tile * BM;
-  const int g = head / (n_q / n_kv);
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
-  const int qrow = q0 + 32 * w + col;                 // this lane's query position
-  const bool wave_live = q0 + 32 * w < T;
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = w >> 2;                              // SIMD w & 3 hosts waves w, w ^ 4
+  const int rq0 = q0 + 32 * (2 * (w & 3) + grp);       // first query row of this wave
+  const int qrow = rq0 + col;                          // this lane's query position
   const int64_t qstride = (int64_t)n_q * D, kvstride = (int64_t)n_kv * D;
+
+  const int kend = min(T, q0 + BM);                    // keys any row of the workgroup sees
+  const int nkt = (kend + BN - 1) / BN;
+  // tiles this wave computes on: those holding a key <= its last row
+  const int wn = rq0 < T ? min(nkt, (rq0 + 31) / BN + 1) : 0;
 
   // ---- query operand (B of S^T = K Q^T)
   OpT qop[KS];
@@ -124,143 +202,209 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(int n_q, int n_kv, int 
       qop[ks] = __builtin_bit_cast(OpT, *(const u32x4*)(qp + 16 * ks + 8 * half));
   }
 
-  // ---- staging of one K/V tile: global -> registers -> LDS.  Rows past
-  // the prompt's end load row T-1 instead: their scores are masked (the key
-  // is after every query), so they contribute exp(-inf) * finite = 0.
-  constexpr int KCH = BN * D / 8 / 256;               // 16-byte K chunks per thread
-  constexpr int VBL = (BN / 4) * (D / 8);             // 4x8 V blocks per tile
-  u32x4 kreg[KCH], vreg[4];   // plain vectors: stay in registers
+  // ---- staging through registers.  Rows past the prompt's end load row
+  // T-1 instead: their scores are masked (the key is after every query), so
+  // they contribute exp(-inf) * finite = 0.
+  constexpr int KCH = BN * D / 8 / 256;                // 16-byte K chunks per group thread
+  constexpr int VBL = (BN / 4) * (D / 8);              // 4x8 V blocks per tile
+  u32x4 sreg[4];                                       // plain vectors: stay in registers
   const uint16_t* kbase = k + (int64_t)b * T * kvstride + (int64_t)g * D;
   const uint16_t* vbase = v + (int64_t)b * T * kvstride + (int64_t)g * D;
-  auto load_tile = [&](int k0) {
+  auto load_k = [&](int i) {
+    const uint16_t* tb = kbase + (int64_t)(BN * i) * kvstride;
+    const int lim = T - 1 - BN * i;                    // last valid row of the tile
+    const int t = opaque_tid() & 255;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i, row = c / KG, c8 = c % KG;
-      const int key = min(k0 + row, T - 1);
-      kreg[i] = *(const u32x4*)(kbase + (int64_t)key * kvstride + 8 * c8);
+    for (int c0 = 0; c0 < KCH; ++c0) {
+      const int row = min(t / KG + c0 * (256 / KG), lim);
+      sreg[c0] = *(const u32x4*)(tb + row * kvstride + 8 * (t % KG));
     }
-    if (tid < VBL) {
-      const int kg = tid / (D / 8), dg = tid % (D / 8);
+  };
+  auto store_k = [&](int buf) {
+    const int t = opaque_tid() & 255;
+#pragma unroll
+    for (int c0 = 0; c0 < KCH; ++c0)
+      *(u32x4*)&Ks[buf][(t / KG + c0 * (256 / KG)) * KP + 8 * (t % KG)] = sreg[c0];
+  };
+  // V: thread (kg, dg) moves keys 4kg..4kg+3 of d-granule dg; the 16 lanes
+  // of one LDS write pass cover one whole V^T row.
+  auto load_v = [&](int i) {
+    const int t = opaque_tid() & 255;
+    if (t < VBL) {
+      const int kg = t % (BN / 4), dg = t / (BN / 4);
+      const uint16_t* tb = vbase + (int64_t)(BN * i) * kvstride;
+      const int lim = T - 1 - BN * i;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = min(k0 + 4 * kg + r, T - 1);
-        vreg[r] = *(const u32x4*)(vbase + (int64_t)key * kvstride + 8 * dg);
+        const int row = min(4 * kg + r, lim);
+        sreg[r] = *(const u32x4*)(tb + row * kvstride + 8 * dg);
       }
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i, row = c / KG, c8 = c % KG;
-      *(u32x4*)&Ks[buf][row * D + 8 * (c8 ^ ksw(row))] = kreg[i];
-    }
-    if (tid < VBL) {
-      const int kg = tid / (D / 8), dg = tid % (D / 8);
+  auto store_v = [&](int buf) {
+    const int t = opaque_tid() & 255;
+    if (t < VBL) {
+      const int kg = t % (BN / 4), dg = t / (BN / 4);
 #pragma unroll
       for (int dd = 0; dd < 8; ++dd) {
-        const int wd = dd >> 1, row = 8 * dg + dd;
+        const int wd = dd >> 1;
         const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
         uint2 pk;   // keys 0..3 of column dd
-        pk.x = __builtin_amdgcn_perm(vreg[1][wd], vreg[0][wd], sel);
-        pk.y = __builtin_amdgcn_perm(vreg[3][wd], vreg[2][wd], sel);
-        *(uint2*)&Vt[buf][row * BN + 8 * ((kg >> 1) ^ vsw(row)) + 4 * (kg & 1)] = pk;
+        pk.x = __builtin_amdgcn_perm(sreg[1][wd], sreg[0][wd], sel);
+        pk.y = __builtin_amdgcn_perm(sreg[3][wd], sreg[2][wd], sel);
+        *(uint2*)&Vt[buf][(8 * dg + dd) * VP + 4 * kg] = pk;
       }
     }
   };
 
+  // ---- per-wave state
   f32x16 o[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
   float m = -INFINITY, lsum = 0.f;
+  f32x16 sacc[2];
+  OpT pop[4];
 
-  const int kend = min(T, q0 + BM);                   // keys any row of the tile sees
-  const int nkt = (kend + BN - 1) / BN;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < nkt; ++j) {
-    const int buf = j & 1, k0 = j * BN;
-    if (j + 1 < nkt) load_tile(k0 + BN);
-
-    // wave-level causal skip: every key of the tile is after every query of the wave
-    if (wave_live && k0 <= q0 + 32 * w + 31) {
-      f32x16 sacc[2];
+  // S^T of tile i (buffer i & 1)
+  auto qk = [&](int i) {
+    const int buf = i & 1, t = opaque_tid(), c = t & 31, h = (t >> 5) & 1;
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+    for (int st = 0; st < 2; ++st) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[st][e] = 0.f;
-        const int row = 32 * st + row_key(col);
-        const uint16_t* krow = &Ks[buf][row * D];
-        const int sw = ksw(row);
+      for (int e = 0; e < 16; ++e) sacc[st][e] = 0.f;
+      const uint16_t* krow = &Ks[buf][(32 * st + row_key(c)) * KP + 8 * h];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          OpT a = __builtin_bit_cast(OpT, *(const u32x4*)(krow + 8 * ((2 * ks + half) ^ sw)));
-          sacc[st] = mfma32(a, qop[ks], sacc[st]);
-        }
+      for (int ks = 0; ks < KS; ++ks) {
+        OpT a = __builtin_bit_cast(OpT, *(const u32x4*)(krow + 16 * ks));
+        sacc[st] = mfma32(a, qop[ks], sacc[st]);
       }
-      // causal mask on tiles that reach past the wave's first query
-      if (k0 + BN - 1 > q0 + 32 * w) {
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int r = 8 * (e >> 2) + 4 * half + (e & 3);
-            if (k0 + 32 * st + row_key(r) > qrow) sacc[st][e] = -INFINITY;
-          }
-      }
-      float rmax = -INFINITY;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) rmax = fmaxf(rmax, sacc[st][e]);
-      rmax = fmaxf(rmax, __shfl_xor(rmax, 32, 64)) * sl2;   // base-2 domain (sl2 > 0)
-      // stale-max online softmax update
-      const float m_new = fmaxf(m, rmax);
-      const bool grow = m_new > m + kStale;           // also true when m = -inf and m_new finite
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float alpha = grow ? (m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_new)) : 1.f;
-        lsum *= alpha;
-#pragma unroll
-        for (int i = 0; i < DT; ++i)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
-      }
-      if (grow) m = m_new;
-      const float msub = m == -INFINITY ? 0.f : m;   // fully masked rows so far: p = 0
-      float p[2][16];
+    }
+    interleave_lds_mfma<2 * KS, 3>();
+  };
+  // online softmax of tile i, first half: mask, row max, rescale of O and l
+  auto rowmax = [&](int i) {
+    const int k0 = BN * i;
+    if (k0 + BN - 1 > rq0) {                           // tile reaches past the wave's first row
+      // element e of sacc[st] holds key k0 + 32 st + 8 half + kofs(e)
+      const int t = opaque_tid();
+      const int thr = rq0 + (t & 31) - k0 - 8 * ((t >> 5) & 1);
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          p[st][e] = __builtin_amdgcn_exp2f(fmaf(sacc[st][e], sl2, -msub));
-          lsum += p[st][e];
-        }
-      // O^T += V^T P^T over 4 k-steps of 16 keys
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const OpT pop = pack8<OpT>(&p[st][8 * kb]);
-          const int gr = 4 * st + 2 * kb + half;       // logical granule of the keys
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const int row = 32 * dt + col;
-            const uint16_t* vr = &Vt[buf][row * BN + 8 * (gr ^ vsw(row))];
-            OpT a = __builtin_bit_cast(OpT, *(const u32x4*)vr);
-            o[dt] = mfma32(a, pop, o[dt]);
-          }
+          const int jj = e >> 2, kofs = (jj < 2 ? 4 * jj : 16 + 4 * (jj - 2)) + (e & 3);
+          if (32 * st + kofs > thr) sacc[st][e] = -INFINITY;
         }
     }
-    if (j + 1 < nkt) store_tile(buf ^ 1);
+    float rmax = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) rmax = fmaxf(rmax, sacc[st][e]);
+    rmax = fmaxf(rmax, half_swap(rmax)) * sl2;         // base-2 domain (sl2 > 0)
+    const float m_new = fmaxf(m, rmax);
+    const bool grow = m_new > m + kStale;              // also true when m = -inf and m_new finite
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float alpha = grow ? (m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_new)) : 1.f;
+      lsum *= alpha;
+#pragma unroll
+      for (int d = 0; d < DT; ++d)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
+    }
+    if (grow) m = m_new;
+  };
+  // probabilities of tile i under the running max -> pop
+  auto expo = [&](int i) {
+    const float msub = m == -INFINITY ? 0.f : m;       // fully masked rows so far: p = 0
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[st][8 * kb + e], sl2, -msub));
+        pop[2 * st + kb] = pack8<OpT>(p);
+      }
+  };
+  // l += row sums of P_i; O^T += V^T P^T of tile i over 4 k-steps of 16 keys
+  auto pv = [&](int i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lsum = sum8(pop[j], lsum);
+    const int buf = i & 1, t = opaque_tid(), c = t & 31, h = (t >> 5) & 1;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const uint16_t* vr = &Vt[buf][(32 * dt + c) * VP + 32 * st + 16 * kb + 8 * h];
+          OpT a = __builtin_bit_cast(OpT, *(const u32x4*)vr);
+          o[dt] = mfma32(a, pop[2 * st + kb], o[dt]);
+        }
+      }
+    interleave_lds_mfma<4 * DT, 3>();
+  };
+
+  // ---- prologue: K_0 into LDS; loads of K_1 (group 1) and V_0 (group 0)
+  if (grp == 1) {
+    load_k(0);
+    store_k(0);
+    if (1 < nkt) load_k(1);
+  } else {
+    load_v(0);
+  }
+  __syncthreads();
+
+  // ---- slots.  Every wave runs the same sequence, per tile i: a matrix
+  // phase (row sums and PV of P_{i-1}, then S_i, its row max and the
+  // rescale of O and l) and an exponent phase (P_i plus its group's staging
+  // duty), each closed by a barrier.  Group 1 starts one
+  // slot late, so in slot 2i+g group g runs the matrix phase of tile i and
+  // in slot 2i+1+g its exponent phase.  Staging: group 1 writes K_{i+2} in
+  // its exponent phase of tile i (slot 2i+2), group 0 writes V_i in its
+  // exponent phase of tile i (slot 2i+1); in both cases the buffer's
+  // previous tile was last read in slot 2i+1 or earlier, and the new tile
+  // is first read two or more slots later.  Loads are issued two slots
+  // before their LDS write.
+  if (grp == 1) {
+    if (1 < nkt) {
+      store_k(1);
+      if (2 < nkt) load_k(2);
+    }
     __syncthreads();
   }
+  for (int i = 0; i <= nkt; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (i >= 1 && i - 1 < wn) pv(i - 1);             // P_{i-1} dies before S_i is born
+    if (i < wn) {
+      qk(i);
+      rowmax(i);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    if (i < wn) expo(i);
+    if (grp == 1) {
+      if (i + 2 < nkt) {
+        store_k(i & 1);
+        if (i + 3 < nkt) load_k(i + 3);
+      }
+    } else if (i < nkt) {
+      store_v(i & 1);
+      if (i + 1 < nkt) load_v(i + 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+  }
+  if (grp == 0) __syncthreads();                     // same barrier count for both groups
 
   // ---- epilogue: O / l for this lane's query column
-  if (!wave_live || qrow >= T) return;
-  const float l = lsum + __shfl_xor(lsum, 32, 64);
+  if (wn == 0 || qrow >= T) return;
+  const float l = lsum + half_swap(lsum);
   const float inv = 1.f / l;
   uint16_t* orow = out + ((int64_t)b * T + qrow) * qstride + (int64_t)head * D;
 #pragma unroll
@@ -285,10 +429,12 @@ template <int D, bool F16>
 hipError_t run(const CacheView& cv, int n, int T, const void* q, const void* k, const void* v,
                void* out, float sl2, hipStream_t s) {
   const int ntiles = (T + BM - 1) / BM;
-  const int xcd_heads = (cv.n_q % 8 == 0 && (cv.n_q / 8) % (cv.n_q / cv.n_kv) == 0) ? 1 : 0;
-  hipLaunchKernelGGL((k_prefill_mfma<D, F16>), dim3(cv.n_q, n, ntiles), dim3(256), 0, s, cv.n_q,
+  const int64_t units = (int64_t)cv.n_q * n * ntiles;
+  if (units > INT32_MAX) return hipErrorInvalidValue;
+  const int xcd_split = units % 8 == 0 ? 1 : 0;
+  hipLaunchKernelGGL((k_prefill_mfma<D, F16>), dim3((uint32_t)units), dim3(512), 0, s, cv.n_q,
                      cv.n_kv, T, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                     (uint16_t*)out, sl2, ntiles, xcd_heads);
+                     (uint16_t*)out, sl2, ntiles, n, (int)units, xcd_split);
   return hipGetLastError();
 }
 
