@@ -361,15 +361,16 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
 
   // ---- slots.  Every wave runs the same sequence, per tile i: a matrix
   // phase (row sums and PV of P_{i-1}, then S_i, its row max and the
-  // rescale of O and l) and an exponent phase (P_i plus its group's staging
-  // duty), each closed by a barrier.  Group 1 starts one
-  // slot late, so in slot 2i+g group g runs the matrix phase of tile i and
-  // in slot 2i+1+g its exponent phase.  Staging: group 1 writes K_{i+2} in
-  // its exponent phase of tile i (slot 2i+2), group 0 writes V_i in its
-  // exponent phase of tile i (slot 2i+1); in both cases the buffer's
-  // previous tile was last read in slot 2i+1 or earlier, and the new tile
-  // is first read two or more slots later.  Loads are issued two slots
-  // before their LDS write.
+  // rescale of O and l) and an exponent phase (its group's staging duty,
+  // then P_i), each closed by a barrier.  Group 1 starts one slot late, so
+  // in slot 2i+g group g runs the matrix phase of tile i and in slot 2i+1+g
+  // its exponent phase.  Staging: group 1 writes K_{i+2} in its exponent
+  // phase of tile i (slot 2i+2), group 0 writes V_i in its exponent phase
+  // of tile i (slot 2i+1); in both cases the buffer's previous tile was last
+  // read in slot 2i+1 or earlier, and the new tile is first read two or
+  // more slots later.  Loads are issued two slots before their LDS write.
+  // The matrix phase runs at a raised wave priority: its MFMAs issue first
+  // and the other wave's VALU work fills the remaining issue cycles.
   if (grp == 1) {
     if (1 < nkt) {
       store_k(1);
@@ -379,15 +380,17 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
   }
   for (int i = 0; i <= nkt; ++i) {
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(2);
     if (i >= 1 && i - 1 < wn) pv(i - 1);             // P_{i-1} dies before S_i is born
     if (i < wn) {
       qk(i);
       rowmax(i);
     }
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    if (i < wn) expo(i);
+    // staging first: its LDS writes drain while the exponentials run
     if (grp == 1) {
       if (i + 2 < nkt) {
         store_k(i & 1);
@@ -397,6 +400,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
       store_v(i & 1);
       if (i + 1 < nkt) load_v(i + 1);
     }
+    if (i < wn) expo(i);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   }
