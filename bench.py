@@ -15,9 +15,15 @@ workload (4 x 8,192 tokens, 32/8 heads of 128, bf16), whose metric is
 algorithmic TFLOP/s.
 
 `roofline` is measured for the dominant call of each workload with HIP
-events recorded on the stream the library launches on, over the timed
-launches; `cpu_baseline` times the float64 oracle on a bounded sample of the
-same workload on this host's cores.  Inputs are synthetic and seeded.
+events recorded on the stream the library launches on: for decode, the same
+call repeated K times after the timed steps, each launch preceded by a read
+of a separate 1 GiB buffer that evicts the Infinity Cache; for prefill, over
+the timed launches.  `traffic` is the HBM bytes per call that rocprofv3's
+FETCH_SIZE / WRITE_SIZE counters recorded (profiles/counters.json, scaled by
+a copy-kernel calibration), reported only while the kernel sources are
+unchanged since that measurement.  `cpu_baseline` times the float64 oracle
+on a bounded sample of the same workload on this host's cores.  Inputs are
+synthetic and seeded.
 """
 import argparse
 import json
@@ -49,6 +55,39 @@ def blas_threads():
         return max([p.get("num_threads", 0) for p in threadpool_info()] or [0])
     except Exception:
         return None
+
+
+# ---------------------------------------------------------------- counters
+COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+KERNEL_SOURCES = ["mfma_decode.hip", "decode.hip", "mfma_prefill.hip", "prefill.hip",
+                  "cache_kernels.hip", "common.h", "fp8_e4m3.h", "kvfa_internal.h"]
+
+
+def kernel_source_digest():
+    """sha256 over the device sources, in a fixed order."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "kv_cache_flashattention_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def counter_traffic(key):
+    """HBM bytes per call from rocprofv3 FETCH_SIZE / WRITE_SIZE runs recorded
+    in profiles/counters.json, scaled by the copy-kernel calibration factors;
+    None unless the kernels are byte-identical in source to those measured."""
+    try:
+        with open(COUNTERS) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    e = rec.get("workloads", {}).get(key)
+    if e is None or rec.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    cal = rec["calibration"]
+    return (e["fetch_kib_per_call"] * 1024 * cal["fetch_factor"]
+            + e["write_kib_per_call"] * 1024 * cal["write_factor"])
 
 
 # ---------------------------------------------------------------- decode
@@ -128,17 +167,38 @@ def bench_decode(name, steps, warmup, torch, kv, with_cpu):
     # algorithmic bytes of each timed decode: lengths lens0+1 .. lens0+steps
     total_bytes = sum(decode_bytes(w, lens0 + i + 1, kv_elem) for i in range(steps))
     kern_ms = [a.elapsed_time(b) for a, b in events]
-    kern_avg_s = float(np.mean(kern_ms)) / 1e3
-    per_call = total_bytes / steps
+    warm_avg_s = float(np.mean(kern_ms)) / 1e3
+    # Roofline: the same decode call (state after the timed steps), each
+    # launch preceded by a full read of a separate 1 GiB buffer, which evicts
+    # the 256 MB Infinity Cache without leaving dirty lines behind, so that
+    # every K/V byte of the call comes from HBM.
+    lens1 = lens0 + steps
+    per_call = decode_bytes(w, lens1, kv_elem)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    cold = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(steps)]
+    for i in range(steps):
+        torch.sum(flush, dim=0, out=sink)
+        cold[i][0].record(stream)
+        c.attn_decode(0, seqs, q, out=out, ws=ws)
+        cold[i][1].record(stream)
+    torch.cuda.synchronize()
+    del flush, sink
+    kern_avg_s = float(np.mean([a.elapsed_time(b) for a, b in cold])) / 1e3
     achieved = per_call / kern_avg_s / 1e9
     res = {
         "workload": name,
         "value": total_bytes / wall / 1e9,
         "ms_per_step": wall / steps * 1e3,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": counter_traffic("decode_" + name),
                      "kernel": "kvc_attn_decode (split partial + merge)",
-                     "avg_call_us": kern_avg_s * 1e6, "bytes_per_call": per_call},
+                     "avg_call_us": kern_avg_s * 1e6, "bytes_per_call": per_call,
+                     "cache_evicted_before_each_call": True,
+                     "avg_call_us_warm": warm_avg_s * 1e6},
         "shape": {"batch": w.batch, "n_q": w.n_q, "n_kv": w.n_kv, "d": w.d,
                   "kv_dtype": w.kv_dtype, "mean_len": float(np.mean(lens0 + 1))},
     }
@@ -216,7 +276,8 @@ def bench_prefill(steps, warmup, torch, kv, with_cpu, small=False):
         "value": flops * steps / wall / 1e12, "unit": "TFLOP/s",
         "ms_per_step": wall / steps * 1e3,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
+                     "traffic": counter_traffic("prefill_llama8b_prefill"),
                      "kernel": "kvc_attn_prefill (K/V append + causal attention)",
                      "avg_call_us": call_s * 1e6, "flops_per_call": flops},
         "shape": {"batch": w.batch, "T": w.T, "n_q": w.n_q, "n_kv": w.n_kv, "d": w.d},
