@@ -208,3 +208,21 @@ def prefill_attention(q, k, v, scale):
     """
     T = np.asarray(q).shape[0]
     return gqa_attention(q, k, v, scale, q_pos=np.arange(T))
+
+
+def extend_attention(q, k, v, scale):
+    """k new query rows against a cache that already holds their own rows.
+
+    The cache holds L rows (the k new tokens' K/V rows included, appended
+    before the queries attend); the queries are the last k positions
+    L - k .. L - 1, and query t sees keys 0 .. L - k + t.  This is one chunk
+    of a prompt processed against the cache the earlier chunks filled
+    ([KVFA] continuous-batching section: chunked prefill folded into a decode
+    iteration; [KPF] prefill spikes split into chunks), and it is the target
+    model's single pass over k drafted positions ([KVFA] speculative-decoding
+    section).
+    q: [k, n_q, d]; k, v: [L, n_kv, d] with L >= k.  Returns [k, n_q, d].
+    """
+    Tq, L = np.asarray(q).shape[0], np.asarray(k).shape[0]
+    assert 1 <= Tq <= L
+    return gqa_attention(q, k, v, scale, q_pos=np.arange(L - Tq, L))

@@ -96,6 +96,55 @@ def check_decode_vs_sdpa(decode_fn, seed=2):
     return True
 
 
+def sdpa_masked_ref(q, k, v, scale, q_pos):
+    """torch SDPA in float64 with an explicit boolean mask: key j visible to
+    the query at position p iff j <= p.  q [Tq, n_q, d], k/v [L, n_kv, d]."""
+    L = k.shape[0]
+    Q = torch.from_numpy(np.ascontiguousarray(q.transpose(1, 0, 2)))[None].double()
+    K = torch.from_numpy(np.ascontiguousarray(k.transpose(1, 0, 2)))[None].double()
+    V = torch.from_numpy(np.ascontiguousarray(v.transpose(1, 0, 2)))[None].double()
+    mask = torch.from_numpy(np.arange(L)[None, :] <= np.asarray(q_pos)[:, None])
+    out = torch.nn.functional.scaled_dot_product_attention(
+        Q, K, V, attn_mask=mask, scale=scale, enable_gqa=True)
+    return out[0].numpy().transpose(1, 0, 2)
+
+
+def check_extend_vs_sdpa(extend_fn, seed=11):
+    """k query rows at positions L-k..L-1 against L cached rows equal torch
+    SDPA with the explicit bottom-right mask."""
+    rng = np.random.default_rng(seed)
+    for (k_, L, n_q, n_kv, d) in ((1, 1, 4, 2, 8), (3, 40, 8, 2, 16), (17, 17, 4, 4, 8),
+                                  (5, 70, 16, 1, 8), (33, 100, 6, 3, 16)):
+        q = rng.standard_normal((k_, n_q, d))
+        kc = rng.standard_normal((L, n_kv, d))
+        vc = rng.standard_normal((L, n_kv, d))
+        scale = 1 / math.sqrt(d)
+        ref = sdpa_masked_ref(q, kc, vc, scale, np.arange(L - k_, L))
+        if not np.allclose(extend_fn(q, kc, vc, scale), ref, rtol=0, atol=1e-12):
+            return False
+    return True
+
+
+def check_chunked_equals_whole(extend_fn, prefill_fn, seed=12):
+    """Chunked prefill: a prompt processed in consecutive chunks, each chunk's
+    queries against the cache filled up to the chunk's end, gives the rows of
+    the whole-prompt causal prefill.  Also k = 1 against L rows is one decode
+    row and k = L is the whole prompt."""
+    rng = np.random.default_rng(seed)
+    T, n_q, n_kv, d = 45, 8, 2, 16
+    q = rng.standard_normal((T, n_q, d))
+    kc = rng.standard_normal((T, n_kv, d))
+    vc = rng.standard_normal((T, n_kv, d))
+    scale = 1 / math.sqrt(d)
+    whole = prefill_fn(q, kc, vc, scale)
+    for cuts in ((0, 10, 11, 30, 45), (0, 1, 2, 3, 45), (0, 45)):
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            got = extend_fn(q[a:b], kc[:b], vc[:b], scale)
+            if not np.allclose(got, whole[a:b], rtol=0, atol=1e-12):
+                return False
+    return True
+
+
 def check_tiled_equals_definition(tiled_fn, attention_fn, seed=3):
     """The tiled flash loop (any tile sizes) reaches the definition."""
     rng = np.random.default_rng(seed)

@@ -169,3 +169,20 @@ def test_fp8_slab_without_requant_is_caught():
     codes, s = C.fp8_slab_write(np.zeros((16, 2), np.uint8), np.float32(0), 0, rows[:1])
     codes, s = C.fp8_slab_write(codes, s, 1, rows[1:])
     assert _slab_error_ok(codes, s, rows.astype(np.float64), 1)
+
+
+def test_extend_with_top_left_positions_is_caught():
+    """Chunk queries placed at positions 0..k-1 instead of L-k..L-1."""
+    def top_left(q, k, v, scale):
+        return A.gqa_attention(q, k, v, scale, q_pos=np.arange(np.asarray(q).shape[0]))
+    assert not pins.check_extend_vs_sdpa(top_left)
+    assert not pins.check_chunked_equals_whole(top_left, A.prefill_attention)
+
+
+def test_extend_off_by_one_is_caught():
+    """Query t seeing keys 0..L-k+t-1 (its own row hidden)."""
+    def strict(q, k, v, scale):
+        Tq, L = np.asarray(q).shape[0], np.asarray(k).shape[0]
+        return A.gqa_attention(q, k, v, scale, q_pos=np.arange(L - Tq, L) - 0.5)
+    assert not pins.check_extend_vs_sdpa(strict)
+    assert not pins.check_chunked_equals_whole(strict, A.prefill_attention)

@@ -30,6 +30,14 @@ def test_decode_matches_torch_sdpa_float64():
     assert pins.check_decode_vs_sdpa(A.decode_attention)
 
 
+def test_extend_matches_torch_sdpa_with_bottom_right_mask():
+    assert pins.check_extend_vs_sdpa(A.extend_attention)
+
+
+def test_chunked_prefill_equals_whole_prompt():
+    assert pins.check_chunked_equals_whole(A.extend_attention, A.prefill_attention)
+
+
 def test_tiled_flash_loop_reaches_definition():
     assert pins.check_tiled_equals_definition(A.flash_attention_tiled, A.attention)
 
