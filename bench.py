@@ -11,8 +11,9 @@ allocator + table update), kv_append of the new K/V rows, then attn_decode
 the decode's algorithmic HBM bytes per step (K/V rows read through the
 tables, queries, outputs, table entries) divided by the wall-clock time per
 step.  The same JSON line carries a `prefill` object for the causal-prefill
-workload (4 x 8,192 tokens, 32/8 heads of 128, bf16), whose metric is
-algorithmic TFLOP/s.
+workload (4 x 8,192 tokens, 32/8 heads of 128, bf16) and an `extend` object
+for chunked prefill (the last 512-token chunk of those prompts against the
+7,680 rows already cached), both in algorithmic TFLOP/s.
 
 `roofline` is measured for the dominant call of each workload with HIP
 events recorded on the stream the library launches on: for decode, the same
@@ -314,6 +315,105 @@ def cpu_prefill(w, q, k, v, torch, budget_s=12.0):
                       f"(sequence, head) pairs ({spent:.1f} s)"}
 
 
+# ---------------------------------------------------------------- extend
+EXTEND_CHUNK = 512
+
+
+def extend_flops(batch, ctx, chunk, n_q, d):
+    """4*d per visible (query, key) pair: query t of the chunk sees ctx + t + 1 keys."""
+    pairs = chunk * ctx + chunk * (chunk + 1) // 2
+    return 4 * d * pairs * batch * n_q
+
+
+def bench_extend(steps, warmup, torch, kv, with_cpu):
+    """Chunked prefill: the last 512-token chunk of the four 8,192-token
+    prompts of the prefill workload, against the 7,680 cached rows before it.
+    A step writes the chunk's K/V into the paged cache (kvc_write at 7,680)
+    and runs kvc_attn_extend on its queries; the roofline times the
+    attention call."""
+    from workloads import prefill_workload
+    w = prefill_workload()
+    ctx = w.T - EXTEND_CHUNK
+    qn, kn, vn = w.qkv()
+    q = torch.from_numpy(qn[:, ctx:]).to(torch.bfloat16).cuda().contiguous()
+    k, v = (torch.from_numpy(a).to(torch.bfloat16).cuda() for a in (kn, vn))
+    del qn, kn, vn
+    nb = -(-w.T // 16)
+    c = kv.KvCache(1, w.n_q, w.n_kv, w.d, w.batch * nb, w.batch, nb, "bf16")
+    perm = np.random.default_rng(5).permutation(w.batch * nb).astype(np.int32)
+    for b in range(w.batch):
+        c.set_block_table(b, perm[b * nb:(b + 1) * nb], w.T)
+    seqs = torch.arange(w.batch, dtype=torch.int32, device="cuda")
+    c.write(0, seqs, 0, k[:, :ctx].contiguous(), v[:, :ctx].contiguous())
+    kc, vc = k[:, ctx:].contiguous(), v[:, ctx:].contiguous()
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        c.write(0, seqs, ctx, kc, vc)
+        if ev is not None:
+            ev[0].record(stream)
+        c.attn_extend(0, seqs, q, out=out)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    flops = extend_flops(w.batch, ctx, EXTEND_CHUNK, w.n_q, w.d)
+    call_s = float(np.mean([a.elapsed_time(b) for a, b in events])) / 1e3
+    achieved = flops / call_s / 1e12
+    res = {
+        "workload": "llama8b_extend",
+        "value": flops * steps / wall / 1e12, "unit": "TFLOP/s",
+        "ms_per_step": wall / steps * 1e3,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
+                     "traffic": counter_traffic("extend_llama8b_extend"),
+                     "kernel": "kvc_attn_extend (paged causal chunk attention)",
+                     "avg_call_us": call_s * 1e6, "flops_per_call": flops},
+        "shape": {"batch": w.batch, "context": ctx, "chunk": EXTEND_CHUNK, "n_q": w.n_q,
+                  "n_kv": w.n_kv, "d": w.d},
+    }
+    if with_cpu:
+        res["cpu_baseline"] = cpu_extend(w, ctx, q, k, v)
+    return res
+
+
+def cpu_extend(w, ctx, q, k, v, budget_s=12.0):
+    """The float64 oracle on the same chunk, one (sequence, query head) at a
+    time, until the budget is used; reported as algorithmic TFLOP/s."""
+    from oracle import attention as A
+    scale = 1.0 / math.sqrt(w.d)
+    G = w.n_q // w.n_kv
+    spent, heads = 0.0, 0
+    for b in range(w.batch):
+        for h in range(w.n_q):
+            qh = q[b, :, h].double().cpu().numpy()
+            kh = k[b, :, h // G].double().cpu().numpy()
+            vh = v[b, :, h // G].double().cpu().numpy()
+            t0 = time.perf_counter()
+            A.attention(qh, kh, vh, scale, q_pos=np.arange(ctx, w.T))
+            spent += time.perf_counter() - t0
+            heads += 1
+            if spent >= budget_s:
+                break
+        if spent >= budget_s:
+            break
+    flops = extend_flops(1, ctx, EXTEND_CHUNK, 1, w.d) * heads
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": cpu_cores(),
+            "blas_threads": blas_threads(), "kind": "oracle",
+            "sample": f"float64 oracle chunk attention of {heads} of {w.batch * w.n_q} "
+                      f"(sequence, head) pairs ({spent:.1f} s)"}
+
+
 DECODE_WORKLOADS = {
     "llama8b_decode": "40 sequences, 32 q / 8 kv heads, d 128, bf16 cache, 16-token blocks, "
                       "shuffled tables, lengths uniform in [512, 4096]; grow + kv_append + decode",
@@ -332,7 +432,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b_decode",
-                    choices=sorted(DECODE_WORKLOADS) + ["llama8b_prefill"])
+                    choices=sorted(DECODE_WORKLOADS) + ["llama8b_prefill", "llama8b_extend"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-prefill", action="store_true",
                     help="headline decode only (no prefill section)")
@@ -362,6 +462,18 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     with_cpu = not args.no_cpu
 
+    if args.workload == "llama8b_extend":
+        ex = bench_extend(args.steps, args.warmup, torch, kv, with_cpu)
+        line = {"metric": METRIC, "value": ex["value"], "unit": "TFLOP/s", "n_gpus": 1,
+                "steps": args.steps, "warmup": args.warmup, "ms_per_step": ex["ms_per_step"],
+                "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                "dtype": "bf16", "data": "synthetic (seeded N(0,1))",
+                "config": {"workload": "llama8b_extend: last 512-token chunk of 4 x 8,192-token "
+                                       "prompts against 7,680 cached rows, 32 q / 8 kv heads, "
+                                       "d 128, bf16 paged cache"},
+                "roofline": ex["roofline"], "cpu_baseline": ex.get("cpu_baseline")}
+        print(json.dumps(line))
+        return
     if args.workload == "llama8b_prefill":
         pf = bench_prefill(args.steps, args.warmup, torch, kv, with_cpu)
         line = {"metric": METRIC, "value": pf["value"], "unit": "TFLOP/s", "n_gpus": 1,
@@ -385,6 +497,7 @@ def main():
             "roofline": dec["roofline"], "cpu_baseline": dec.get("cpu_baseline")}
     if args.workload == "llama8b_decode" and not args.no_prefill:
         line["prefill"] = bench_prefill(max(3, args.steps // 4), 1, torch, kv, with_cpu)
+        line["extend"] = bench_extend(max(5, args.steps // 2), 2, torch, kv, with_cpu)
     print(json.dumps(line))
 
 

@@ -140,6 +140,12 @@ int kvc_seq_alloc(kvc_cache* cache, int32_t seq, int32_t n_tokens, hipStream_t s
  * updated on `stream`. */
 int kvc_seq_grow(kvc_cache* cache, int32_t n, const int32_t* seqs_host, hipStream_t stream);
 
+/* Grow one live sequence by n_tokens at once (a prompt chunk): the same
+ * blocks, in the same order, as n_tokens single-token grows of that sequence
+ * (kvcache-7e2 PagedAttention: a block is taken when a token starts one).
+ * All or nothing: KVC_E_NO_BLOCKS or KVC_E_INVAL leave the state unchanged. */
+int kvc_seq_grow_by(kvc_cache* cache, int32_t seq, int32_t n_tokens, hipStream_t stream);
+
 /* Return all blocks of `seq` to the free list, in table order (the page's
  * release), and mark it not live (device length 0, table entries -1). */
 int kvc_seq_release(kvc_cache* cache, int32_t seq, hipStream_t stream);
@@ -186,6 +192,23 @@ int kvc_write(kvc_cache* cache, int32_t layer, int32_t n, const int32_t* seqs_de
 int kvc_attn_prefill(kvc_cache* cache, int32_t layer, int32_t n, const int32_t* seqs_dev,
                      int32_t T, const void* q_dev, const void* k_dev, const void* v_dev,
                      void* out_dev, float scale, hipStream_t stream);
+
+/* attn_extend: T new query rows per sequence against everything the cache
+ * holds for it, the new rows' own K/V included (written before the call,
+ * e.g. by kvc_write at start = len - T).  Query t of sequence s sits at
+ * position len(s) - T + t and sees cached rows 0 .. len(s) - T + t: one chunk
+ * of a prompt processed against the chunks before it (kvcache-7e2
+ * continuous-batching section: chunked prefill; abhishekpatel.co: long
+ * prefills split into chunks), or the target's pass over T drafted tokens
+ * (kvcache-7e2 speculative-decoding section).  q_dev, out_dev:
+ * [n][T][n_q_heads][d_head] in the io type, 16-byte aligned.  bf16 and f16
+ * caches (KVC_E_UNSUPPORTED otherwise); scale finite and > 0.  A device
+ * entry that is out of range, has len < T, or whose table holds an invalid
+ * block id among its first ceil(len/16) entries gets NaN rows.  No
+ * workspace. */
+int kvc_attn_extend(kvc_cache* cache, int32_t layer, int32_t n, const int32_t* seqs_dev,
+                    int32_t T, const void* q_dev, void* out_dev, float scale,
+                    hipStream_t stream);
 
 /* Workspace bytes kvc_attn_decode needs for a batch of n sequences with this
  * num_splits (0 = automatic), given the longest live sequence of the cache

@@ -63,6 +63,7 @@ _SIGS = {
     "kvc_destroy": [_P],
     "kvc_seq_alloc": [_P, _I, _I, _P],
     "kvc_seq_grow": [_P, _I, ctypes.POINTER(_I), _P],
+    "kvc_seq_grow_by": [_P, _I, _I, _P],
     "kvc_seq_release": [_P, _I, _P],
     "kvc_set_block_table": [_P, _I, ctypes.POINTER(_I), _I, _I, _P],
     "kvc_seq_len": [_P, _I, ctypes.POINTER(_I)],
@@ -71,6 +72,7 @@ _SIGS = {
     "kvc_append": [_P, _I, _I, _P, _P, _P, _P],
     "kvc_write": [_P, _I, _I, _P, _I, _I, _P, _P, _P],
     "kvc_attn_prefill": [_P, _I, _I, _P, _I, _P, _P, _P, _P, ctypes.c_float, _P],
+    "kvc_attn_extend": [_P, _I, _I, _P, _I, _P, _P, ctypes.c_float, _P],
     "kvc_decode_workspace_bytes": [_P, _I, _I, ctypes.POINTER(ctypes.c_uint64)],
     "kvc_attn_decode": [_P, _I, _I, _P, _P, _P, ctypes.c_float, _I, _P, ctypes.c_uint64, _P],
     "kvc_gather": [_P, _I, _I, _I, _I, _P, _P, _P],
@@ -191,6 +193,9 @@ class KvCache:
     def seq_release(self, seq):
         _check(lib().kvc_seq_release(self._h, seq, self._s()))
 
+    def seq_grow_by(self, seq, n_tokens):
+        _check(lib().kvc_seq_grow_by(self._h, seq, n_tokens, self._s()))
+
     def set_block_table(self, seq, blocks, length):
         arr = (_I * len(blocks))(*[int(b) for b in blocks])
         _check(lib().kvc_set_block_table(self._h, seq, arr, len(blocks), length, self._s()))
@@ -252,6 +257,20 @@ class KvCache:
         _check(lib().kvc_attn_prefill(
             self._h, layer, n, sp, T, self._io(q, (n, T, self.n_q, self.d), "q"),
             self._io(k, (n, T, self.n_kv, self.d), "k"), self._io(v, (n, T, self.n_kv, self.d), "v"),
+            self._io(out, (n, T, self.n_q, self.d), "out"), ctypes.c_float(scale), _stream()))
+        return out
+
+    def attn_extend(self, layer, seqs, q, scale=None, out=None):
+        """T new query rows per sequence (q [n, T, n_q, d]) against the whole
+        cached context, whose last T rows are the new tokens' own K/V."""
+        n, T = q.shape[0], q.shape[1]
+        scale = 1.0 / math.sqrt(self.d) if scale is None else scale
+        if seqs.numel() != n:
+            raise ValueError("seqs must have one entry per query block")
+        if out is None:
+            out = torch.empty((n, T, self.n_q, self.d), dtype=self.io_dtype, device=q.device)
+        _check(lib().kvc_attn_extend(
+            self._h, layer, n, self._seqs(seqs), T, self._io(q, (n, T, self.n_q, self.d), "q"),
             self._io(out, (n, T, self.n_q, self.d), "out"), ctypes.c_float(scale), _stream()))
         return out
 

@@ -260,6 +260,32 @@ int kvc_seq_grow(kvc_cache* c, int32_t n, const int32_t* seqs, hipStream_t strea
   return up.finish();
 }
 
+int kvc_seq_grow_by(kvc_cache* c, int32_t seq, int32_t n_tokens, hipStream_t stream) {
+  if (!c) return fail(KVC_E_INVAL, "cache is NULL");
+  int r = check_seq(c, seq);
+  if (r) return r;
+  if (!c->live[seq]) return fail(KVC_E_STATE, "sequence is not live");
+  if (n_tokens < 0) return fail(KVC_E_INVAL, "negative token count");
+  const int64_t len = c->len[seq], to = len + n_tokens;
+  if (to > (int64_t)c->cfg.max_blocks_per_seq * kBlock)
+    return fail(KVC_E_INVAL, "sequence would exceed its table width");
+  // one block per token that starts a block: the blocks n single-token
+  // grows would take, in the same (last-freed-first) order
+  const int64_t need = (to + kBlock - 1) / kBlock - (len + kBlock - 1) / kBlock;
+  if (need > (int64_t)c->free_list.size()) return fail(KVC_E_NO_BLOCKS, "free list exhausted");
+  Uploader up(c, stream);
+  for (int64_t i = 0; i < need; ++i) {
+    int32_t b = c->free_list.back();
+    c->free_list.pop_back();
+    c->owned[b] = 1;
+    up.bt(seq, (int32_t)c->table[seq].size(), b);
+    c->table[seq].push_back(b);
+  }
+  c->len[seq] = (int32_t)to;
+  up.len(seq, c->len[seq]);
+  return up.finish();
+}
+
 int kvc_seq_release(kvc_cache* c, int32_t seq, hipStream_t stream) {
   if (!c) return fail(KVC_E_INVAL, "cache is NULL");
   int r = check_seq(c, seq);
@@ -393,6 +419,28 @@ int kvc_attn_prefill(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs
   if (seqs) e = launch_write(c->view(), layer, n, seqs, 0, T, k, v, stream);
   if (e == hipSuccess) e = launch_prefill(c->view(), n, T, q, k, v, out, scale, stream);
   return e == hipSuccess ? KVC_OK : hip_fail(e, "prefill launch");
+}
+
+int kvc_attn_extend(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs, int32_t T,
+                    const void* q, void* out, float scale, hipStream_t stream) {
+  if (!c) return fail(KVC_E_INVAL, "cache is NULL");
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(KVC_E_INVAL, "scale must be finite and positive");
+  if (c->cfg.kv_dtype != KVC_BF16 && c->cfg.kv_dtype != KVC_F16)
+    return fail(KVC_E_UNSUPPORTED, "attn_extend needs a bf16 or f16 cache");
+  int r = need_dev(c);
+  if (r) return r;
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(KVC_E_STATE, "layer out of range");
+  if (n < 0 || T < 0) return fail(KVC_E_INVAL, "negative size");
+  if (n == 0 || T == 0) return KVC_OK;
+  if ((int64_t)T > (int64_t)c->cfg.max_blocks_per_seq * kBlock)
+    return fail(KVC_E_INVAL, "more query rows than a sequence can hold");
+  if (!seqs || !q || !out) return fail(KVC_E_INVAL, "NULL device pointer");
+  if (!aligned16(q) || !aligned16(out)) return fail(KVC_E_INVAL, "q/out must be 16-byte aligned");
+  bool handled = false;
+  hipError_t e = launch_extend(c->view(), layer, n, seqs, T, q, out, scale, stream, &handled);
+  if (e == hipSuccess && !handled) return fail(KVC_E_UNSUPPORTED, "no extend kernel for this shape");
+  return e == hipSuccess ? KVC_OK : hip_fail(e, "extend launch");
 }
 
 int kvc_decode_workspace_bytes(const kvc_cache* c, int32_t n, int32_t num_splits, uint64_t* out) {

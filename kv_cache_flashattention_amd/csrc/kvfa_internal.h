@@ -75,5 +75,9 @@ hipError_t launch_decode(const CacheView& cv, int layer, int n, const int32_t* s
                          void* ws, hipStream_t s);
 hipError_t launch_prefill(const CacheView& cv, int n, int T, const void* q, const void* k,
                           const void* v, void* out, float scale, hipStream_t s);
+// T query rows per sequence against the paged cache (bf16 / f16 caches);
+// *handled = false when the cache type has no such kernel.
+hipError_t launch_extend(const CacheView& cv, int layer, int n, const int32_t* seqs, int T,
+                         const void* q, void* out, float scale, hipStream_t s, bool* handled);
 
 }  // namespace kvfa

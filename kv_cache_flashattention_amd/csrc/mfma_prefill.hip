@@ -148,14 +148,20 @@ __device__ __forceinline__ int row_key(int r) {
   return (jj < 2) ? 8 * h + 4 * jj + i : 16 + 8 * h + 4 * (jj - 2) + i;
 }
 
-template <int D, bool F16>
+// PAGED = false: whole prompts, K/V rows [n][T][n_kv][d] beside the queries,
+// query t at position t.  PAGED = true: T new query rows per sequence
+// against the len(s) rows the paged cache holds for it (the new rows'
+// K/V included), query t at position len(s) - T + t; K/V tiles are staged
+// straight from the (block, kv head) slabs through the block table.
+template <int D, bool F16, bool PAGED>
 __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int T,
                                                          const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v,
                                                          uint16_t* __restrict__ out, float sl2,
                                                          int ntiles, int n_seq, int n_units,
-                                                         int xcd_split) {
+                                                         int xcd_split, CacheView cv, int layer,
+                                                         const int32_t* __restrict__ seqs) {
   typedef typename Op<F16>::T OpT;
   constexpr int KS = D / 16;        // k-steps of QK^T
   constexpr int DT = D / 32;        // 32-row tiles of O^T
@@ -188,10 +194,34 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
   const int qrow = rq0 + col;                          // this lane's query position
   const int64_t qstride = (int64_t)n_q * D, kvstride = (int64_t)n_kv * D;
 
-  const int kend = min(T, q0 + BM);                    // keys any row of the workgroup sees
+  // ---- keys: L rows; query row t sits at position qoff + t
+  int L = T, seq = 0;
+  if constexpr (PAGED) {
+    seq = seqs[b];
+    bool bad = seq < 0 || seq >= cv.max_seqs;
+    L = bad ? 0 : cv.len[seq];
+    bad = bad || L < T || L > cv.max_bps * kBlock;
+    if (!bad) {
+      const int32_t* bt = cv.bt + (int64_t)seq * cv.max_bps;
+      for (int j = tid; j < (L + kBlock - 1) / kBlock; j += 512) {
+        const int e = bt[j];
+        bad = bad || e < 0 || e >= cv.n_blocks;
+      }
+    }
+    if (__syncthreads_or(bad)) {                       // invalid entry: NaN rows
+      const uint16_t nan = F16 ? 0x7E00 : 0x7FC0;
+      for (int e = tid; e < BM * D; e += 512) {
+        const int row = q0 + e / D;
+        if (row < T) out[((int64_t)b * T + row) * qstride + (int64_t)head * D + e % D] = nan;
+      }
+      return;
+    }
+  }
+  const int qoff = L - T;
+  const int kend = min(L, qoff + q0 + BM);             // keys any row of the workgroup sees
   const int nkt = (kend + BN - 1) / BN;
-  // tiles this wave computes on: those holding a key <= its last row
-  const int wn = rq0 < T ? min(nkt, (rq0 + 31) / BN + 1) : 0;
+  // tiles this wave computes on: those holding a key <= its last row's position
+  const int wn = rq0 < T ? min(nkt, (qoff + rq0 + 31) / BN + 1) : 0;
 
   // ---- query operand (B of S^T = K Q^T)
   OpT qop[KS];
@@ -202,22 +232,37 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
       qop[ks] = __builtin_bit_cast(OpT, *(const u32x4*)(qp + 16 * ks + 8 * half));
   }
 
-  // ---- staging through registers.  Rows past the prompt's end load row
-  // T-1 instead: their scores are masked (the key is after every query), so
+  // ---- staging through registers.  Rows past the last key load row L-1
+  // instead: their scores are masked (the key is after every query), so
   // they contribute exp(-inf) * finite = 0.
   constexpr int KCH = BN * D / 8 / 256;                // 16-byte K chunks per group thread
-  constexpr int VBL = (BN / 4) * (D / 8);              // 4x8 V blocks per tile
+  constexpr int VBL = (BN / 4) * (D / 8);              // prompt: 4x8 V blocks per tile
+  constexpr int VCH = D * BN / 8 / 256;                // paged: 16-byte V^T chunks per thread
   u32x4 sreg[4];                                       // plain vectors: stay in registers
   const uint16_t* kbase = k + (int64_t)b * T * kvstride + (int64_t)g * D;
   const uint16_t* vbase = v + (int64_t)b * T * kvstride + (int64_t)g * D;
+  // paged: slab (block e, kv head g) of this layer starts at pool + e * slab
+  const int64_t slab = (int64_t)n_kv * kBlock * D;
+  const uint16_t* kpool = (const uint16_t*)cv.k + ((int64_t)layer * cv.n_blocks * n_kv + g) * kBlock * D;
+  const uint16_t* vpool = (const uint16_t*)cv.v + ((int64_t)layer * cv.n_blocks * n_kv + g) * kBlock * D;
+  const int32_t* btab = cv.bt + (int64_t)seq * cv.max_bps;
   auto load_k = [&](int i) {
-    const uint16_t* tb = kbase + (int64_t)(BN * i) * kvstride;
-    const int lim = T - 1 - BN * i;                    // last valid row of the tile
+    const int lim = L - 1 - BN * i;                    // last valid row of the tile
     const int t = opaque_tid() & 255;
+    if constexpr (PAGED) {
 #pragma unroll
-    for (int c0 = 0; c0 < KCH; ++c0) {
-      const int row = min(t / KG + c0 * (256 / KG), lim);
-      sreg[c0] = *(const u32x4*)(tb + row * kvstride + 8 * (t % KG));
+      for (int c0 = 0; c0 < KCH; ++c0) {
+        const int kp = BN * i + min(t / KG + c0 * (256 / KG), lim);
+        const uint16_t* sl = kpool + btab[kp >> 4] * slab;
+        sreg[c0] = *(const u32x4*)(sl + (kp & (kBlock - 1)) * D + 8 * (t % KG));
+      }
+    } else {
+      const uint16_t* tb = kbase + (int64_t)(BN * i) * kvstride;
+#pragma unroll
+      for (int c0 = 0; c0 < KCH; ++c0) {
+        const int row = min(t / KG + c0 * (256 / KG), lim);
+        sreg[c0] = *(const u32x4*)(tb + row * kvstride + 8 * (t % KG));
+      }
     }
   };
   auto store_k = [&](int buf) {
@@ -226,14 +271,26 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
     for (int c0 = 0; c0 < KCH; ++c0)
       *(u32x4*)&Ks[buf][(t / KG + c0 * (256 / KG)) * KP + 8 * (t % KG)] = sreg[c0];
   };
-  // V: thread (kg, dg) moves keys 4kg..4kg+3 of d-granule dg; the 16 lanes
-  // of one LDS write pass cover one whole V^T row.
+  // Prompt V: thread (kg, dg) moves keys 4kg..4kg+3 of d-granule dg,
+  // transposing them; the 16 lanes of one LDS write pass cover one whole
+  // V^T row.  Paged V: the slabs are already [d][16], so chunk c = (d row
+  // c / 8, block (c / 2) % 4 of the tile, half c % 2) is a plain 16-byte
+  // copy; keys at or past L (stale slots of the last block, blocks past the
+  // end) are zeroed, since 0 * NaN would poison the PV product.
   auto load_v = [&](int i) {
     const int t = opaque_tid() & 255;
-    if (t < VBL) {
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int c0 = 0; c0 < VCH; ++c0) {
+        const int c = t + 256 * c0, rr = c >> 3, j = (c >> 1) & 3, h = c & 1;
+        const int kb = min(BN * i + kBlock * j, L - 1) >> 4;
+        const uint16_t* sl = vpool + btab[kb] * slab;
+        sreg[c0] = *(const u32x4*)(sl + rr * kBlock + 8 * h);
+      }
+    } else if (t < VBL) {
       const int kg = t % (BN / 4), dg = t / (BN / 4);
       const uint16_t* tb = vbase + (int64_t)(BN * i) * kvstride;
-      const int lim = T - 1 - BN * i;
+      const int lim = L - 1 - BN * i;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = min(4 * kg + r, lim);
@@ -241,9 +298,25 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
       }
     }
   };
-  auto store_v = [&](int buf) {
+  auto store_v = [&](int buf, int i) {
     const int t = opaque_tid() & 255;
-    if (t < VBL) {
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int c0 = 0; c0 < VCH; ++c0) {
+        const int c = t + 256 * c0, rr = c >> 3, j = (c >> 1) & 3, h = c & 1;
+        const int nvalid = L - (BN * i + kBlock * j + 8 * h);   // keys of the chunk below L
+        u32x4 x = sreg[c0];
+        if (nvalid < 8) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t keep = (2 * e + 1 < nvalid) ? 0xFFFFFFFFu
+                                : (2 * e < nvalid) ? 0x0000FFFFu : 0u;
+            x[e] &= keep;
+          }
+        }
+        *(u32x4*)&Vt[buf][rr * VP + kBlock * j + 8 * h] = x;
+      }
+    } else if (t < VBL) {
       const int kg = t % (BN / 4), dg = t / (BN / 4);
 #pragma unroll
       for (int dd = 0; dd < 8; ++dd) {
@@ -286,10 +359,10 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
   // online softmax of tile i, first half: mask, row max, rescale of O and l
   auto rowmax = [&](int i) {
     const int k0 = BN * i;
-    if (k0 + BN - 1 > rq0) {                           // tile reaches past the wave's first row
+    if (k0 + BN - 1 > qoff + rq0) {                    // tile reaches past the wave's first row
       // element e of sacc[st] holds key k0 + 32 st + 8 half + kofs(e)
       const int t = opaque_tid();
-      const int thr = rq0 + (t & 31) - k0 - 8 * ((t >> 5) & 1);
+      const int thr = qoff + rq0 + (t & 31) - k0 - 8 * ((t >> 5) & 1);
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -397,7 +470,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
         if (i + 3 < nkt) load_k(i + 3);
       }
     } else if (i < nkt) {
-      store_v(i & 1);
+      store_v(i & 1, i);
       if (i + 1 < nkt) load_v(i + 1);
     }
     if (i < wn) expo(i);
@@ -429,17 +502,35 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
     }
 }
 
-template <int D, bool F16>
-hipError_t run(const CacheView& cv, int n, int T, const void* q, const void* k, const void* v,
-               void* out, float sl2, hipStream_t s) {
+template <int D, bool F16, bool PAGED>
+hipError_t run(const CacheView& cv, int layer, int n, const int32_t* seqs, int T, const void* q,
+               const void* k, const void* v, void* out, float sl2, hipStream_t s) {
   const int ntiles = (T + BM - 1) / BM;
   const int64_t units = (int64_t)cv.n_q * n * ntiles;
   if (units > INT32_MAX) return hipErrorInvalidValue;
   const int xcd_split = units % 8 == 0 ? 1 : 0;
-  hipLaunchKernelGGL((k_prefill_mfma<D, F16>), dim3((uint32_t)units), dim3(512), 0, s, cv.n_q,
-                     cv.n_kv, T, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                     (uint16_t*)out, sl2, ntiles, n, (int)units, xcd_split);
+  hipLaunchKernelGGL((k_prefill_mfma<D, F16, PAGED>), dim3((uint32_t)units), dim3(512), 0, s,
+                     cv.n_q, cv.n_kv, T, (const uint16_t*)q, (const uint16_t*)k,
+                     (const uint16_t*)v, (uint16_t*)out, sl2, ntiles, n, (int)units, xcd_split,
+                     cv, layer, seqs);
   return hipGetLastError();
+}
+
+template <bool PAGED>
+hipError_t dispatch(const CacheView& cv, int layer, int n, const int32_t* seqs, int T,
+                    const void* q, const void* k, const void* v, void* out, float sl2,
+                    hipStream_t s, bool* handled) {
+  *handled = true;
+  const int io = io_dtype(cv.dtype);
+  if (io == KVC_BF16 && (!PAGED || cv.dtype == KVC_BF16)) {
+    if (cv.d == 128) return run<128, false, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, s);
+    if (cv.d == 64) return run<64, false, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, s);
+  } else if (io == KVC_F16) {
+    if (cv.d == 128) return run<128, true, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, s);
+    if (cv.d == 64) return run<64, true, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, s);
+  }
+  *handled = false;
+  return hipSuccess;
 }
 
 }  // namespace
@@ -447,17 +538,13 @@ hipError_t run(const CacheView& cv, int n, int T, const void* q, const void* k, 
 hipError_t launch_prefill_mfma(const CacheView& cv, int n, int T, const void* q, const void* k,
                                const void* v, void* out, float sl2, hipStream_t s,
                                bool* handled) {
-  *handled = true;
-  const int io = io_dtype(cv.dtype);
-  if (io == KVC_BF16) {
-    if (cv.d == 128) return run<128, false>(cv, n, T, q, k, v, out, sl2, s);
-    if (cv.d == 64) return run<64, false>(cv, n, T, q, k, v, out, sl2, s);
-  } else if (io == KVC_F16) {
-    if (cv.d == 128) return run<128, true>(cv, n, T, q, k, v, out, sl2, s);
-    if (cv.d == 64) return run<64, true>(cv, n, T, q, k, v, out, sl2, s);
-  }
-  *handled = false;
-  return hipSuccess;
+  return dispatch<false>(cv, 0, n, nullptr, T, q, k, v, out, sl2, s, handled);
+}
+
+hipError_t launch_extend_mfma(const CacheView& cv, int layer, int n, const int32_t* seqs, int T,
+                              const void* q, void* out, float sl2, hipStream_t s,
+                              bool* handled) {
+  return dispatch<true>(cv, layer, n, seqs, T, q, nullptr, nullptr, out, sl2, s, handled);
 }
 
 }  // namespace kvfa

@@ -16,6 +16,9 @@ namespace kvfa {
 hipError_t launch_prefill_mfma(const CacheView& cv, int n, int T, const void* q, const void* k,
                                const void* v, void* out, float scale_log2, hipStream_t s,
                                bool* handled);
+hipError_t launch_extend_mfma(const CacheView& cv, int layer, int n, const int32_t* seqs, int T,
+                              const void* q, void* out, float scale_log2, hipStream_t s,
+                              bool* handled);
 
 namespace {
 
@@ -119,6 +122,11 @@ hipError_t launch_prefill(const CacheView& cv, int n, int T, const void* q, cons
     case KVC_F16: return run_valu<_Float16>(cv, n, T, q, k, v, out, sl2, s);
     default: return run_valu<BF16>(cv, n, T, q, k, v, out, sl2, s);
   }
+}
+
+hipError_t launch_extend(const CacheView& cv, int layer, int n, const int32_t* seqs, int T,
+                         const void* q, void* out, float scale, hipStream_t s, bool* handled) {
+  return launch_extend_mfma(cv, layer, n, seqs, T, q, out, scale * kLog2e, s, handled);
 }
 
 }  // namespace kvfa

@@ -64,6 +64,14 @@ class PagedCacheModel:
                 self.table[s].append(self.free.pop())
             self.length[s] += 1
 
+    def grow_by(self, seq, n):
+        """n single-token grows of one sequence (a prompt chunk)."""
+        need = -(-(self.length[seq] + n) // BLOCK) - -(-self.length[seq] // BLOCK)
+        if need > len(self.free):
+            raise MemoryError("no free blocks")
+        for _ in range(n):
+            self.grow([seq])
+
     def release(self, seq):
         self.free.extend(self.table.pop(seq))
         del self.length[seq]

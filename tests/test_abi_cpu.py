@@ -99,6 +99,21 @@ def test_allocator_matches_the_page_listing_model():
             else:
                 with pytest.raises(kv.KvcError):
                     c.seq_alloc(s, n)
+        elif op < 0.45 and live:
+            s = rng.choice(live)
+            n = rng.randrange(0, 40)
+            need = -(-(m.length[s] + n) // 16) - -(-m.length[s] // 16)
+            if m.length[s] + n > 8 * 16:
+                with pytest.raises(kv.KvcError) as e:
+                    c.seq_grow_by(s, n)
+                assert e.value.code == kv.KVC_E_INVAL
+            elif need > len(m.free):
+                with pytest.raises(kv.KvcError) as e:
+                    c.seq_grow_by(s, n)
+                assert e.value.code == kv.KVC_E_NO_BLOCKS
+            else:
+                m.grow_by(s, n)
+                c.seq_grow_by(s, n)
         elif op < 0.8 and live:
             seqs = rng.sample(live, rng.randrange(1, len(live) + 1))
             if any(m.length[s] + 1 > 8 * 16 for s in seqs):
@@ -204,3 +219,11 @@ def test_decode_workspace_plan():
     f.seq_alloc(0, 4096)
     assert f.decode_workspace_bytes(40, num_splits=1) == 0
     assert f.decode_workspace_bytes(40, num_splits=4) == 40 * 32 * 4 * 130 * 4
+
+
+@pytest.mark.parametrize("dtype", ["f32", "fp8"])
+def test_extend_refuses_cache_types_without_a_kernel(dtype):
+    c = kv.KvCache(1, 8, 2, 128, 16, 2, 4, dtype, device=None)
+    p = ctypes.c_void_p(16)
+    rc = kv.lib().kvc_attn_extend(c._h, 0, 1, p, 4, p, p, ctypes.c_float(0.1), None)
+    assert rc == kv.KVC_E_UNSUPPORTED
