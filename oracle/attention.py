@@ -34,14 +34,32 @@ def softmax_rows(S):
     return E / np.sum(E, axis=-1, keepdims=True)
 
 
-def attention(q, k, v, scale, q_pos=None):
+def visible_keys(q_pos, L, window=0, sinks=0):
+    """Boolean [Tq, L]: key j is visible to the query at position p iff
+    j <= p (causal) and, when a window w > 0 is given, j is one of the w
+    most recent positions p - w + 1 .. p or one of the first `sinks`
+    positions.  The window is the sliding window of [KPF] "Sparse attention"
+    (each token sees only the previous w tokens) and [KVFA] eviction
+    paragraph (a window drops the oldest tokens); the sinks are the first
+    few tokens that attention-sink eviction always keeps ([KVFA], same
+    paragraph).  window = 0 means no window (full causal attention)."""
+    j = np.arange(L)[None, :]
+    p = np.asarray(q_pos)[:, None]
+    vis = j <= p
+    if window > 0:
+        vis &= (j > p - window) | (j < sinks)
+    return vis
+
+
+def attention(q, k, v, scale, q_pos=None, window=0, sinks=0):
     """Causal softmax attention of one head, fully materialised, float64.
 
     q: [Tq, d] queries; k, v: [L, d] keys and values in logical order.
     q_pos: absolute position of each query row (default: the last Tq
     positions, i.e. L - Tq .. L - 1, which is the bottom-right alignment a
     decode step or a whole-prompt prefill both use).  Key j is visible to a
-    query at position p iff j <= p.
+    query at position p iff j <= p, restricted by a sliding window and
+    attention sinks when window > 0 (``visible_keys``).
     Returns O = softmax(q k^T * scale + mask) v, shape [Tq, d].
     """
     q = np.asarray(q, dtype=np.float64)
@@ -52,13 +70,13 @@ def attention(q, k, v, scale, q_pos=None):
         q_pos = np.arange(L - Tq, L)
     q_pos = np.asarray(q_pos)
     S = (q @ k.T) * scale
-    visible = np.arange(L)[None, :] <= q_pos[:, None]
+    visible = visible_keys(q_pos, L, window, sinks)
     S = np.where(visible, S, -np.inf)
     P = softmax_rows(S)
     return P @ v
 
 
-def gqa_attention(q, k, v, scale, q_pos=None):
+def gqa_attention(q, k, v, scale, q_pos=None, window=0, sinks=0):
     """Grouped-query attention over all heads, float64.
 
     q: [Tq, n_q, d]; k, v: [L, n_kv, d] with n_q a multiple of n_kv.  Query
@@ -74,7 +92,7 @@ def gqa_attention(q, k, v, scale, q_pos=None):
     out = np.empty(q.shape, dtype=np.float64)
     for h in range(n_q):
         g = h // G
-        out[:, h, :] = attention(q[:, h, :], k[:, g, :], v[:, g, :], scale, q_pos)
+        out[:, h, :] = attention(q[:, h, :], k[:, g, :], v[:, g, :], scale, q_pos, window, sinks)
     return out
 
 
@@ -188,7 +206,7 @@ def merge_partials(m, l, O):
     return (w[:, None] * np.asarray(O)).sum(axis=0) / (w * np.asarray(l)).sum()
 
 
-def decode_attention(q, k, v, scale):
+def decode_attention(q, k, v, scale, window=0, sinks=0):
     """One decode step of one sequence: every cached row is visible.
 
     q: [n_q, d] (the new token's queries), k, v: [L, n_kv, d] with the new
@@ -197,20 +215,21 @@ def decode_attention(q, k, v, scale):
     Returns [n_q, d].
     """
     q = np.asarray(q, dtype=np.float64)
-    return gqa_attention(q[None], k, v, scale, q_pos=[k.shape[0] - 1])[0]
+    return gqa_attention(q[None], k, v, scale, q_pos=[k.shape[0] - 1], window=window,
+                         sinks=sinks)[0]
 
 
-def prefill_attention(q, k, v, scale):
+def prefill_attention(q, k, v, scale, window=0, sinks=0):
     """Causal attention of a whole prompt on an empty cache.
 
     q: [T, n_q, d]; k, v: [T, n_kv, d]; query t sees keys 0..t.
     Returns [T, n_q, d].
     """
     T = np.asarray(q).shape[0]
-    return gqa_attention(q, k, v, scale, q_pos=np.arange(T))
+    return gqa_attention(q, k, v, scale, q_pos=np.arange(T), window=window, sinks=sinks)
 
 
-def extend_attention(q, k, v, scale):
+def extend_attention(q, k, v, scale, window=0, sinks=0):
     """k new query rows against a cache that already holds their own rows.
 
     The cache holds L rows (the k new tokens' K/V rows included, appended
@@ -225,4 +244,4 @@ def extend_attention(q, k, v, scale):
     """
     Tq, L = np.asarray(q).shape[0], np.asarray(k).shape[0]
     assert 1 <= Tq <= L
-    return gqa_attention(q, k, v, scale, q_pos=np.arange(L - Tq, L))
+    return gqa_attention(q, k, v, scale, q_pos=np.arange(L - Tq, L), window=window, sinks=sinks)

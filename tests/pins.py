@@ -145,6 +145,58 @@ def check_chunked_equals_whole(extend_fn, prefill_fn, seed=12):
     return True
 
 
+def check_window_vs_sdpa(attention_fn, seed=13):
+    """Window/sink masks: equal torch SDPA with the explicit boolean mask
+    built from the rule written out element by element."""
+    rng = np.random.default_rng(seed)
+    for (Tq, L, w, s, d) in ((1, 50, 8, 0, 8), (1, 50, 8, 3, 8), (20, 20, 5, 2, 16),
+                             (7, 90, 30, 4, 8), (33, 100, 1, 0, 8), (33, 100, 1, 5, 8),
+                             (10, 40, 64, 2, 8)):
+        q = rng.standard_normal((Tq, 2, d))
+        k = rng.standard_normal((L, 1, d))
+        v = rng.standard_normal((L, 1, d))
+        pos = np.arange(L - Tq, L)
+        mask = np.zeros((Tq, L), dtype=bool)
+        for i, p in enumerate(pos):
+            for j in range(L):
+                mask[i, j] = j <= p and (p - j < w or j < s)
+        Q = torch.from_numpy(np.ascontiguousarray(q.transpose(1, 0, 2)))[None].double()
+        K = torch.from_numpy(np.ascontiguousarray(k.transpose(1, 0, 2)))[None].double()
+        V = torch.from_numpy(np.ascontiguousarray(v.transpose(1, 0, 2)))[None].double()
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            Q, K, V, attn_mask=torch.from_numpy(mask), scale=1 / math.sqrt(d),
+            enable_gqa=True)[0].numpy().transpose(1, 0, 2)
+        got = attention_fn(q, k, v, 1 / math.sqrt(d), pos, w, s)
+        if not np.allclose(got, ref, rtol=0, atol=1e-12):
+            return False
+    return True
+
+
+def check_window_special_cases(attention_fn, seed=14):
+    """A window of 1 without sinks returns each query's own value row; a
+    window at least as long as the context is full causal attention; a
+    window with sinks equals full attention over the kept rows gathered
+    explicitly (sinks, then the window), for one decode row."""
+    rng = np.random.default_rng(seed)
+    L, d = 60, 8
+    q = rng.standard_normal((L, 1, d))
+    k = rng.standard_normal((L, 1, d))
+    v = rng.standard_normal((L, 1, d))
+    pos = np.arange(L)
+    if not np.array_equal(attention_fn(q, k, v, 0.3, pos, 1, 0)[:, 0], v[:, 0]):
+        return False
+    if not np.allclose(attention_fn(q, k, v, 0.3, pos, L, 0),
+                       attention_fn(q, k, v, 0.3, pos, 0, 0), rtol=0, atol=1e-14):
+        return False
+    w, s = 12, 4
+    keep = np.r_[0:s, L - w:L]
+    got = attention_fn(q[-1:], k, v, 0.3, [L - 1], w, s)
+    sc = (k[keep, 0] @ q[-1, 0]) * 0.3
+    e = np.exp(sc - sc.max())
+    ref = (e / e.sum()) @ v[keep, 0]
+    return bool(np.allclose(got[0, 0], ref, rtol=0, atol=1e-13))
+
+
 def check_tiled_equals_definition(tiled_fn, attention_fn, seed=3):
     """The tiled flash loop (any tile sizes) reaches the definition."""
     rng = np.random.default_rng(seed)

@@ -186,3 +186,18 @@ def test_extend_off_by_one_is_caught():
         return A.gqa_attention(q, k, v, scale, q_pos=np.arange(L - Tq, L) - 0.5)
     assert not pins.check_extend_vs_sdpa(strict)
     assert not pins.check_chunked_equals_whole(strict, A.prefill_attention)
+
+
+def test_window_off_by_one_is_caught():
+    """A window that keeps w + 1 rows (j >= p - w instead of j > p - w)."""
+    def wide(q, k, v, scale, q_pos=None, window=0, sinks=0):
+        return A.gqa_attention(q, k, v, scale, q_pos, window + 1 if window else 0, sinks)
+    assert not pins.check_window_vs_sdpa(wide)
+    assert not pins.check_window_special_cases(wide)
+
+
+def test_sinks_ignored_is_caught():
+    def no_sinks(q, k, v, scale, q_pos=None, window=0, sinks=0):
+        return A.gqa_attention(q, k, v, scale, q_pos, window, 0)
+    assert not pins.check_window_vs_sdpa(no_sinks)
+    assert not pins.check_window_special_cases(no_sinks)

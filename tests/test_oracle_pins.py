@@ -38,6 +38,14 @@ def test_chunked_prefill_equals_whole_prompt():
     assert pins.check_chunked_equals_whole(A.extend_attention, A.prefill_attention)
 
 
+def test_window_and_sink_masks_match_torch_sdpa():
+    assert pins.check_window_vs_sdpa(A.gqa_attention)
+
+
+def test_window_and_sink_special_cases():
+    assert pins.check_window_special_cases(A.gqa_attention)
+
+
 def test_tiled_flash_loop_reaches_definition():
     assert pins.check_tiled_equals_definition(A.flash_attention_tiled, A.attention)
 
