@@ -13,7 +13,9 @@ tables, queries, outputs, table entries) divided by the wall-clock time per
 step.  The same JSON line carries a `prefill` object for the causal-prefill
 workload (4 x 8,192 tokens, 32/8 heads of 128, bf16) and an `extend` object
 for chunked prefill (the last 512-token chunk of those prompts against the
-7,680 rows already cached), both in algorithmic TFLOP/s.
+7,680 rows already cached), both in algorithmic TFLOP/s, and a
+`decode_window` object: the decode batch under a 1,024-row sliding window
+with 4 sink rows, in GB/s of the rows it can see.
 
 `roofline` is measured for the dominant call of each workload with HIP
 events recorded on the stream the library launches on: for decode, the same
@@ -126,6 +128,55 @@ def decode_bytes(w, lengths, kv_elem):
     tab = blocks * 4
     sc = 2 * blocks * w.n_kv * 4 if kv_elem == 1 else 0
     return kvb + qo + tab + sc
+
+
+def window_rows(L, window, sinks):
+    """Rows a decode query at position L-1 sees under a sliding window of
+    `window` rows plus `sinks` sink rows, and the blocks holding them."""
+    if window <= 0 or L <= window:
+        pos = np.arange(L)
+    else:
+        pos = np.r_[0:min(sinks, L - window), L - window:L]
+    return len(pos), len(np.unique(pos // 16))
+
+
+def bench_decode_window(steps, torch, kv, window=1024, sinks=4):
+    """The Llama-8B decode batch with a 1,024-row sliding window and 4 sink
+    rows: only the visible rows are read.  Algorithmic bytes count the
+    visible K/V rows, their table entries, Q and O; every call is preceded
+    by the Infinity-Cache eviction used for the decode roofline."""
+    w, c, io = build_decode("llama8b_decode", torch, kv)
+    seqs = torch.arange(w.batch, dtype=torch.int32, device="cuda")
+    q = torch.from_numpy(w.q()).to(io).cuda()
+    out = torch.empty((w.batch, w.n_q, w.d), dtype=io, device="cuda")
+    ws = torch.empty((max(c.decode_workspace_bytes(w.batch), 16),), dtype=torch.uint8,
+                     device="cuda")
+    vis = [window_rows(int(L), window, sinks) for L in w.lengths]
+    rows, blocks = sum(r for r, _ in vis), sum(b for _, b in vis)
+    per_call = 2 * rows * w.n_kv * w.d * 2 + 2 * w.batch * w.n_q * w.d * 2 + 4 * blocks
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        c.attn_decode(0, seqs, q, out=out, ws=ws, window=window, sinks=sinks)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        torch.sum(flush, dim=0, out=sink)
+        ev[i][0].record(stream)
+        c.attn_decode(0, seqs, q, out=out, ws=ws, window=window, sinks=sinks)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    call_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    achieved = per_call / call_s / 1e9
+    return {"workload": f"llama8b_decode, window {window} + {sinks} sink rows",
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "kvc_attn_decode_window (work list + merge)",
+                         "avg_call_us": call_s * 1e6, "bytes_per_call": per_call,
+                         "cache_evicted_before_each_call": True},
+            "visible_rows": rows, "all_rows": int(np.sum(w.lengths))}
 
 
 def bench_decode(name, steps, warmup, torch, kv, with_cpu):
@@ -498,6 +549,7 @@ def main():
     if args.workload == "llama8b_decode" and not args.no_prefill:
         line["prefill"] = bench_prefill(max(3, args.steps // 4), 1, torch, kv, with_cpu)
         line["extend"] = bench_extend(max(5, args.steps // 2), 2, torch, kv, with_cpu)
+        line["decode_window"] = bench_decode_window(max(5, args.steps // 2), torch, kv)
     print(json.dumps(line))
 
 

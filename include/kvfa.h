@@ -229,6 +229,28 @@ int kvc_attn_decode(kvc_cache* cache, int32_t layer, int32_t n, const int32_t* s
                     const void* q_dev, void* out_dev, float scale, int32_t num_splits,
                     void* ws_dev, uint64_t ws_bytes, hipStream_t stream);
 
+/* Sliding-window / attention-sink variants of the three attention calls
+ * (abhishekpatel.co "Sparse attention": each token sees only the previous w
+ * tokens; kvcache-7e2 eviction paragraph: a sliding window drops the oldest
+ * tokens, attention sinks always keep the first few).  With window > 0 the
+ * query at position p sees key j iff p - window < j <= p or j < sinks;
+ * window = 0 is full causal attention (sinks then change nothing).  Same
+ * arguments, layouts and errors as the calls above; window, sinks >= 0
+ * (KVC_E_INVAL otherwise); f32 caches have no windowed kernel
+ * (KVC_E_UNSUPPORTED when window > 0).  The decode reads only the blocks a
+ * query can see, so its cost follows min(len, window + sinks). */
+int kvc_attn_prefill_window(kvc_cache* cache, int32_t layer, int32_t n, const int32_t* seqs_dev,
+                            int32_t T, const void* q_dev, const void* k_dev, const void* v_dev,
+                            void* out_dev, float scale, int32_t window, int32_t sinks,
+                            hipStream_t stream);
+int kvc_attn_decode_window(kvc_cache* cache, int32_t layer, int32_t n, const int32_t* seqs_dev,
+                           const void* q_dev, void* out_dev, float scale, int32_t window,
+                           int32_t sinks, int32_t num_splits, void* ws_dev, uint64_t ws_bytes,
+                           hipStream_t stream);
+int kvc_attn_extend_window(kvc_cache* cache, int32_t layer, int32_t n, const int32_t* seqs_dev,
+                           int32_t T, const void* q_dev, void* out_dev, float scale,
+                           int32_t window, int32_t sinks, hipStream_t stream);
+
 /* Block-table gather: copy the stored bit patterns of positions start ..
  * start+count-1 of `seq` in logical order into k_out_dev, v_out_dev, each
  * [count][n_kv_heads][d_head] of the storage type (fp8: raw codes). */

@@ -75,6 +75,10 @@ _SIGS = {
     "kvc_attn_extend": [_P, _I, _I, _P, _I, _P, _P, ctypes.c_float, _P],
     "kvc_decode_workspace_bytes": [_P, _I, _I, ctypes.POINTER(ctypes.c_uint64)],
     "kvc_attn_decode": [_P, _I, _I, _P, _P, _P, ctypes.c_float, _I, _P, ctypes.c_uint64, _P],
+    "kvc_attn_decode_window": [_P, _I, _I, _P, _P, _P, ctypes.c_float, _I, _I, _I, _P,
+                               ctypes.c_uint64, _P],
+    "kvc_attn_prefill_window": [_P, _I, _I, _P, _I, _P, _P, _P, _P, ctypes.c_float, _I, _I, _P],
+    "kvc_attn_extend_window": [_P, _I, _I, _P, _I, _P, _P, ctypes.c_float, _I, _I, _P],
     "kvc_gather": [_P, _I, _I, _I, _I, _P, _P, _P],
     "kvc_last_error": [],
 }
@@ -246,7 +250,7 @@ class KvCache:
         _check(lib().kvc_write(self._h, layer, n, self._seqs(seqs), start, T,
                                self._io(k, shape, "k"), self._io(v, shape, "v"), _stream()))
 
-    def attn_prefill(self, layer, q, k, v, seqs=None, scale=None, out=None):
+    def attn_prefill(self, layer, q, k, v, seqs=None, scale=None, out=None, window=0, sinks=0):
         n, T = q.shape[0], q.shape[1]
         scale = 1.0 / math.sqrt(self.d) if scale is None else scale
         if out is None:
@@ -254,13 +258,17 @@ class KvCache:
         sp = self._seqs(seqs) if seqs is not None else ctypes.c_void_p(0)
         if seqs is not None and seqs.numel() != n:
             raise ValueError("seqs must have one entry per prompt")
-        _check(lib().kvc_attn_prefill(
-            self._h, layer, n, sp, T, self._io(q, (n, T, self.n_q, self.d), "q"),
-            self._io(k, (n, T, self.n_kv, self.d), "k"), self._io(v, (n, T, self.n_kv, self.d), "v"),
-            self._io(out, (n, T, self.n_q, self.d), "out"), ctypes.c_float(scale), _stream()))
+        args = (self._h, layer, n, sp, T, self._io(q, (n, T, self.n_q, self.d), "q"),
+                self._io(k, (n, T, self.n_kv, self.d), "k"),
+                self._io(v, (n, T, self.n_kv, self.d), "v"),
+                self._io(out, (n, T, self.n_q, self.d), "out"), ctypes.c_float(scale))
+        if window or sinks:
+            _check(lib().kvc_attn_prefill_window(*args, window, sinks, _stream()))
+        else:
+            _check(lib().kvc_attn_prefill(*args, _stream()))
         return out
 
-    def attn_extend(self, layer, seqs, q, scale=None, out=None):
+    def attn_extend(self, layer, seqs, q, scale=None, out=None, window=0, sinks=0):
         """T new query rows per sequence (q [n, T, n_q, d]) against the whole
         cached context, whose last T rows are the new tokens' own K/V."""
         n, T = q.shape[0], q.shape[1]
@@ -269,9 +277,12 @@ class KvCache:
             raise ValueError("seqs must have one entry per query block")
         if out is None:
             out = torch.empty((n, T, self.n_q, self.d), dtype=self.io_dtype, device=q.device)
-        _check(lib().kvc_attn_extend(
-            self._h, layer, n, self._seqs(seqs), T, self._io(q, (n, T, self.n_q, self.d), "q"),
-            self._io(out, (n, T, self.n_q, self.d), "out"), ctypes.c_float(scale), _stream()))
+        args = (self._h, layer, n, self._seqs(seqs), T, self._io(q, (n, T, self.n_q, self.d), "q"),
+                self._io(out, (n, T, self.n_q, self.d), "out"), ctypes.c_float(scale))
+        if window or sinks:
+            _check(lib().kvc_attn_extend_window(*args, window, sinks, _stream()))
+        else:
+            _check(lib().kvc_attn_extend(*args, _stream()))
         return out
 
     def decode_workspace_bytes(self, n, num_splits=0):
@@ -279,7 +290,10 @@ class KvCache:
         _check(lib().kvc_decode_workspace_bytes(self._h, n, num_splits, ctypes.byref(out)))
         return out.value
 
-    def attn_decode(self, layer, seqs, q, scale=None, num_splits=0, out=None, ws=None):
+    def attn_decode(self, layer, seqs, q, scale=None, num_splits=0, out=None, ws=None,
+                    window=0, sinks=0):
+        """One query row per sequence against its whole cache; window > 0
+        restricts it to the last `window` rows plus the first `sinks`."""
         n = seqs.numel()
         scale = 1.0 / math.sqrt(self.d) if scale is None else scale
         if out is None:
@@ -287,10 +301,16 @@ class KvCache:
         if ws is None:
             nb = self.decode_workspace_bytes(n, num_splits)
             ws = torch.empty((max(nb, 16),), dtype=torch.uint8, device=q.device)
-        _check(lib().kvc_attn_decode(
-            self._h, layer, n, self._seqs(seqs), self._io(q, (n, self.n_q, self.d), "q"),
-            self._io(out, (n, self.n_q, self.d), "out"), ctypes.c_float(scale), num_splits,
-            _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+        qp, op = self._io(q, (n, self.n_q, self.d), "q"), self._io(out, (n, self.n_q, self.d), "out")
+        wsp, wsb = _ptr(ws), ws.numel() * ws.element_size()
+        if window or sinks:
+            _check(lib().kvc_attn_decode_window(
+                self._h, layer, n, self._seqs(seqs), qp, op, ctypes.c_float(scale), window, sinks,
+                num_splits, wsp, wsb, _stream()))
+        else:
+            _check(lib().kvc_attn_decode(
+                self._h, layer, n, self._seqs(seqs), qp, op, ctypes.c_float(scale), num_splits,
+                wsp, wsb, _stream()))
         return out
 
     def gather(self, layer, seq, start, count):

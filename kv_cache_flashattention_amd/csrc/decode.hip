@@ -25,7 +25,7 @@ namespace kvfa {
 
 hipError_t launch_decode_mfma(const CacheView& cv, int layer, int n, const int32_t* seqs,
                               const void* q, void* out, float scale_log2, const DecodePlan& plan,
-                              void* ws, hipStream_t s, bool* handled);
+                              void* ws, int window, int sinks, hipStream_t s, bool* handled);
 
 DecodePlan make_decode_plan(const CacheView& cv, int32_t n, int32_t max_len, int32_t num_splits,
                             int32_t cu_count) {
@@ -242,11 +242,13 @@ hipError_t run_valu_d(const CacheView& cv, int layer, int n, const int32_t* seqs
 
 hipError_t launch_decode(const CacheView& cv, int layer, int n, const int32_t* seqs,
                          const void* q, void* out, float scale, const DecodePlan& plan,
-                         void* ws, hipStream_t s) {
+                         void* ws, int window, int sinks, hipStream_t s) {
   const float sl2 = scale * kLog2e;
   bool handled = false;
-  hipError_t e = launch_decode_mfma(cv, layer, n, seqs, q, out, sl2, plan, ws, s, &handled);
+  hipError_t e = launch_decode_mfma(cv, layer, n, seqs, q, out, sl2, plan, ws, window, sinks, s,
+                                    &handled);
   if (handled) return e;
+  if (window > 0) return hipErrorInvalidValue;          // the VALU kernel has no window
   if (cv.d == 128) return run_valu_d<128>(cv, layer, n, seqs, q, out, sl2, plan, ws, s);
   return run_valu_d<64>(cv, layer, n, seqs, q, out, sl2, plan, ws, s);
 }

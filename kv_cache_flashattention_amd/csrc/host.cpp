@@ -399,12 +399,31 @@ int kvc_write(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs, int32
   return e == hipSuccess ? KVC_OK : hip_fail(e, "write launch");
 }
 
+namespace {
+// window >= 0 (0: full causal attention), sinks >= 0; the VALU (f32) kernels
+// have no window.
+int check_window(const kvc_cache* c, int32_t window, int32_t sinks) {
+  if (window < 0 || sinks < 0) return fail(KVC_E_INVAL, "window and sinks must be >= 0");
+  if (window > 0 && c->cfg.kv_dtype == KVC_F32)
+    return fail(KVC_E_UNSUPPORTED, "sliding windows need a bf16, f16 or fp8 cache");
+  return KVC_OK;
+}
+}  // namespace
+
 int kvc_attn_prefill(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs, int32_t T,
                      const void* q, const void* k, const void* v, void* out, float scale,
                      hipStream_t stream) {
+  return kvc_attn_prefill_window(c, layer, n, seqs, T, q, k, v, out, scale, 0, 0, stream);
+}
+
+int kvc_attn_prefill_window(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs,
+                            int32_t T, const void* q, const void* k, const void* v, void* out,
+                            float scale, int32_t window, int32_t sinks, hipStream_t stream) {
   if (!c) return fail(KVC_E_INVAL, "cache is NULL");
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(KVC_E_INVAL, "scale must be finite and positive");
+  int rw = check_window(c, window, sinks);
+  if (rw) return rw;
   int r = need_dev(c);
   if (r) return r;
   if (layer < 0 || layer >= c->cfg.n_layers) return fail(KVC_E_STATE, "layer out of range");
@@ -417,15 +436,22 @@ int kvc_attn_prefill(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs
     return fail(KVC_E_INVAL, "prompt longer than the table width");
   hipError_t e = hipSuccess;
   if (seqs) e = launch_write(c->view(), layer, n, seqs, 0, T, k, v, stream);
-  if (e == hipSuccess) e = launch_prefill(c->view(), n, T, q, k, v, out, scale, stream);
+  if (e == hipSuccess) e = launch_prefill(c->view(), n, T, q, k, v, out, scale, window, sinks, stream);
   return e == hipSuccess ? KVC_OK : hip_fail(e, "prefill launch");
 }
 
 int kvc_attn_extend(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs, int32_t T,
                     const void* q, void* out, float scale, hipStream_t stream) {
+  return kvc_attn_extend_window(c, layer, n, seqs, T, q, out, scale, 0, 0, stream);
+}
+
+int kvc_attn_extend_window(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs,
+                           int32_t T, const void* q, void* out, float scale, int32_t window,
+                           int32_t sinks, hipStream_t stream) {
   if (!c) return fail(KVC_E_INVAL, "cache is NULL");
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(KVC_E_INVAL, "scale must be finite and positive");
+  if (window < 0 || sinks < 0) return fail(KVC_E_INVAL, "window and sinks must be >= 0");
   if (c->cfg.kv_dtype != KVC_BF16 && c->cfg.kv_dtype != KVC_F16)
     return fail(KVC_E_UNSUPPORTED, "attn_extend needs a bf16 or f16 cache");
   int r = need_dev(c);
@@ -438,7 +464,8 @@ int kvc_attn_extend(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs,
   if (!seqs || !q || !out) return fail(KVC_E_INVAL, "NULL device pointer");
   if (!aligned16(q) || !aligned16(out)) return fail(KVC_E_INVAL, "q/out must be 16-byte aligned");
   bool handled = false;
-  hipError_t e = launch_extend(c->view(), layer, n, seqs, T, q, out, scale, stream, &handled);
+  hipError_t e = launch_extend(c->view(), layer, n, seqs, T, q, out, scale, window, sinks, stream,
+                               &handled);
   if (e == hipSuccess && !handled) return fail(KVC_E_UNSUPPORTED, "no extend kernel for this shape");
   return e == hipSuccess ? KVC_OK : hip_fail(e, "extend launch");
 }
@@ -454,9 +481,18 @@ int kvc_decode_workspace_bytes(const kvc_cache* c, int32_t n, int32_t num_splits
 int kvc_attn_decode(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs, const void* q,
                     void* out, float scale, int32_t num_splits, void* ws, uint64_t ws_bytes,
                     hipStream_t stream) {
+  return kvc_attn_decode_window(c, layer, n, seqs, q, out, scale, 0, 0, num_splits, ws, ws_bytes,
+                                stream);
+}
+
+int kvc_attn_decode_window(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs,
+                           const void* q, void* out, float scale, int32_t window, int32_t sinks,
+                           int32_t num_splits, void* ws, uint64_t ws_bytes, hipStream_t stream) {
   if (!c) return fail(KVC_E_INVAL, "cache is NULL");
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(KVC_E_INVAL, "scale must be finite and positive");
+  int rw = check_window(c, window, sinks);
+  if (rw) return rw;
   int r = need_dev(c);
   if (r) return r;
   if (layer < 0 || layer >= c->cfg.n_layers) return fail(KVC_E_STATE, "layer out of range");
@@ -471,7 +507,8 @@ int kvc_attn_decode(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs,
     return fail(KVC_E_WORKSPACE, "workspace too small: need " + std::to_string(p.ws_bytes) +
                                      " bytes");
   if (p.ws_bytes > 0 && !aligned16(ws)) return fail(KVC_E_INVAL, "workspace must be 16-byte aligned");
-  hipError_t e = launch_decode(c->view(), layer, n, seqs, q, out, scale, p, ws, stream);
+  hipError_t e = launch_decode(c->view(), layer, n, seqs, q, out, scale, p, ws, window, sinks,
+                               stream);
   return e == hipSuccess ? KVC_OK : hip_fail(e, "decode launch");
 }
 

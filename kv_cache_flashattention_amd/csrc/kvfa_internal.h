@@ -72,12 +72,16 @@ hipError_t launch_gather(const CacheView& cv, int layer, int seq, int start, int
                          void* k_out, void* v_out, hipStream_t s);
 hipError_t launch_decode(const CacheView& cv, int layer, int n, const int32_t* seqs,
                          const void* q, void* out, float scale, const DecodePlan& plan,
-                         void* ws, hipStream_t s);
+                         void* ws, int window, int sinks, hipStream_t s);
+// window > 0: key j visible to position p iff p - window < j <= p or
+// j < sinks; window = 0: full causal attention.
 hipError_t launch_prefill(const CacheView& cv, int n, int T, const void* q, const void* k,
-                          const void* v, void* out, float scale, hipStream_t s);
+                          const void* v, void* out, float scale, int window, int sinks,
+                          hipStream_t s);
 // T query rows per sequence against the paged cache (bf16 / f16 caches);
 // *handled = false when the cache type has no such kernel.
 hipError_t launch_extend(const CacheView& cv, int layer, int n, const int32_t* seqs, int T,
-                         const void* q, void* out, float scale, hipStream_t s, bool* handled);
+                         const void* q, void* out, float scale, int window, int sinks,
+                         hipStream_t s, bool* handled);
 
 }  // namespace kvfa

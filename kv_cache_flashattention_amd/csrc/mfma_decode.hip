@@ -125,6 +125,31 @@ struct WorkWs {
   int32_t* counts;
 };
 
+constexpr int kUnit = 32;   // tokens per work unit
+
+// Units of one segment that a query at position L-1 can see.  Without a
+// window: all ceil(L/32) units.  With a window w: the units holding sink
+// positions 0 .. sinks-1, then the units from the one holding position L-w
+// on; when the two ranges meet, all units.  unit(i) maps the segment's i-th
+// visible unit to its unit index in the sequence.
+struct UnitMap {
+  int count, ns, gap;
+  __device__ UnitMap(int L, int window, int sinks) {
+    const int nu = (L + kUnit - 1) / kUnit;
+    count = nu, ns = nu, gap = 0;
+    if (window > 0 && L > window) {
+      const int w0 = (L - window) / kUnit;
+      const int s1 = (min(sinks, L) + kUnit - 1) / kUnit;
+      if (w0 > s1) {
+        ns = s1;
+        gap = w0 - s1;
+        count = nu - gap;
+      }
+    }
+  }
+  __device__ int unit(int i) const { return i < ns ? i : i + gap; }
+};
+
 __host__ __device__ inline int64_t work_slots(int nb, int nkvg, int waves) {
   return (int64_t)nb * nkvg + waves;
 }
@@ -144,13 +169,12 @@ __device__ __forceinline__ int64_t share(int64_t a, int64_t W, int64_t P) {
   return a * (W / P) + (a * (W % P)) / P;
 }
 
-constexpr int kUnit = 32;   // tokens per work unit
 
 template <int KV, int D>
 __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
                                                         const int32_t* seqs, const uint16_t* q,
                                                         void* ws, int nb, int qgroups, int waves,
-                                                        float sl2) {
+                                                        float sl2, int window, int sinks) {
   typedef typename Op<KV>::T OpT;
   typedef Unit<KV, D> U;
   constexpr int KS = U::KS, DT = U::DT, KL = U::KL;
@@ -174,7 +198,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
       int c = 0;
       if (b < nb) {
         const int L = valid_len(cv, seqs[b]);
-        c = L > 0 ? (L + kUnit - 1) / kUnit : 0;
+        c = L > 0 ? UnitMap(L, window, sinks).count : 0;
         s_counts[b] = c;
       }
       loc[i] = (int64_t)c * nkvg;
@@ -239,6 +263,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
     const int kvh = kvg / qgroups, qg = kvg % qgroups;
     const int seq = seqs[b];
     const int L = valid_len(cv, seq);                  // > 0: the entry has units
+    const UnitMap umap(L, window, sinks);
 
     // Query operand (B of S^T = K Q^T): column r16 = query row qg*16 + r16.
     const int qi = qg * 16 + r16;
@@ -263,7 +288,8 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
 
     // Issue every load of unit c into buffer B (table entries past the
     // sequence's end are clamped to its last block; their tokens are masked).
-    auto issue = [&](U& B, int c) {
+    auto issue = [&](U& B, int cs) {
+      const int c = umap.unit(cs);
       int64_t sbase[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -299,9 +325,13 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
     };
 
     // Fold unit c (loaded in B) into (m, l, O).
-    auto compute = [&](const U& B, int c) {
+    auto compute = [&](const U& B, int cs) {
+      const int c = umap.unit(cs);
       const int nvalid = min(kUnit, L - c * kUnit);
       const bool tail = nvalid < kUnit;
+      // window: positions before L - window that are not sinks are hidden
+      const int wlo = window > 0 ? L - window : 0;
+      const bool wedge = c * kUnit < wlo && c * kUnit + kUnit > sinks;
       // ---- S^T = K Q^T, two 16-token tiles
       f32x4 sacc[2];
 #pragma unroll
@@ -336,6 +366,10 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
         for (int i = 0; i < 4; ++i) {
           float x = sacc[t][i] * (sl2 * ksc);
           if (tail && pos0 + 4 * t + i >= nvalid) x = -INFINITY;
+          if (wedge) {
+            const int pos = c * kUnit + pos0 + 4 * t + i;
+            if (pos < wlo && pos >= sinks) x = -INFINITY;
+          }
           p[t][i] = x;
           cmax = fmaxf(cmax, x);
         }
@@ -515,7 +549,8 @@ __global__ __launch_bounds__(256) void k_decode_work_merge(CacheView cv, const v
 
 template <int KV, int D>
 hipError_t run(const CacheView& cv, int layer, int n, const int32_t* seqs, const void* q,
-               void* out, float sl2, const DecodePlan& p, void* ws, hipStream_t st) {
+               void* out, float sl2, const DecodePlan& p, void* ws, int window, int sinks,
+               hipStream_t st) {
   const int G = cv.n_q / cv.n_kv;
   const int qgroups = (G + 15) / 16;
   const int grid = (p.waves + 3) / 4;
@@ -524,7 +559,7 @@ hipError_t run(const CacheView& cv, int layer, int n, const int32_t* seqs, const
     const uint16_t* qb = (const uint16_t*)q + (int64_t)b0 * cv.n_q * D;
     uint16_t* ob = (uint16_t*)out + (int64_t)b0 * cv.n_q * D;
     hipLaunchKernelGGL((k_decode_work<KV, D>), dim3(grid), dim3(256), 0, st, cv, layer,
-                       seqs + b0, qb, ws, nb, qgroups, p.waves, sl2);
+                       seqs + b0, qb, ws, nb, qgroups, p.waves, sl2, window, sinks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_decode_work_merge<KV == KV_F16, D>), dim3(cv.n_q, nb), dim3(256), 0, st,
@@ -573,17 +608,17 @@ int work_list_waves_per_cu(const CacheView& cv) {
 
 hipError_t launch_decode_mfma(const CacheView& cv, int layer, int n, const int32_t* seqs,
                               const void* q, void* out, float sl2, const DecodePlan& p, void* ws,
-                              hipStream_t st, bool* handled) {
+                              int window, int sinks, hipStream_t st, bool* handled) {
   *handled = p.work_list != 0;
   if (!*handled) return hipSuccess;
   if (cv.d == 128) {
-    if (cv.dtype == KVC_BF16) return run<KV_BF16, 128>(cv, layer, n, seqs, q, out, sl2, p, ws, st);
-    if (cv.dtype == KVC_F16) return run<KV_F16, 128>(cv, layer, n, seqs, q, out, sl2, p, ws, st);
-    return run<KV_FP8, 128>(cv, layer, n, seqs, q, out, sl2, p, ws, st);
+    if (cv.dtype == KVC_BF16) return run<KV_BF16, 128>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st);
+    if (cv.dtype == KVC_F16) return run<KV_F16, 128>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st);
+    return run<KV_FP8, 128>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st);
   }
-  if (cv.dtype == KVC_BF16) return run<KV_BF16, 64>(cv, layer, n, seqs, q, out, sl2, p, ws, st);
-  if (cv.dtype == KVC_F16) return run<KV_F16, 64>(cv, layer, n, seqs, q, out, sl2, p, ws, st);
-  return run<KV_FP8, 64>(cv, layer, n, seqs, q, out, sl2, p, ws, st);
+  if (cv.dtype == KVC_BF16) return run<KV_BF16, 64>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st);
+  if (cv.dtype == KVC_F16) return run<KV_F16, 64>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st);
+  return run<KV_FP8, 64>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st);
 }
 
 }  // namespace kvfa

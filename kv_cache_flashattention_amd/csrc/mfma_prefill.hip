@@ -153,7 +153,7 @@ __device__ __forceinline__ int row_key(int r) {
 // against the len(s) rows the paged cache holds for it (the new rows'
 // K/V included), query t at position len(s) - T + t; K/V tiles are staged
 // straight from the (block, kv head) slabs through the block table.
-template <int D, bool F16, bool PAGED>
+template <int D, bool F16, bool PAGED, bool WIN>
 __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int T,
                                                          const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ k,
@@ -161,7 +161,8 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
                                                          uint16_t* __restrict__ out, float sl2,
                                                          int ntiles, int n_seq, int n_units,
                                                          int xcd_split, CacheView cv, int layer,
-                                                         const int32_t* __restrict__ seqs) {
+                                                         const int32_t* __restrict__ seqs,
+                                                         int window, int sinks) {
   typedef typename Op<F16>::T OpT;
   constexpr int KS = D / 16;        // k-steps of QK^T
   constexpr int DT = D / 32;        // 32-row tiles of O^T
@@ -219,9 +220,32 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
   }
   const int qoff = L - T;
   const int kend = min(L, qoff + q0 + BM);             // keys any row of the workgroup sees
-  const int nkt = (kend + BN - 1) / BN;
-  // tiles this wave computes on: those holding a key <= its last row's position
-  const int wn = rq0 < T ? min(nkt, (qoff + rq0 + 31) / BN + 1) : 0;
+  const int nkc = (kend + BN - 1) / BN;                // key tiles up to the causal limit
+  // Tile list.  Without a window: tiles 0 .. nkc-1.  With a window w: the
+  // tiles holding sink keys, then the tiles from the one holding the
+  // workgroup's first windowed key (position qoff + q0 - w + 1) on.
+  int nst = 0, wt0 = 0;
+  if constexpr (WIN) {
+    nst = min((sinks + BN - 1) / BN, nkc);
+    wt0 = max(nst, max(0, qoff + q0 - window + 1) / BN);
+  }
+  const int nkt = nst + (nkc - wt0);                   // tiles in the list
+  auto tile_of = [&](int i) { return WIN ? (i < nst ? i : wt0 + (i - nst)) : i; };
+  // Does this wave need list entry i: a key of the tile visible to one of its
+  // rows (positions pw .. pw + 31)?  Without a window: the tiles up to the
+  // one holding its last row's position.
+  const int pw = qoff + rq0;
+  const int wn = rq0 < T ? min(nkt, (pw + 31) / BN + 1) : 0;
+  auto need = [&](int i) {
+    if constexpr (!WIN) {
+      return i < wn;
+    } else {
+      if (rq0 >= T || i >= nkt) return false;
+      const int k0 = BN * tile_of(i);
+      if (k0 > pw + 31) return false;                  // after every row
+      return k0 < sinks || k0 + BN - 1 > pw - window;
+    }
+  };
 
   // ---- query operand (B of S^T = K Q^T)
   OpT qop[KS];
@@ -246,7 +270,8 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
   const uint16_t* kpool = (const uint16_t*)cv.k + ((int64_t)layer * cv.n_blocks * n_kv + g) * kBlock * D;
   const uint16_t* vpool = (const uint16_t*)cv.v + ((int64_t)layer * cv.n_blocks * n_kv + g) * kBlock * D;
   const int32_t* btab = cv.bt + (int64_t)seq * cv.max_bps;
-  auto load_k = [&](int i) {
+  auto load_k = [&](int li) {
+    const int i = tile_of(li);
     const int lim = L - 1 - BN * i;                    // last valid row of the tile
     const int t = opaque_tid() & 255;
     if constexpr (PAGED) {
@@ -277,7 +302,8 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
   // c / 8, block (c / 2) % 4 of the tile, half c % 2) is a plain 16-byte
   // copy; keys at or past L (stale slots of the last block, blocks past the
   // end) are zeroed, since 0 * NaN would poison the PV product.
-  auto load_v = [&](int i) {
+  auto load_v = [&](int li) {
+    const int i = tile_of(li);
     const int t = opaque_tid() & 255;
     if constexpr (PAGED) {
 #pragma unroll
@@ -298,7 +324,8 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
       }
     }
   };
-  auto store_v = [&](int buf, int i) {
+  auto store_v = [&](int buf, int li) {
+    const int i = tile_of(li);
     const int t = opaque_tid() & 255;
     if constexpr (PAGED) {
 #pragma unroll
@@ -358,17 +385,25 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
   };
   // online softmax of tile i, first half: mask, row max, rescale of O and l
   auto rowmax = [&](int i) {
-    const int k0 = BN * i;
-    if (k0 + BN - 1 > qoff + rq0) {                    // tile reaches past the wave's first row
+    const int k0 = BN * tile_of(i);
+    // the tile reaches past the wave's first row, or (window) holds a
+    // non-sink key at or before the last row's window start
+    const bool diag = k0 + BN - 1 > pw;
+    const bool wedge = WIN && k0 <= pw + 31 - window && k0 + BN > sinks;
+    if (diag || wedge) {
       // element e of sacc[st] holds key k0 + 32 st + 8 half + kofs(e)
       const int t = opaque_tid();
-      const int thr = qoff + rq0 + (t & 31) - k0 - 8 * ((t >> 5) & 1);
+      const int rel = pw + (t & 31) - k0 - 8 * ((t >> 5) & 1);   // query position - key base
+      const int kbase = k0 + 8 * ((t >> 5) & 1);
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int jj = e >> 2, kofs = (jj < 2 ? 4 * jj : 16 + 4 * (jj - 2)) + (e & 3);
-          if (32 * st + kofs > thr) sacc[st][e] = -INFINITY;
+          const int jj = e >> 2, kofs = 32 * st + (jj < 2 ? 4 * jj : 16 + 4 * (jj - 2)) + (e & 3);
+          bool hide = kofs > rel;                                  // key after the query
+          if (WIN)                                                // outside window, not a sink
+            hide = hide || (kofs <= rel - window && kbase + kofs >= sinks);
+          if (hide) sacc[st][e] = -INFINITY;
         }
     }
     float rmax = -INFINITY;
@@ -454,8 +489,8 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
   for (int i = 0; i <= nkt; ++i) {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(2);
-    if (i >= 1 && i - 1 < wn) pv(i - 1);             // P_{i-1} dies before S_i is born
-    if (i < wn) {
+    if (i >= 1 && need(i - 1)) pv(i - 1);            // P_{i-1} dies before S_i is born
+    if (need(i)) {
       qk(i);
       rowmax(i);
     }
@@ -473,14 +508,14 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
       store_v(i & 1, i);
       if (i + 1 < nkt) load_v(i + 1);
     }
-    if (i < wn) expo(i);
+    if (need(i)) expo(i);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   }
   if (grp == 0) __syncthreads();                     // same barrier count for both groups
 
   // ---- epilogue: O / l for this lane's query column
-  if (wn == 0 || qrow >= T) return;
+  if (rq0 >= T || qrow >= T) return;
   const float l = lsum + half_swap(lsum);
   const float inv = 1.f / l;
   uint16_t* orow = out + ((int64_t)b * T + qrow) * qstride + (int64_t)head * D;
@@ -504,30 +539,37 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
 
 template <int D, bool F16, bool PAGED>
 hipError_t run(const CacheView& cv, int layer, int n, const int32_t* seqs, int T, const void* q,
-               const void* k, const void* v, void* out, float sl2, hipStream_t s) {
+               const void* k, const void* v, void* out, float sl2, int window, int sinks,
+               hipStream_t s) {
   const int ntiles = (T + BM - 1) / BM;
   const int64_t units = (int64_t)cv.n_q * n * ntiles;
   if (units > INT32_MAX) return hipErrorInvalidValue;
   const int xcd_split = units % 8 == 0 ? 1 : 0;
-  hipLaunchKernelGGL((k_prefill_mfma<D, F16, PAGED>), dim3((uint32_t)units), dim3(512), 0, s,
-                     cv.n_q, cv.n_kv, T, (const uint16_t*)q, (const uint16_t*)k,
-                     (const uint16_t*)v, (uint16_t*)out, sl2, ntiles, n, (int)units, xcd_split,
-                     cv, layer, seqs);
+  if (window > 0)
+    hipLaunchKernelGGL((k_prefill_mfma<D, F16, PAGED, true>), dim3((uint32_t)units), dim3(512), 0,
+                       s, cv.n_q, cv.n_kv, T, (const uint16_t*)q, (const uint16_t*)k,
+                       (const uint16_t*)v, (uint16_t*)out, sl2, ntiles, n, (int)units, xcd_split,
+                       cv, layer, seqs, window, sinks);
+  else
+    hipLaunchKernelGGL((k_prefill_mfma<D, F16, PAGED, false>), dim3((uint32_t)units), dim3(512),
+                       0, s, cv.n_q, cv.n_kv, T, (const uint16_t*)q, (const uint16_t*)k,
+                       (const uint16_t*)v, (uint16_t*)out, sl2, ntiles, n, (int)units, xcd_split,
+                       cv, layer, seqs, 0, 0);
   return hipGetLastError();
 }
 
 template <bool PAGED>
 hipError_t dispatch(const CacheView& cv, int layer, int n, const int32_t* seqs, int T,
                     const void* q, const void* k, const void* v, void* out, float sl2,
-                    hipStream_t s, bool* handled) {
+                    int window, int sinks, hipStream_t s, bool* handled) {
   *handled = true;
   const int io = io_dtype(cv.dtype);
   if (io == KVC_BF16 && (!PAGED || cv.dtype == KVC_BF16)) {
-    if (cv.d == 128) return run<128, false, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, s);
-    if (cv.d == 64) return run<64, false, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, s);
+    if (cv.d == 128) return run<128, false, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);
+    if (cv.d == 64) return run<64, false, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);
   } else if (io == KVC_F16) {
-    if (cv.d == 128) return run<128, true, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, s);
-    if (cv.d == 64) return run<64, true, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, s);
+    if (cv.d == 128) return run<128, true, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);
+    if (cv.d == 64) return run<64, true, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);
   }
   *handled = false;
   return hipSuccess;
@@ -536,15 +578,16 @@ hipError_t dispatch(const CacheView& cv, int layer, int n, const int32_t* seqs, 
 }  // namespace
 
 hipError_t launch_prefill_mfma(const CacheView& cv, int n, int T, const void* q, const void* k,
-                               const void* v, void* out, float sl2, hipStream_t s,
-                               bool* handled) {
-  return dispatch<false>(cv, 0, n, nullptr, T, q, k, v, out, sl2, s, handled);
+                               const void* v, void* out, float sl2, int window, int sinks,
+                               hipStream_t s, bool* handled) {
+  return dispatch<false>(cv, 0, n, nullptr, T, q, k, v, out, sl2, window, sinks, s, handled);
 }
 
 hipError_t launch_extend_mfma(const CacheView& cv, int layer, int n, const int32_t* seqs, int T,
-                              const void* q, void* out, float sl2, hipStream_t s,
-                              bool* handled) {
-  return dispatch<true>(cv, layer, n, seqs, T, q, nullptr, nullptr, out, sl2, s, handled);
+                              const void* q, void* out, float sl2, int window, int sinks,
+                              hipStream_t s, bool* handled) {
+  return dispatch<true>(cv, layer, n, seqs, T, q, nullptr, nullptr, out, sl2, window, sinks, s,
+                        handled);
 }
 
 }  // namespace kvfa

@@ -14,11 +14,11 @@
 namespace kvfa {
 
 hipError_t launch_prefill_mfma(const CacheView& cv, int n, int T, const void* q, const void* k,
-                               const void* v, void* out, float scale_log2, hipStream_t s,
-                               bool* handled);
+                               const void* v, void* out, float scale_log2, int window, int sinks,
+                               hipStream_t s, bool* handled);
 hipError_t launch_extend_mfma(const CacheView& cv, int layer, int n, const int32_t* seqs, int T,
-                              const void* q, void* out, float scale_log2, hipStream_t s,
-                              bool* handled);
+                              const void* q, void* out, float scale_log2, int window, int sinks,
+                              hipStream_t s, bool* handled);
 
 namespace {
 
@@ -112,11 +112,13 @@ hipError_t run_valu(const CacheView& cv, int n, int T, const void* q, const void
 }  // namespace
 
 hipError_t launch_prefill(const CacheView& cv, int n, int T, const void* q, const void* k,
-                          const void* v, void* out, float scale, hipStream_t s) {
+                          const void* v, void* out, float scale, int window, int sinks,
+                          hipStream_t s) {
   const float sl2 = scale * kLog2e;
   bool handled = false;
-  hipError_t e = launch_prefill_mfma(cv, n, T, q, k, v, out, sl2, s, &handled);
+  hipError_t e = launch_prefill_mfma(cv, n, T, q, k, v, out, sl2, window, sinks, s, &handled);
   if (handled) return e;
+  if (window > 0) return hipErrorInvalidValue;          // the VALU kernel has no window
   switch (io_dtype(cv.dtype)) {
     case KVC_F32: return run_valu<float>(cv, n, T, q, k, v, out, sl2, s);
     case KVC_F16: return run_valu<_Float16>(cv, n, T, q, k, v, out, sl2, s);
@@ -125,8 +127,10 @@ hipError_t launch_prefill(const CacheView& cv, int n, int T, const void* q, cons
 }
 
 hipError_t launch_extend(const CacheView& cv, int layer, int n, const int32_t* seqs, int T,
-                         const void* q, void* out, float scale, hipStream_t s, bool* handled) {
-  return launch_extend_mfma(cv, layer, n, seqs, T, q, out, scale * kLog2e, s, handled);
+                         const void* q, void* out, float scale, int window, int sinks,
+                         hipStream_t s, bool* handled) {
+  return launch_extend_mfma(cv, layer, n, seqs, T, q, out, scale * kLog2e, window, sinks, s,
+                            handled);
 }
 
 }  // namespace kvfa

@@ -227,3 +227,23 @@ def test_extend_refuses_cache_types_without_a_kernel(dtype):
     p = ctypes.c_void_p(16)
     rc = kv.lib().kvc_attn_extend(c._h, 0, 1, p, 4, p, p, ctypes.c_float(0.1), None)
     assert rc == kv.KVC_E_UNSUPPORTED
+
+
+def test_window_arguments_are_checked():
+    p = ctypes.c_void_p(16)
+    L = kv.lib()
+    c = kv.KvCache(1, 8, 2, 128, 16, 2, 4, "bf16", device=None)
+    rc = L.kvc_attn_decode_window(c._h, 0, 1, p, p, p, ctypes.c_float(0.1), -1, 0, 0, None, 0,
+                                  None)
+    assert rc == kv.KVC_E_INVAL
+    rc = L.kvc_attn_prefill_window(c._h, 0, 1, None, 4, p, p, p, p, ctypes.c_float(0.1), 8, -2,
+                                   None)
+    assert rc == kv.KVC_E_INVAL
+    rc = L.kvc_attn_extend_window(c._h, 0, 1, p, 4, p, p, ctypes.c_float(0.1), -3, 0, None)
+    assert rc == kv.KVC_E_INVAL
+    f = kv.KvCache(1, 8, 2, 128, 16, 2, 4, "f32", device=None)
+    rc = L.kvc_attn_decode_window(f._h, 0, 1, p, p, p, ctypes.c_float(0.1), 8, 0, 0, None, 0, None)
+    assert rc == kv.KVC_E_UNSUPPORTED
+    rc = L.kvc_attn_prefill_window(f._h, 0, 1, None, 4, p, p, p, p, ctypes.c_float(0.1), 8, 0,
+                                   None)
+    assert rc == kv.KVC_E_UNSUPPORTED
