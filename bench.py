@@ -465,6 +465,37 @@ def cpu_extend(w, ctx, q, k, v, budget_s=12.0):
                       f"(sequence, head) pairs ({spent:.1f} s)"}
 
 
+# ---------------------------------------------------------------- prefix sharing
+def bench_prefix_share(torch, kv, n_seq=40, prompt=600, n_layers=32):
+    """Forty conversations sharing one 600-token system prompt (Llama-8B
+    cache shape: 32 layers, 8 kv heads of 128, bf16).  Sharing holds the
+    prompt's 38 blocks once; the first grow of every sequence copies the
+    shared, partly filled last block (copy-on-write).  Reports the blocks
+    held and the copy kernel's rate (bytes copied / GPU time of the grow)."""
+    n_kv, d = 8, 128
+    nb_prompt = -(-prompt // 16)
+    c = kv.KvCache(n_layers, 32, n_kv, d, nb_prompt + 2 * n_seq + 8, n_seq + 1, nb_prompt + 4,
+                   "bf16")
+    c.seq_alloc(0, prompt)
+    for s in range(1, n_seq + 1):
+        c.seq_share_prefix(0, s, prompt)
+    held = c.cfg.n_blocks - c.free_blocks()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    c.seq_grow(list(range(1, n_seq + 1)))
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3
+    copied = n_seq * n_layers * 2 * n_kv * 16 * d * 2          # K and V of each copied block
+    return {"workload": f"{n_seq} sequences sharing a {prompt}-token prompt, Llama-8B cache shape "
+                        f"({n_layers} layers, {n_kv} kv heads of {d}, bf16)",
+            "blocks_held_shared": held, "blocks_held_unshared": (n_seq + 1) * nb_prompt,
+            "first_grow_us": us, "copy_on_write_bytes": copied,
+            "copy_on_write_GBps": copied / (us * 1e-6) / 1e9}
+
+
 DECODE_WORKLOADS = {
     "llama8b_decode": "40 sequences, 32 q / 8 kv heads, d 128, bf16 cache, 16-token blocks, "
                       "shuffled tables, lengths uniform in [512, 4096]; grow + kv_append + decode",
@@ -550,6 +581,7 @@ def main():
         line["prefill"] = bench_prefill(max(3, args.steps // 4), 1, torch, kv, with_cpu)
         line["extend"] = bench_extend(max(5, args.steps // 2), 2, torch, kv, with_cpu)
         line["decode_window"] = bench_decode_window(max(5, args.steps // 2), torch, kv)
+        line["prefix_share"] = bench_prefix_share(torch, kv)
     print(json.dumps(line))
 
 

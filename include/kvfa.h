@@ -150,6 +150,25 @@ int kvc_seq_grow_by(kvc_cache* cache, int32_t seq, int32_t n_tokens, hipStream_t
  * release), and mark it not live (device length 0, table entries -1). */
 int kvc_seq_release(kvc_cache* cache, int32_t seq, hipStream_t stream);
 
+/* Prefix sharing (kvcache-7e2 PagedAttention `share_prefix`; kvcache-7e2 and
+ * abhishekpatel.co: sequences with a common beginning point at the same
+ * physical blocks, copying only when one of them would change a block).
+ * `dst` (not live) becomes live holding the first prefix_len rows of `src`
+ * (live, 0 <= prefix_len <= len(src)) by sharing its first
+ * ceil(prefix_len/16) blocks; no data moves.  Every block counts the
+ * sequences holding it: kvc_seq_release returns a block to the free list
+ * only when the last holder releases it.  Copy-on-write: when a grow would
+ * put new rows into a partly filled last block that another sequence also
+ * holds, the growing sequence first gets its own copy of that block (one
+ * free block, all layers, K, V and fp8 scales, copied on the stream before
+ * the grow's table update).  Rows below a sequence's length at its last
+ * grow must not be rewritten while their block is shared. */
+int kvc_seq_share_prefix(kvc_cache* cache, int32_t src, int32_t dst, int32_t prefix_len,
+                         hipStream_t stream);
+
+/* Number of sequences holding `block` (0 = free). */
+int kvc_block_refs(const kvc_cache* cache, int32_t block, int32_t* out);
+
 /* Make `seq` live with an explicit block list (each block must be free) and
  * length `len` (nblk must equal ceil(len/16)).  For tests and callers that
  * manage placement themselves. */

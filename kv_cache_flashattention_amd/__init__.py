@@ -64,6 +64,8 @@ _SIGS = {
     "kvc_seq_alloc": [_P, _I, _I, _P],
     "kvc_seq_grow": [_P, _I, ctypes.POINTER(_I), _P],
     "kvc_seq_grow_by": [_P, _I, _I, _P],
+    "kvc_seq_share_prefix": [_P, _I, _I, _I, _P],
+    "kvc_block_refs": [_P, _I, ctypes.POINTER(_I)],
     "kvc_seq_release": [_P, _I, _P],
     "kvc_set_block_table": [_P, _I, ctypes.POINTER(_I), _I, _I, _P],
     "kvc_seq_len": [_P, _I, ctypes.POINTER(_I)],
@@ -196,6 +198,14 @@ class KvCache:
 
     def seq_release(self, seq):
         _check(lib().kvc_seq_release(self._h, seq, self._s()))
+
+    def seq_share_prefix(self, src, dst, prefix_len):
+        _check(lib().kvc_seq_share_prefix(self._h, src, dst, prefix_len, self._s()))
+
+    def block_refs(self, block):
+        out = _I()
+        _check(lib().kvc_block_refs(self._h, block, ctypes.byref(out)))
+        return out.value
 
     def seq_grow_by(self, seq, n_tokens):
         _check(lib().kvc_seq_grow_by(self._h, seq, n_tokens, self._s()))

@@ -71,6 +71,35 @@ __global__ void k_table_update(CacheView cv, TableUpdate u) {
   }
 }
 
+// ---------------------------------------------------------------- block copy
+// Copy-on-write of a shared block: workgroup (pair p, layer l) copies the
+// K and V data of block src[p] to block dst[p] in layer l (all kv heads,
+// contiguous in both pools) and, for fp8, their per-head scales.  Block ids
+// come from the host manager, which only hands out ids below n_blocks.
+__global__ __launch_bounds__(256) void k_copy_blocks(CacheView cv, BlockCopy u) {
+  const int p = blockIdx.x, layer = blockIdx.y;
+  if (p >= u.n) return;
+  const int64_t src = u.src[p], dst = u.dst[p];
+  if (src < 0 || src >= cv.n_blocks || dst < 0 || dst >= cv.n_blocks) return;
+  const int64_t bytes = (int64_t)cv.n_kv * kBlock * cv.d * elem_bytes(cv.dtype);
+  const int64_t so = ((int64_t)layer * cv.n_blocks + src) * bytes;
+  const int64_t dof = ((int64_t)layer * cv.n_blocks + dst) * bytes;
+  const uint4* ks = (const uint4*)((const uint8_t*)cv.k + so);
+  const uint4* vs = (const uint4*)((const uint8_t*)cv.v + so);
+  uint4* kd = (uint4*)((uint8_t*)cv.k + dof);
+  uint4* vd = (uint4*)((uint8_t*)cv.v + dof);
+  for (int64_t i = threadIdx.x; i < bytes / 16; i += blockDim.x) {
+    kd[i] = ks[i];
+    vd[i] = vs[i];
+  }
+  if (cv.dtype == KVC_FP8_E4M3FN && threadIdx.x < cv.n_kv) {
+    const int64_t s0 = ((int64_t)layer * cv.n_blocks + src) * cv.n_kv + threadIdx.x;
+    const int64_t d0 = ((int64_t)layer * cv.n_blocks + dst) * cv.n_kv + threadIdx.x;
+    cv.ks[d0] = cv.ks[s0];
+    cv.vs[d0] = cv.vs[s0];
+  }
+}
+
 // ---------------------------------------------------------------- append
 // One wave per (sequence, kv head): the new row goes to slot (L-1) % 16 of
 // block table[(L-1) / 16].  16/32-bit storage copies the bits.
@@ -281,6 +310,12 @@ hipError_t launch_fill_tables(const CacheView& cv, hipStream_t s) {
 
 hipError_t launch_table_update(const CacheView& cv, const TableUpdate& u, hipStream_t s) {
   hipLaunchKernelGGL(k_table_update, dim3(1), dim3(256), 0, s, cv, u);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(const CacheView& cv, const BlockCopy& u, hipStream_t s) {
+  if (u.n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_copy_blocks, dim3(u.n, cv.n_layers), dim3(256), 0, s, cv, u);
   return hipGetLastError();
 }
 

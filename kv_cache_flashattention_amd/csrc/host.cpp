@@ -6,7 +6,14 @@
 // one block table per sequence and its length ("KV Cache & Flash Attention."
 // (kvcache-7e2), PagedAttention section: fixed 16-token blocks, a per-sequence
 // table, a new block only when the last one is full, release returns every
-// block).  Every change is mirrored to the caller's device tables by a small
+// block).  Sequences may share the blocks of a common prefix
+// (kvcache-7e2 PagedAttention `share_prefix`); each block counts the
+// sequences holding it, and a release returns only the blocks nobody holds
+// any more.  A shared block is copied before a sequence writes into it
+// (abhishekpatel.co: blocks are shared "copying only if one of them would
+// change a block"): a grow whose new rows land in a shared, partly filled
+// last block first gives the growing sequence its own copy.  Every change
+// is mirrored to the caller's device tables by a small
 // kernel whose arguments carry the changed entries, enqueued on the caller's
 // stream, so attention kernels later on that stream see it.
 #include <algorithm>
@@ -28,7 +35,7 @@ struct kvc_cache {
   std::vector<std::vector<int32_t>> table;      // per sequence
   std::vector<int32_t> len;                     // per sequence
   std::vector<uint8_t> live;                    // per sequence
-  std::vector<uint8_t> owned;                   // per block: 1 if some sequence holds it
+  std::vector<int32_t> refs;                    // per block: sequences holding it (0 = free)
   int32_t cu_count = 256;                       // compute units of the device (decode plan)
   CacheView view() const {
     CacheView v{};
@@ -114,6 +121,60 @@ struct Uploader {
   }
 };
 
+// Collects copy-on-write block copies and launches them (before the table
+// updates of the same call) in batches of at most kCopyMax pairs.
+struct Copier {
+  kvc_cache* c;
+  hipStream_t s;
+  BlockCopy u{};
+  hipError_t err = hipSuccess;
+  Copier(kvc_cache* c_, hipStream_t s_) : c(c_), s(s_) {}
+  void put(int32_t src, int32_t dst) {
+    if (!c->has_dev) return;
+    u.src[u.n] = src;
+    u.dst[u.n] = dst;
+    if (++u.n == kCopyMax) flush();
+  }
+  void flush() {
+    if (u.n == 0) return;
+    hipError_t e = launch_copy_blocks(c->view(), u, s);
+    if (e != hipSuccess && err == hipSuccess) err = e;
+    u.n = 0;
+  }
+  int finish() {
+    flush();
+    return err == hipSuccess ? KVC_OK : hip_fail(err, "block copy launch");
+  }
+};
+
+int32_t take_block(kvc_cache* c) {
+  int32_t b = c->free_list.back();
+  c->free_list.pop_back();
+  c->refs[b] = 1;
+  return b;
+}
+
+// Before new rows are written at position len of `seq`: if they land in a
+// partly filled last block that another sequence also holds, give `seq` its
+// own copy of that block.  Returns whether a copy was made.
+bool unshare_last(kvc_cache* c, int32_t seq, Copier& cp, Uploader& up) {
+  const int32_t len = c->len[seq];
+  if (len % kBlock == 0) return false;                 // the next row starts a new block
+  auto& t = c->table[seq];
+  const int32_t old = t.back();
+  if (c->refs[old] <= 1) return false;
+  const int32_t nb = take_block(c);
+  cp.put(old, nb);
+  c->refs[old] -= 1;
+  t.back() = nb;
+  up.bt(seq, (int32_t)t.size() - 1, nb);
+  return true;
+}
+
+bool needs_copy(const kvc_cache* c, int32_t seq) {
+  return c->len[seq] % kBlock != 0 && c->refs[c->table[seq].back()] > 1;
+}
+
 int check_seq(const kvc_cache* c, int32_t seq) {
   if (seq < 0 || seq >= c->cfg.max_seqs) return fail(KVC_E_INVAL, "sequence id out of range");
   return KVC_OK;
@@ -178,7 +239,7 @@ int kvc_create(const kvc_config* cfg, const kvc_buffers* dev, hipStream_t stream
   c->table.resize(cfg->max_seqs);
   c->len.assign(cfg->max_seqs, 0);
   c->live.assign(cfg->max_seqs, 0);
-  c->owned.assign(cfg->n_blocks, 0);
+  c->refs.assign(cfg->n_blocks, 0);
   if (dev) {
     c->has_dev = true;
     c->dev = *dev;
@@ -215,9 +276,7 @@ int kvc_seq_alloc(kvc_cache* c, int32_t seq, int32_t n_tokens, hipStream_t strea
   auto& t = c->table[seq];
   t.clear();
   for (int64_t i = 0; i < nb; ++i) {
-    int32_t b = c->free_list.back();
-    c->free_list.pop_back();
-    c->owned[b] = 1;
+    int32_t b = take_block(c);
     t.push_back(b);
     up.bt(seq, (int32_t)i, b);
   }
@@ -241,23 +300,26 @@ int kvc_seq_grow(kvc_cache* c, int32_t n, const int32_t* seqs, hipStream_t strea
     seen[s] = 1;
     if ((int64_t)c->len[s] + 1 > (int64_t)c->cfg.max_blocks_per_seq * kBlock)
       return fail(KVC_E_INVAL, "sequence would exceed its table width");
-    if (c->len[s] % kBlock == 0) ++need;
+    if (c->len[s] % kBlock == 0 || needs_copy(c, s)) ++need;
   }
   if (need > (int64_t)c->free_list.size()) return fail(KVC_E_NO_BLOCKS, "free list exhausted");
+  Copier cp(c, stream);
   Uploader up(c, stream);
   for (int32_t i = 0; i < n; ++i) {
     int32_t s = seqs[i];
     if (c->len[s] % kBlock == 0) {
-      int32_t b = c->free_list.back();
-      c->free_list.pop_back();
-      c->owned[b] = 1;
+      int32_t b = take_block(c);
       up.bt(s, (int32_t)c->table[s].size(), b);
       c->table[s].push_back(b);
+    } else {
+      unshare_last(c, s, cp, up);
     }
     c->len[s] += 1;
     up.len(s, c->len[s]);
   }
-  return up.finish();
+  int rc = cp.finish();
+  int ru = up.finish();
+  return rc ? rc : ru;
 }
 
 int kvc_seq_grow_by(kvc_cache* c, int32_t seq, int32_t n_tokens, hipStream_t stream) {
@@ -271,19 +333,23 @@ int kvc_seq_grow_by(kvc_cache* c, int32_t seq, int32_t n_tokens, hipStream_t str
     return fail(KVC_E_INVAL, "sequence would exceed its table width");
   // one block per token that starts a block: the blocks n single-token
   // grows would take, in the same (last-freed-first) order
-  const int64_t need = (to + kBlock - 1) / kBlock - (len + kBlock - 1) / kBlock;
-  if (need > (int64_t)c->free_list.size()) return fail(KVC_E_NO_BLOCKS, "free list exhausted");
+  const int64_t fresh = (to + kBlock - 1) / kBlock - (len + kBlock - 1) / kBlock;
+  const bool copy = n_tokens > 0 && needs_copy(c, seq);
+  if (fresh + (copy ? 1 : 0) > (int64_t)c->free_list.size())
+    return fail(KVC_E_NO_BLOCKS, "free list exhausted");
+  Copier cp(c, stream);
   Uploader up(c, stream);
-  for (int64_t i = 0; i < need; ++i) {
-    int32_t b = c->free_list.back();
-    c->free_list.pop_back();
-    c->owned[b] = 1;
+  if (copy) unshare_last(c, seq, cp, up);
+  for (int64_t i = 0; i < fresh; ++i) {
+    int32_t b = take_block(c);
     up.bt(seq, (int32_t)c->table[seq].size(), b);
     c->table[seq].push_back(b);
   }
   c->len[seq] = (int32_t)to;
   up.len(seq, c->len[seq]);
-  return up.finish();
+  int rc = cp.finish();
+  int ru = up.finish();
+  return rc ? rc : ru;
 }
 
 int kvc_seq_release(kvc_cache* c, int32_t seq, hipStream_t stream) {
@@ -294,8 +360,7 @@ int kvc_seq_release(kvc_cache* c, int32_t seq, hipStream_t stream) {
   Uploader up(c, stream);
   auto& t = c->table[seq];
   for (size_t i = 0; i < t.size(); ++i) {
-    c->free_list.push_back(t[i]);
-    c->owned[t[i]] = 0;
+    if (--c->refs[t[i]] == 0) c->free_list.push_back(t[i]);
     up.bt(seq, (int32_t)i, -1);
   }
   t.clear();
@@ -318,7 +383,7 @@ int kvc_set_block_table(kvc_cache* c, int32_t seq, const int32_t* blocks, int32_
   for (int32_t i = 0; i < nblk; ++i) {
     int32_t b = blocks[i];
     if (b < 0 || b >= c->cfg.n_blocks) return fail(KVC_E_INVAL, "block id out of range");
-    if (c->owned[b] || seen[b]) return fail(KVC_E_STATE, "block is not free");
+    if (c->refs[b] || seen[b]) return fail(KVC_E_STATE, "block is not free");
     seen[b] = 1;
   }
   // Remove the chosen blocks from the free list, keeping the order of the rest.
@@ -331,13 +396,44 @@ int kvc_set_block_table(kvc_cache* c, int32_t seq, const int32_t* blocks, int32_
   auto& t = c->table[seq];
   t.assign(blocks, blocks + nblk);
   for (int32_t i = 0; i < nblk; ++i) {
-    c->owned[blocks[i]] = 1;
+    c->refs[blocks[i]] = 1;
     up.bt(seq, i, blocks[i]);
   }
   c->len[seq] = len;
   c->live[seq] = 1;
   up.len(seq, len);
   return up.finish();
+}
+
+int kvc_seq_share_prefix(kvc_cache* c, int32_t src, int32_t dst, int32_t prefix_len,
+                         hipStream_t stream) {
+  if (!c) return fail(KVC_E_INVAL, "cache is NULL");
+  int r = check_seq(c, src);
+  if (!r) r = check_seq(c, dst);
+  if (r) return r;
+  if (!c->live[src]) return fail(KVC_E_STATE, "source sequence is not live");
+  if (c->live[dst] || src == dst) return fail(KVC_E_STATE, "destination sequence is already live");
+  if (prefix_len < 0 || prefix_len > c->len[src])
+    return fail(KVC_E_INVAL, "prefix_len must lie in 0 .. len(src)");
+  const int32_t n = (prefix_len + kBlock - 1) / kBlock;
+  Uploader up(c, stream);
+  auto& t = c->table[dst];
+  t.assign(c->table[src].begin(), c->table[src].begin() + n);
+  for (int32_t i = 0; i < n; ++i) {
+    c->refs[t[i]] += 1;
+    up.bt(dst, i, t[i]);
+  }
+  c->len[dst] = prefix_len;
+  c->live[dst] = 1;
+  up.len(dst, prefix_len);
+  return up.finish();
+}
+
+int kvc_block_refs(const kvc_cache* c, int32_t block, int32_t* out) {
+  if (!c || !out) return fail(KVC_E_INVAL, "NULL argument");
+  if (block < 0 || block >= c->cfg.n_blocks) return fail(KVC_E_INVAL, "block id out of range");
+  *out = c->refs[block];
+  return KVC_OK;
 }
 
 int kvc_seq_len(const kvc_cache* c, int32_t seq, int32_t* out) {

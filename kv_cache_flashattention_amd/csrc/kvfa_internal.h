@@ -32,6 +32,15 @@ struct TableUpdate {
   int32_t val[kTableUpdateMax];
 };
 
+// Copy-on-write block copies: block src -> dst, every layer, K and V slabs of
+// all kv heads and (fp8) their scales.
+constexpr int kCopyMax = 120;
+struct BlockCopy {
+  int32_t n;
+  int32_t src[kCopyMax];
+  int32_t dst[kCopyMax];
+};
+
 // How one decode call divides its work.
 //  * Matrix-core path (16-bit and fp8 caches): a work list.  The batch's
 //    32-token units, over every (sequence, kv-head group), are cut into
@@ -51,7 +60,7 @@ struct DecodePlan {
   uint64_t ws_bytes;  // workspace bytes the call needs
 };
 
-inline int elem_bytes(int dtype) {
+__host__ __device__ inline int elem_bytes(int dtype) {
   return dtype == KVC_F32 ? 4 : dtype == KVC_FP8_E4M3FN ? 1 : 2;
 }
 inline int io_dtype(int dtype) { return dtype == KVC_FP8_E4M3FN ? KVC_BF16 : dtype; }
@@ -64,6 +73,7 @@ int work_list_waves_per_cu(const CacheView& cv);
 // Launchers: return hipSuccess or the launch error.
 hipError_t launch_fill_tables(const CacheView& cv, hipStream_t s);
 hipError_t launch_table_update(const CacheView& cv, const TableUpdate& u, hipStream_t s);
+hipError_t launch_copy_blocks(const CacheView& cv, const BlockCopy& u, hipStream_t s);
 hipError_t launch_append(const CacheView& cv, int layer, int n, const int32_t* seqs,
                          const void* k, const void* v, hipStream_t s);
 hipError_t launch_write(const CacheView& cv, int layer, int n, const int32_t* seqs, int start,

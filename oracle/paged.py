@@ -11,6 +11,16 @@ tables") describes the same block table.  The free list is the page's plain
 Python list: initially 0 .. n_blocks-1, ``pop()`` takes from the end and a
 release appends the sequence's blocks in table order.
 
+Prefix sharing follows [KVFA] ``share_prefix`` (a second sequence's table
+starts with the first ceil(prefix_len/16) blocks of the first) with the rule
+[KVFA] and [KPF] state in prose: sequences with a common beginning point at
+the same blocks and a block is copied only when one of them would change it.
+Each block counts the sequences holding it; a release frees only blocks no
+one holds any more (appended in table order); a grow whose new row lands in a
+partly filled last block held by another sequence first moves the growing
+sequence to a fresh copy of that block (taken from the free list like any
+other block, all layers copied).
+
 Physical layout of one layer's pools (the library's documented layout):
   K[block][kv_head][slot 0..15][d]      (a token's d values contiguous)
   V[block][kv_head][d][slot 0..15]      (a d-column's 16 tokens contiguous)
@@ -44,36 +54,71 @@ class PagedCacheModel:
             self.Ks = np.full((n_layers, n_blocks, n_kv), nanbits, dtype=np.uint32).view(np.float32)
             self.Vs = np.full((n_layers, n_blocks, n_kv), nanbits, dtype=np.uint32).view(np.float32)
         self.free = list(range(n_blocks))
+        self.refs = [0] * n_blocks
         self.table = {}
         self.length = {}
 
     # ------------------------------------------------------------ allocation
+    def _take(self):
+        b = self.free.pop()
+        self.refs[b] = 1
+        return b
+
     def alloc(self, seq, n_tokens):
         n = -(-n_tokens // BLOCK)                      # ceil-div
         if n > len(self.free):
             raise MemoryError("no free blocks")
-        self.table[seq] = [self.free.pop() for _ in range(n)]
+        self.table[seq] = [self._take() for _ in range(n)]
         self.length[seq] = n_tokens
 
+    def _shared_partial(self, s):
+        return self.length[s] % BLOCK != 0 and self.refs[self.table[s][-1]] > 1
+
+    def _copy_block(self, src, dst):
+        self.K[:, dst] = self.K[:, src]
+        self.V[:, dst] = self.V[:, src]
+        if self.dtype == "fp8":
+            self.Ks[:, dst] = self.Ks[:, src]
+            self.Vs[:, dst] = self.Vs[:, src]
+
     def grow(self, seqs):
-        need = sum(1 for s in seqs if self.length[s] % BLOCK == 0)
+        need = sum(1 for s in seqs if self.length[s] % BLOCK == 0 or self._shared_partial(s))
         if need > len(self.free):
             raise MemoryError("no free blocks")
         for s in seqs:
             if self.length[s] % BLOCK == 0:
-                self.table[s].append(self.free.pop())
+                self.table[s].append(self._take())
+            elif self._shared_partial(s):               # copy before writing
+                old = self.table[s][-1]
+                new = self._take()
+                self._copy_block(old, new)
+                self.refs[old] -= 1
+                self.table[s][-1] = new
             self.length[s] += 1
 
     def grow_by(self, seq, n):
         """n single-token grows of one sequence (a prompt chunk)."""
         need = -(-(self.length[seq] + n) // BLOCK) - -(-self.length[seq] // BLOCK)
+        need += 1 if n > 0 and self._shared_partial(seq) else 0
         if need > len(self.free):
             raise MemoryError("no free blocks")
         for _ in range(n):
             self.grow([seq])
 
+    def share_prefix(self, src, dst, prefix_len):
+        """dst holds the first prefix_len rows of src through the same blocks."""
+        assert dst not in self.table and 0 <= prefix_len <= self.length[src]
+        n = -(-prefix_len // BLOCK)
+        self.table[dst] = self.table[src][:n].copy()
+        for b in self.table[dst]:
+            self.refs[b] += 1
+        self.length[dst] = prefix_len
+
     def release(self, seq):
-        self.free.extend(self.table.pop(seq))
+        for b in self.table.pop(seq):
+            self.refs[b] -= 1
+            if self.refs[b] == 0:
+                self.free.append(b)
         del self.length[seq]
 
     def set_table(self, seq, blocks, length):
@@ -82,6 +127,7 @@ class PagedCacheModel:
         assert len(blocks) == -(-length // BLOCK)
         for b in blocks:
             self.free.remove(b)
+            self.refs[b] = 1
         self.table[seq] = blocks
         self.length[seq] = length
 

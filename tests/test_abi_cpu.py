@@ -72,6 +72,7 @@ def host_cache(n_blocks=40, max_seqs=6, max_bps=8):
 
 def assert_same(c, m):
     assert c.free_blocks() == len(m.free)
+    assert [c.block_refs(b) for b in range(len(m.refs))] == m.refs
     for s in range(c.cfg.max_seqs):
         if s in m.table:
             assert c.seq_blocks(s) == m.table[s] and c.seq_len(s) == m.length[s]
@@ -99,10 +100,20 @@ def test_allocator_matches_the_page_listing_model():
             else:
                 with pytest.raises(kv.KvcError):
                     c.seq_alloc(s, n)
+        elif op < 0.38 and live:
+            src = rng.choice(live)
+            free_ids = [x for x in range(6) if x not in m.table]
+            if not free_ids:
+                continue
+            dst = rng.choice(free_ids)
+            plen = rng.randrange(0, m.length[src] + 1)
+            m.share_prefix(src, dst, plen)
+            c.seq_share_prefix(src, dst, plen)
         elif op < 0.45 and live:
             s = rng.choice(live)
             n = rng.randrange(0, 40)
             need = -(-(m.length[s] + n) // 16) - -(-m.length[s] // 16)
+            need += 1 if n > 0 and m._shared_partial(s) else 0
             if m.length[s] + n > 8 * 16:
                 with pytest.raises(kv.KvcError) as e:
                     c.seq_grow_by(s, n)
@@ -118,7 +129,7 @@ def test_allocator_matches_the_page_listing_model():
             seqs = rng.sample(live, rng.randrange(1, len(live) + 1))
             if any(m.length[s] + 1 > 8 * 16 for s in seqs):
                 continue
-            need = sum(1 for s in seqs if m.length[s] % 16 == 0)
+            need = sum(1 for s in seqs if m.length[s] % 16 == 0 or m._shared_partial(s))
             if need > len(m.free):
                 with pytest.raises(kv.KvcError) as e:
                     c.seq_grow(seqs)
@@ -131,8 +142,9 @@ def test_allocator_matches_the_page_listing_model():
             m.release(s)
             c.seq_release(s)
         assert_same(c, m)
-        owned = [b for t in m.table.values() for b in t]
-        assert len(owned) == len(set(owned)) and not set(owned) & set(m.free)
+        held = [b for t in m.table.values() for b in t]
+        assert not set(held) & set(m.free)
+        assert all(m.refs[b] == held.count(b) for b in set(held))
 
 
 def test_exhaustion_leaves_state_unchanged():
@@ -247,3 +259,43 @@ def test_window_arguments_are_checked():
     rc = L.kvc_attn_prefill_window(f._h, 0, 1, None, 4, p, p, p, p, ctypes.c_float(0.1), 8, 0,
                                    None)
     assert rc == kv.KVC_E_UNSUPPORTED
+
+
+def test_share_prefix_and_copy_on_write_bookkeeping():
+    """Sharing a prefix that ends inside a block: both sequences hold it
+    (refcount 2); the first grow of either one moves it to a fresh block
+    and leaves the other one alone; releases free a block only when its
+    last holder goes."""
+    c, m = host_cache(), PagedCacheModel(1, 2, 64, "bf16", 40, 6, 8, poison=False)
+    for x in (c, m):
+        (x.seq_alloc if x is c else x.alloc)(0, 40)               # blocks for rows 0..39
+    c.seq_share_prefix(0, 1, 36)
+    m.share_prefix(0, 1, 36)
+    assert_same(c, m)
+    shared = c.seq_blocks(0)
+    assert c.seq_blocks(1) == shared and all(c.block_refs(b) == 2 for b in shared)
+    c.seq_grow([1])                                                # row 36 of seq 1: copy
+    m.grow([1])
+    assert_same(c, m)
+    assert c.seq_blocks(1)[:2] == shared[:2] and c.seq_blocks(1)[2] != shared[2]
+    assert c.block_refs(shared[2]) == 1
+    c.seq_grow([0])                                                # row 40 of seq 0: no copy
+    m.grow([0])
+    assert_same(c, m) and c.seq_blocks(0) == shared
+    c.seq_share_prefix(1, 2, 32)                                   # whole blocks: no copy later
+    m.share_prefix(1, 2, 32)
+    c.seq_grow_by(2, 5)
+    m.grow_by(2, 5)
+    assert_same(c, m)
+    assert c.seq_blocks(2)[:2] == shared[:2]
+    free0 = c.free_blocks()
+    c.seq_release(0)
+    m.release(0)
+    assert_same(c, m)
+    assert c.free_blocks() == free0 + 1                            # only block 2 of seq 0
+    with pytest.raises(kv.KvcError) as e:
+        c.seq_share_prefix(1, 2, 3)                                # dst already live
+    assert e.value.code == kv.KVC_E_STATE
+    with pytest.raises(kv.KvcError) as e:
+        c.seq_share_prefix(1, 3, 38)                               # longer than src
+    assert e.value.code == kv.KVC_E_INVAL
