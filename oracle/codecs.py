@@ -142,3 +142,77 @@ def fp8_slab_write(codes, scale, r0, new_rows):
         q = (row / s).astype(np.float32) if s > 0 else row
         codes[r0 + i] = e4m3_encode(q)
     return codes, s
+
+
+# ------------------------------------------------------------------ int4
+# The pages name an int4 cache only in passing ([KVFA] memory-cost section:
+# servers quantize the cache to fp8 or int4 first).  Reading: symmetric
+# integers -7 .. 7 (the code -8 is never produced) times one float32 scale
+# per (layer, block, kv head) slab, the same slab granularity and growth rule
+# as the fp8 cache with 7 in place of 448.  Two codes per byte, element 2i in
+# the low nibble, two's complement.
+INT4_MAX = 7
+
+
+def int4_encode(y):
+    """Codes of already-scaled float32 values: round to nearest, ties to
+    even, clamped to -7 .. 7.  Returns int8 codes."""
+    y = np.asarray(y, dtype=np.float64)
+    if np.isnan(y).any():
+        raise ValueError("NaN has no encoding in this codec")
+    return np.clip(np.rint(y), -INT4_MAX, INT4_MAX).astype(np.int8)
+
+
+def int4_decode(codes):
+    """Exact value of int4 codes (before the scale)."""
+    return np.asarray(codes, dtype=np.float64)
+
+
+def int4_slab_write(codes, scale, r0, new_rows):
+    """Write rows r0 .. r0+n-1 of one (block, kv head) slab of an int4 cache.
+
+    codes: int8 [16, d] current codes of the slab (rows < r0 are live);
+    scale: float32 current scale (ignored when r0 == 0); new_rows: [n, d]
+    float32 values.  Returns (codes, scale).  The scale is absmax/7 over every
+    row written so far, kept as max(s_old, absmax(new)/7); when it grows the
+    live rows are re-encoded: x = fl32(code * s_old), code' =
+    encode(fl32(x / s_new)).  An all-zero slab has scale 0 and codes 0.
+    """
+    codes = np.array(codes, dtype=np.int8, copy=True)
+    new_rows = np.asarray(new_rows, dtype=np.float32)
+    amax = F32(np.max(np.abs(new_rows))) if new_rows.size else F32(0.0)
+    s_new = F32(amax / F32(INT4_MAX))
+    if r0 == 0:
+        s = s_new
+    else:
+        s_old = F32(scale)
+        s = F32(max(s_old, s_new))
+        if s > s_old:
+            for r in range(r0):
+                x = (codes[r].astype(np.float32) * s_old).astype(np.float32)
+                codes[r] = int4_encode((x / s).astype(np.float32))
+    for i in range(new_rows.shape[0]):
+        row = new_rows[i]
+        q = (row / s).astype(np.float32) if s > 0 else row
+        codes[r0 + i] = int4_encode(q)
+    return codes, s
+
+
+def int4_pack(codes, axis=-1):
+    """Pack int8 codes two per byte along `axis` (even index in the low
+    nibble).  The axis length must be even."""
+    c = np.moveaxis(np.asarray(codes, dtype=np.int8), axis, -1).astype(np.uint8) & 0x0F
+    packed = c[..., 0::2] | (c[..., 1::2] << 4)
+    return np.moveaxis(packed.astype(np.uint8), -1, axis)
+
+
+def int4_unpack(packed, axis=-1):
+    """Inverse of int4_pack: int8 codes."""
+    p = np.moveaxis(np.asarray(packed, dtype=np.uint8), axis, -1)
+    lo = (p & 0x0F).astype(np.int8)
+    hi = (p >> 4).astype(np.int8)
+    lo = np.where(lo > 7, lo - 16, lo).astype(np.int8)
+    hi = np.where(hi > 7, hi - 16, hi).astype(np.int8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.int8)
+    out[..., 0::2], out[..., 1::2] = lo, hi
+    return np.moveaxis(out, -1, axis)

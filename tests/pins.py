@@ -362,3 +362,46 @@ def check_bf16_vs_torch(bits_fn, seed=8):
     x = np.concatenate([x, ties, -ties, np.float32([0.0, -0.0, 3.0e38, 1e-40])])
     t = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     return bool(np.array_equal(bits_fn(x), t))
+
+
+def check_int4_encode_brute(encode_fn, seed=15):
+    """Nearest of the 15 levels -7..7 by brute force, ties to the even level,
+    saturation beyond +-7, for random values and every tie point."""
+    rng = np.random.default_rng(seed)
+    ys = np.concatenate([rng.uniform(-9, 9, 4000).astype(np.float32),
+                         np.arange(-8.5, 8.6, 0.5, dtype=np.float32),
+                         np.array([-0.0, 0.0, 7.49, -7.51, 100.0, -1e6], dtype=np.float32)])
+    levels = np.arange(-7, 8)
+    got = encode_fn(ys)
+    for y, c in zip(ys.astype(np.float64), got):
+        dist = np.abs(levels - y)
+        best = levels[dist == dist.min()]
+        want = best[0] if len(best) == 1 else best[best % 2 == 0][0]
+        if int(c) != int(want):
+            return False
+    return True
+
+
+def check_int4_slab_rule(slab_fn, seed=16):
+    """After every write the scale is absmax/7 of all rows written; decoded
+    values stay within (k+1)/2 scale steps after k re-encodings; rows above
+    the written ones keep their codes."""
+    rng = np.random.default_rng(seed)
+    d = 8
+    codes = np.full((16, d), 5, dtype=np.int8)
+    scale, r0, seen = np.float32(0), 0, []
+    for n in (3, 1, 5, 2, 4):
+        rows = (rng.standard_normal((n, d)) * rng.uniform(0.1, 10)).astype(np.float32)
+        codes, scale = slab_fn(codes, scale, r0, rows)
+        seen.append(rows)
+        allr = np.concatenate(seen)
+        if np.float32(scale) != np.float32(np.abs(allr).max() / np.float32(7)):
+            return False
+        if not np.all(codes[r0 + n:] == 5):
+            return False
+        k = len(seen)
+        err = np.abs(codes[:r0 + n].astype(np.float64) * scale - allr)
+        if np.any(err > (k + 1) / 2 * scale * (1 + 1e-6)):
+            return False
+        r0 += n
+    return True

@@ -201,3 +201,28 @@ def test_sinks_ignored_is_caught():
         return A.gqa_attention(q, k, v, scale, q_pos, window, 0)
     assert not pins.check_window_vs_sdpa(no_sinks)
     assert not pins.check_window_special_cases(no_sinks)
+
+
+def test_int4_ties_away_is_caught():
+    def ties_away(y):
+        y = np.asarray(y, dtype=np.float64)
+        return np.clip(np.sign(y) * np.floor(np.abs(y) + 0.5), -7, 7).astype(np.int8)
+    assert not pins.check_int4_encode_brute(ties_away)
+
+
+def test_int4_truncation_is_caught():
+    def trunc(y):
+        return np.clip(np.trunc(np.asarray(y, dtype=np.float64)), -7, 7).astype(np.int8)
+    assert not pins.check_int4_encode_brute(trunc)
+
+
+def test_int4_slab_without_requantisation_is_caught():
+    def no_requant(codes, scale, r0, new_rows):
+        codes = np.array(codes, dtype=np.int8, copy=True)
+        new_rows = np.asarray(new_rows, dtype=np.float32)
+        s_new = np.float32(np.abs(new_rows).max() / np.float32(7))
+        s = s_new if r0 == 0 else np.float32(max(np.float32(scale), s_new))
+        for i, row in enumerate(new_rows):
+            codes[r0 + i] = C.int4_encode((row / s).astype(np.float32) if s > 0 else row)
+        return codes, s
+    assert not pins.check_int4_slab_rule(no_requant)

@@ -257,3 +257,21 @@ def test_paged_model_bit_copy_and_layout():
     kr, vr = m.logical_raw(1, 0)
     assert np.array_equal(kr, k) and np.array_equal(vr, v)
     assert np.all(m.K[0] == 0xFFFF) and np.all(m.K[1, 1, :, 4:] == 0xFFFF)
+
+
+def test_int4_encode_is_nearest_level_ties_to_even():
+    assert pins.check_int4_encode_brute(C.int4_encode)
+
+
+def test_int4_slab_rule():
+    assert pins.check_int4_slab_rule(C.int4_slab_write)
+
+
+def test_int4_pack_round_trip():
+    rng = np.random.default_rng(3)
+    c = rng.integers(-7, 8, (3, 16, 10)).astype(np.int8)
+    for axis in (-1, -2):
+        p = C.int4_pack(c, axis)
+        assert np.array_equal(C.int4_unpack(p, axis), c)
+    p = C.int4_pack(np.array([[1, -1, 7, -7]], dtype=np.int8))
+    assert p.tolist() == [[0xF1, 0x97]]
