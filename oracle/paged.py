@@ -24,7 +24,10 @@ other block, all layers copied).
 Physical layout of one layer's pools (the library's documented layout):
   K[block][kv_head][slot 0..15][d]      (a token's d values contiguous)
   V[block][kv_head][d][slot 0..15]      (a d-column's 16 tokens contiguous)
-  Kscale, Vscale[block][kv_head]        float32, fp8 caches only
+  Kscale, Vscale[block][kv_head]        float32, fp8 and int4 caches only
+An int4 cache holds its codes here unpacked (int8, -7..7); the library stores
+them two per byte along the last axis (K rows: d/2 bytes, V columns: 8 bytes
+of 16 tokens), which ``codecs.int4_pack`` reproduces.
 Stored elements are raw storage-format bit patterns.  Unwritten slots keep
 whatever was there (tests fill the pools with a poison pattern first), and
 this model keeps the same poison so whole pools can be compared.
@@ -32,11 +35,14 @@ this model keeps the same poison so whole pools can be compared.
 import numpy as np
 
 from .codecs import (bf16_bits_to_f64, e4m3_decode, f16_bits_to_f64,
-                     fp8_slab_write)
+                     fp8_slab_write, int4_slab_write)
 
 BLOCK = 16
-STORAGE = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8}
-POISON = {"f32": 0xFFFFFFFF, "f16": 0xFFFF, "bf16": 0xFFFF, "fp8": 0xFF}
+STORAGE = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8,
+           "int4": np.int8}
+POISON = {"f32": 0xFFFFFFFF, "f16": 0xFFFF, "bf16": 0xFFFF, "fp8": 0xFF,
+          "int4": -1}                                 # 0xF nibbles
+SCALED = ("fp8", "int4")
 
 
 class PagedCacheModel:
@@ -49,7 +55,7 @@ class PagedCacheModel:
         fill = POISON[dtype] if poison else 0
         self.K = np.full((n_layers, n_blocks, n_kv, BLOCK, d), fill, dtype=st)
         self.V = np.full((n_layers, n_blocks, n_kv, d, BLOCK), fill, dtype=st)
-        if dtype == "fp8":
+        if dtype in SCALED:
             nanbits = np.uint32(0xFFFFFFFF) if poison else np.uint32(0)
             self.Ks = np.full((n_layers, n_blocks, n_kv), nanbits, dtype=np.uint32).view(np.float32)
             self.Vs = np.full((n_layers, n_blocks, n_kv), nanbits, dtype=np.uint32).view(np.float32)
@@ -77,7 +83,7 @@ class PagedCacheModel:
     def _copy_block(self, src, dst):
         self.K[:, dst] = self.K[:, src]
         self.V[:, dst] = self.V[:, src]
-        if self.dtype == "fp8":
+        if self.dtype in SCALED:
             self.Ks[:, dst] = self.Ks[:, src]
             self.Vs[:, dst] = self.Vs[:, src]
 
@@ -140,30 +146,32 @@ class PagedCacheModel:
 
         k_rows, v_rows: [T, n_kv, d].  For 16/32-bit caches they are the
         storage bit patterns (uint16 / uint32) and are copied bit for bit; for
-        an fp8 cache they are float32 values (bf16 inputs widened exactly) and
-        go through the per-slab scale rule, one slab write per (block, head)
-        covering all of the new rows that land in that block.
+        an fp8 or int4 cache they are float32 values (bf16 inputs widened
+        exactly) and go through that format's per-slab scale rule, one slab
+        write per (block, head) covering all of the new rows that land in that
+        block.
         """
         T = k_rows.shape[0]
         assert start + T <= self.length[seq]
-        if self.dtype != "fp8":
+        if self.dtype not in SCALED:
             st = STORAGE[self.dtype]
             for i in range(T):
                 b, r = self.physical(seq, start + i)
                 self.K[layer, b, :, r, :] = np.asarray(k_rows[i]).view(st)
                 self.V[layer, b, :, :, r] = np.asarray(v_rows[i]).view(st)
             return
+        slab_write = fp8_slab_write if self.dtype == "fp8" else int4_slab_write
         p = start
         while p < start + T:
             b, r0 = self.physical(seq, p)
             n = min(BLOCK - r0, start + T - p)
             i0 = p - start
             for h in range(self.n_kv):
-                kc, ks = fp8_slab_write(self.K[layer, b, h], self.Ks[layer, b, h], r0,
+                kc, ks = slab_write(self.K[layer, b, h], self.Ks[layer, b, h], r0,
                                         k_rows[i0:i0 + n, h, :])
                 self.K[layer, b, h] = kc
                 self.Ks[layer, b, h] = ks
-                vc, vs = fp8_slab_write(self.V[layer, b, h].T, self.Vs[layer, b, h], r0,
+                vc, vs = slab_write(self.V[layer, b, h].T, self.Vs[layer, b, h], r0,
                                         v_rows[i0:i0 + n, h, :])
                 self.V[layer, b, h] = vc.T
                 self.Vs[layer, b, h] = vs
@@ -177,6 +185,8 @@ class PagedCacheModel:
             return f16_bits_to_f64(raw)
         if self.dtype == "bf16":
             return bf16_bits_to_f64(raw)
+        if self.dtype == "int4":
+            return raw.astype(np.float64)
         return e4m3_decode(raw)
 
     def logical_raw(self, layer, seq, start=0, count=None):
@@ -191,12 +201,20 @@ class PagedCacheModel:
             Vr[i] = self.V[layer, b, :, :, r]
         return Kr, Vr
 
+    def packed_pools(self, layer=None):
+        """int4: the K and V pools as the library stores them, two codes per byte."""
+        from .codecs import int4_pack
+        assert self.dtype == "int4"
+        K = self.K if layer is None else self.K[layer]
+        V = self.V if layer is None else self.V[layer]
+        return int4_pack(K, axis=-1), int4_pack(V, axis=-1)
+
     def logical_values(self, layer, seq):
         """Dequantised K, V of the whole sequence as exact float64 [L, n_kv, d]."""
         L = self.length[seq]
         Kr, Vr = self.logical_raw(layer, seq)
         K, V = self._widen(Kr), self._widen(Vr)
-        if self.dtype == "fp8":
+        if self.dtype in SCALED:
             for i in range(L):
                 b, _ = self.physical(seq, i)
                 K[i] *= self.Ks[layer, b, :].astype(np.float64)[:, None]

@@ -275,3 +275,38 @@ def test_int4_pack_round_trip():
         assert np.array_equal(C.int4_unpack(p, axis), c)
     p = C.int4_pack(np.array([[1, -1, 7, -7]], dtype=np.int8))
     assert p.tolist() == [[0xF1, 0x97]]
+
+
+def test_paged_model_int4_chunks_scales_and_packing():
+    """An int4 cache written in chunks that cross a block boundary: every
+    slab's scale is absmax/7 of the rows written into it, every value lies
+    within (k+1)/2 scale steps of its input after k writes into its slab,
+    untouched slots keep the poison code, and the packed pools unpack to the
+    model's codes."""
+    rng = np.random.default_rng(21)
+    m = PagedCacheModel(1, 2, 8, "int4", n_blocks=4, max_seqs=1, max_blocks_per_seq=4)
+    m.set_table(0, [2], 5)
+    k = (rng.standard_normal((27, 2, 8)) * 3).astype(np.float32)
+    v = (rng.standard_normal((27, 2, 8)) * 0.5).astype(np.float32)
+    m.write_rows(0, 0, 0, k[:5], v[:5])
+    writes = {2: 1}
+    for a, b in ((5, 12), (12, 19), (19, 27)):
+        m.grow_by(0, b - a)
+        m.write_rows(0, 0, a, k[a:b], v[a:b])
+        for blk in {m.physical(0, p)[0] for p in range(a, b)}:
+            writes[blk] = writes.get(blk, 0) + 1
+    K, V = m.logical_values(0, 0)
+    for p in range(27):
+        blk, _ = m.physical(0, p)
+        rows = [q for q in range(27) if m.physical(0, q)[0] == blk]
+        for h in range(2):
+            sk = np.float32(np.abs(k[rows, h]).max() / np.float32(7))
+            assert m.Ks[0, blk, h] == sk
+            tol = (writes[blk] + 1) / 2 * float(sk) * (1 + 1e-6)
+            assert np.all(np.abs(K[p, h] - k[p, h]) <= tol)
+    assert m.table[0] == [2, 3]
+    assert np.all(m.K[0, 3, :, 11:] == -1)                   # positions 27.. unwritten
+    pk, pv = m.packed_pools(0)
+    assert pk.shape == (4, 2, 16, 4) and pv.shape == (4, 2, 8, 8) and pk.dtype == np.uint8
+    assert np.array_equal(C.int4_unpack(pk), m.K[0]) and np.array_equal(C.int4_unpack(pv), m.V[0])
+    assert np.all(pk[0] == 0xFF) and np.all(pv[1] == 0xFF)   # never-allocated blocks: poison
