@@ -97,7 +97,7 @@ def counter_traffic(key):
 def build_decode(name, torch, kv):
     from workloads import decode_workload
     w = decode_workload(name)
-    dt = {"bf16": "bf16", "fp16": "f16", "fp8": "fp8"}[w.kv_dtype]
+    dt = {"bf16": "bf16", "fp16": "f16", "fp8": "fp8", "int4": "int4"}[w.kv_dtype]
     io = kv.IO_TORCH[dt]
     spare = w.batch * 8                                     # room to grow during the run
     max_bps = int(w.blocks_per_seq.max()) + 8
@@ -117,16 +117,20 @@ def build_decode(name, torch, kv):
     return w, c, io
 
 
+KV_ELEM_BYTES = {"bf16": 2, "fp16": 2, "fp8": 1, "int4": 0.5}
+
+
 def decode_bytes(w, lengths, kv_elem):
     """Algorithmic HBM bytes of one decode call: every valid K and V row once
     (per kv head), the query and output rows, one table entry per block, and
-    for fp8 the two scales per block and kv head."""
+    for fp8 and int4 the two scales per block and kv head.  kv_elem: bytes per
+    stored element (0.5 for int4)."""
     rows = int(np.sum(lengths))
-    kvb = 2 * rows * w.n_kv * w.d * kv_elem
+    kvb = int(2 * rows * w.n_kv * w.d * kv_elem)
     qo = 2 * w.batch * w.n_q * w.d * 2
     blocks = int(np.sum(-(-np.asarray(lengths) // 16)))
     tab = blocks * 4
-    sc = 2 * blocks * w.n_kv * 4 if kv_elem == 1 else 0
+    sc = 2 * blocks * w.n_kv * 4 if kv_elem < 2 else 0
     return kvb + qo + tab + sc
 
 
@@ -181,7 +185,7 @@ def bench_decode_window(steps, torch, kv, window=1024, sinks=4):
 
 def bench_decode(name, steps, warmup, torch, kv, with_cpu):
     w, c, io = build_decode(name, torch, kv)
-    kv_elem = 1 if w.kv_dtype == "fp8" else 2
+    kv_elem = KV_ELEM_BYTES[w.kv_dtype]
     seqs_host = list(range(w.batch))
     seqs = torch.arange(w.batch, dtype=torch.int32, device="cuda")
     rng = np.random.default_rng(123)
@@ -503,6 +507,8 @@ DECODE_WORKLOADS = {
                             "1% outliers x8",
     "llama70b_decode_fp8": "8 x 32,768-token contexts, 64 q / 8 kv heads, d 128, fp8-e4m3 cache "
                            "with per-block scales, 1% outliers x8",
+    "llama70b_decode_int4": "8 x 32,768-token contexts, 64 q / 8 kv heads, d 128, int4 cache "
+                            "with per-block scales, 1% outliers x8",
     "long_mha_decode": "1 x 128,000-token context, 32 / 32 heads, d 128, fp16 cache, "
                        "split-context decode",
 }
@@ -569,7 +575,8 @@ def main():
         return
 
     dec = bench_decode(args.workload, args.steps, args.warmup, torch, kv, with_cpu)
-    dtype = {"bf16": "bf16", "fp16": "f16", "fp8": "fp8-e4m3 (bf16 q/o)"}[dec["shape"]["kv_dtype"]]
+    dtype = {"bf16": "bf16", "fp16": "f16", "fp8": "fp8-e4m3 (bf16 q/o)",
+             "int4": "int4 (bf16 q/o)"}[dec["shape"]["kv_dtype"]]
     line = {"metric": METRIC, "value": dec["value"], "unit": "GB/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": dec["ms_per_step"],
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -582,6 +589,8 @@ def main():
         line["extend"] = bench_extend(max(5, args.steps // 2), 2, torch, kv, with_cpu)
         line["decode_window"] = bench_decode_window(max(5, args.steps // 2), torch, kv)
         line["prefix_share"] = bench_prefix_share(torch, kv)
+        line["decode_int4"] = bench_decode("llama70b_decode_int4", max(5, args.steps // 2), 2,
+                                           torch, kv, False)
     print(json.dumps(line))
 
 

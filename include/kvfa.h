@@ -26,7 +26,7 @@
  *
  *   k_pool  [n_layers][n_blocks][n_kv_heads][16][d_head]
  *   v_pool  [n_layers][n_blocks][n_kv_heads][d_head][16]   (slot innermost)
- *   k_scale, v_scale [n_layers][n_blocks][n_kv_heads]  float, fp8 only
+ *   k_scale, v_scale [n_layers][n_blocks][n_kv_heads]  float, fp8 and int4 only
  *   block_table [max_seqs][max_blocks_per_seq]  int32, -1 where unused
  *   seq_len     [max_seqs]                       int32 tokens stored
  *
@@ -39,6 +39,19 @@
  * encode(fl(decode(code) * s_old) / s_new), all in IEEE float32.  Queries and
  * outputs use the storage type, except that an fp8 cache takes bf16 queries,
  * keys, values and outputs ("io type").
+ *
+ * int4 (kvcache-7e2 names an int4 cache in its memory-cost section and
+ * fixes nothing else, so the format below is this library's): codes are
+ * signed integers -7 .. 7 (two's complement nibbles; -8 is never written),
+ * two per byte with the element of even index in the low nibble, so a K
+ * slab is [16][d_head / 2] bytes and a V slab [d_head][8] bytes (tokens 2i
+ * and 2i+1 of a column share byte i).  Scales follow the fp8 rule with 7 in
+ * place of 448: absmax/7 per (layer, block, kv head), a code holds
+ * rint(x / scale) (ties to even) clamped to +-7, and a growing absmax
+ * re-encodes the block's earlier rows as encode(fl(code * s_old) / s_new).
+ * The io type is bf16.  Only kv_append, kvc_write, the decode calls
+ * (kvc_attn_decode, kvc_attn_decode_window), kvc_gather and the
+ * cache-independent prefill calls take an int4 cache.
  *
  * Conventions.  Every function returns KVC_OK (0) or a negative status and
  * never throws; kvc_last_error() gives a message for the calling thread.
@@ -78,7 +91,8 @@ typedef enum kvc_dtype {
   KVC_F32 = 0,
   KVC_F16 = 1,
   KVC_BF16 = 2,
-  KVC_FP8_E4M3FN = 3
+  KVC_FP8_E4M3FN = 3,
+  KVC_INT4 = 4
 } kvc_dtype;
 
 typedef struct kvc_config {
@@ -100,7 +114,7 @@ typedef struct kvc_sizes {    /* bytes the caller must allocate on the device   
 typedef struct kvc_buffers {  /* caller-owned device buffers, sized by kvc_sizes   */
   void* k_pool;
   void* v_pool;
-  float* k_scale;             /* NULL unless kv_dtype is fp8                       */
+  float* k_scale;             /* NULL unless kv_dtype is fp8 or int4               */
   float* v_scale;
   int32_t* block_table;
   int32_t* seq_len;
@@ -111,7 +125,8 @@ typedef struct kvc_cache kvc_cache;
 /* Cache bytes per token over all layers: 2 (K and V) x n_layers x n_kv_heads
  * x d_head x element bytes (kvcache-7e2 memory-cost section; deepforge
  * cache-size formula; abhishekpatel "Opening the hood").  fp8 counts one
- * byte per element; the per-block scales are not included. */
+ * byte per element, int4 half a byte; the per-block scales are not
+ * included. */
 int kvc_bytes_per_token(const kvc_config* cfg, uint64_t* out);
 
 /* Device bytes for every buffer of a cache with this configuration. */
@@ -184,15 +199,15 @@ int kvc_free_blocks(const kvc_cache* cache, int32_t* out);
 /* kv_append: store the newest token's K and V rows of one layer for each of n
  * sequences, at position seq_len[seq] - 1 (call kvc_seq_grow first).
  * k_dev, v_dev: [n][n_kv_heads][d_head] in the io type.  16/32-bit caches
- * store the bits unchanged; fp8 caches apply the scale rule above. */
+ * store the bits unchanged; fp8 and int4 caches apply their scale rule. */
 int kvc_append(kvc_cache* cache, int32_t layer, int32_t n, const int32_t* seqs_dev,
                const void* k_dev, const void* v_dev, hipStream_t stream);
 
 /* Bulk store of T consecutive rows per sequence (prefill, population):
  * positions start .. start+T-1 of each of n sequences, which must all lie
  * below the sequence's length.  k_dev, v_dev: [n][T][n_kv_heads][d_head] in
- * the io type.  For fp8 each (block, kv head) is written once with all of
- * its new rows (the scale rule applied to the rows together). */
+ * the io type.  For fp8 and int4 each (block, kv head) is written once with
+ * all of its new rows (the scale rule applied to the rows together). */
 int kvc_write(kvc_cache* cache, int32_t layer, int32_t n, const int32_t* seqs_dev,
               int32_t start, int32_t T, const void* k_dev, const void* v_dev,
               hipStream_t stream);
@@ -272,7 +287,9 @@ int kvc_attn_extend_window(kvc_cache* cache, int32_t layer, int32_t n, const int
 
 /* Block-table gather: copy the stored bit patterns of positions start ..
  * start+count-1 of `seq` in logical order into k_out_dev, v_out_dev, each
- * [count][n_kv_heads][d_head] of the storage type (fp8: raw codes). */
+ * [count][n_kv_heads][d_head] of the storage type (fp8: raw codes; int4:
+ * [count][n_kv_heads][d_head / 2] bytes, codes packed along d_head as in
+ * the pools' K rows, for V as well). */
 int kvc_gather(const kvc_cache* cache, int32_t layer, int32_t seq, int32_t start, int32_t count,
                void* k_out_dev, void* v_out_dev, hipStream_t stream);
 

@@ -22,13 +22,15 @@ _lib = None
 
 KVC_OK, KVC_E_INVAL, KVC_E_UNSUPPORTED, KVC_E_NO_BLOCKS = 0, -1, -2, -3
 KVC_E_STATE, KVC_E_WORKSPACE, KVC_E_HIP = -4, -5, -6
-KVC_F32, KVC_F16, KVC_BF16, KVC_FP8_E4M3FN = 0, 1, 2, 3
+KVC_F32, KVC_F16, KVC_BF16, KVC_FP8_E4M3FN, KVC_INT4 = 0, 1, 2, 3, 4
 
-DTYPES = {"f32": KVC_F32, "f16": KVC_F16, "bf16": KVC_BF16, "fp8": KVC_FP8_E4M3FN}
+DTYPES = {"f32": KVC_F32, "f16": KVC_F16, "bf16": KVC_BF16, "fp8": KVC_FP8_E4M3FN,
+          "int4": KVC_INT4}
 STORAGE_TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
-                 "fp8": torch.uint8}
+                 "fp8": torch.uint8, "int4": torch.uint8}
 IO_TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
-            "fp8": torch.bfloat16}
+            "fp8": torch.bfloat16, "int4": torch.bfloat16}
+SCALED = ("fp8", "int4")
 BLOCK = 16
 
 
@@ -136,9 +138,11 @@ def required_sizes(cfg):
 class KvCache:
     """One paged cache: device pools and tables as torch tensors + the handle.
 
-    kv_dtype: 'f32' | 'f16' | 'bf16' | 'fp8'.  device=None makes a host-only
-    handle (allocator only).  `poison` fills the pools with 0xFF bytes (NaN in
-    every storage format) so that reads of unwritten slots would show.
+    kv_dtype: 'f32' | 'f16' | 'bf16' | 'fp8' | 'int4'.  device=None makes a
+    host-only handle (allocator only).  `poison` fills the pools with 0xFF
+    bytes (NaN in every floating storage format, code -1 in int4) so that
+    reads of unwritten slots would show.  int4 pools are uint8 tensors
+    [L][B][h][16][d/2] (K) and [L][B][h][d][8] (V), two codes per byte.
     """
 
     def __init__(self, n_layers, n_q_heads, n_kv_heads, d_head, n_blocks, max_seqs,
@@ -155,14 +159,15 @@ class KvCache:
         sizes = required_sizes(self.cfg)
         st = STORAGE_TORCH[kv_dtype]
         fill = 0xFF if poison else 0
-        self.k_pool = torch.full((n_layers, n_blocks, n_kv_heads, BLOCK, d_head), 0,
+        half = 2 if kv_dtype == "int4" else 1
+        self.k_pool = torch.full((n_layers, n_blocks, n_kv_heads, BLOCK, d_head // half), 0,
                                  dtype=st, device=device)
-        self.v_pool = torch.full((n_layers, n_blocks, n_kv_heads, d_head, BLOCK), 0,
+        self.v_pool = torch.full((n_layers, n_blocks, n_kv_heads, d_head, BLOCK // half), 0,
                                  dtype=st, device=device)
         if poison:
             self.k_pool.view(torch.uint8).fill_(fill)
             self.v_pool.view(torch.uint8).fill_(fill)
-        if kv_dtype == "fp8":
+        if kv_dtype in SCALED:
             self.k_scale = torch.zeros((n_layers, n_blocks, n_kv_heads), dtype=torch.float32,
                                        device=device)
             self.v_scale = torch.zeros_like(self.k_scale)
@@ -325,7 +330,8 @@ class KvCache:
 
     def gather(self, layer, seq, start, count):
         st = STORAGE_TORCH[self.kv_dtype]
-        k = torch.empty((count, self.n_kv, self.d), dtype=st, device=self.k_pool.device)
+        d = self.d // 2 if self.kv_dtype == "int4" else self.d
+        k = torch.empty((count, self.n_kv, d), dtype=st, device=self.k_pool.device)
         v = torch.empty_like(k)
         _check(lib().kvc_gather(self._h, layer, seq, start, count, _ptr(k), _ptr(v), _stream()))
         return k, v

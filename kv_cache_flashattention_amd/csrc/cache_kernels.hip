@@ -74,14 +74,14 @@ __global__ void k_table_update(CacheView cv, TableUpdate u) {
 // ---------------------------------------------------------------- block copy
 // Copy-on-write of a shared block: workgroup (pair p, layer l) copies the
 // K and V data of block src[p] to block dst[p] in layer l (all kv heads,
-// contiguous in both pools) and, for fp8, their per-head scales.  Block ids
+// contiguous in both pools) and, for fp8 and int4, their per-head scales.  Block ids
 // come from the host manager, which only hands out ids below n_blocks.
 __global__ __launch_bounds__(256) void k_copy_blocks(CacheView cv, BlockCopy u) {
   const int p = blockIdx.x, layer = blockIdx.y;
   if (p >= u.n) return;
   const int64_t src = u.src[p], dst = u.dst[p];
   if (src < 0 || src >= cv.n_blocks || dst < 0 || dst >= cv.n_blocks) return;
-  const int64_t bytes = (int64_t)cv.n_kv * kBlock * cv.d * elem_bytes(cv.dtype);
+  const int64_t bytes = cv.n_kv * slab_bytes(cv.dtype, cv.d);
   const int64_t so = ((int64_t)layer * cv.n_blocks + src) * bytes;
   const int64_t dof = ((int64_t)layer * cv.n_blocks + dst) * bytes;
   const uint4* ks = (const uint4*)((const uint8_t*)cv.k + so);
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void k_copy_blocks(CacheView cv, BlockCopy u) 
     kd[i] = ks[i];
     vd[i] = vs[i];
   }
-  if (cv.dtype == KVC_FP8_E4M3FN && threadIdx.x < cv.n_kv) {
+  if (has_scales(cv.dtype) && threadIdx.x < cv.n_kv) {
     const int64_t s0 = ((int64_t)layer * cv.n_blocks + src) * cv.n_kv + threadIdx.x;
     const int64_t d0 = ((int64_t)layer * cv.n_blocks + dst) * cv.n_kv + threadIdx.x;
     cv.ks[d0] = cv.ks[s0];
@@ -280,6 +280,143 @@ __global__ __launch_bounds__(256) void k_write_fp8(CacheView cv, int layer, cons
   }
 }
 
+// ---------------------------------------------------------------- int4
+// Codes are signed nibbles, two per byte (even element low).  K slabs are
+// [16][d/2] bytes, V slabs [d][8] bytes (tokens 2i, 2i+1 of a column in
+// byte i).  A code is rint(x / s) clamped to +-7 with s = absmax/7 of the
+// slab's rows; a growing scale re-encodes the older rows from
+// fl(code * s_old).
+__device__ __forceinline__ uint32_t int4_encode(float y) {
+  const float r = fminf(fmaxf(__builtin_rintf(y), -7.0f), 7.0f);
+  return (uint32_t)(int)r & 0xFu;
+}
+__device__ __forceinline__ float int4_value(uint32_t nib) {
+  return (float)(((int)(nib << 28)) >> 28);
+}
+// New nibble of a slot: `old` re-encoded when the scale grew (rows < r0),
+// the new value x encoded (rows r0 .. r0+nnew-1), else unchanged.
+__device__ __forceinline__ uint32_t int4_update(uint32_t old, int r, int r0, int nnew, float s_old,
+                                                float s, float x) {
+  if (r < r0) return s > s_old ? int4_encode((int4_value(old) * s_old) / s) : old;
+  if (r < r0 + nnew) return int4_encode(s > 0.f ? x / s : x);
+  return old;
+}
+
+// One workgroup per (logical block touched, kv head, sequence), like the
+// bulk writes above; start < 0 selects append mode: one row per sequence,
+// at position seq_len - 1, inputs [n][n_kv][d].  Every thread owns whole
+// bytes, so the two nibbles of a byte are written together.
+__global__ __launch_bounds__(256) void k_write_int4(CacheView cv, int layer, const int32_t* seqs,
+                                                    int start, int T, const uint16_t* kin,
+                                                    const uint16_t* vin) {
+  __shared__ float red[2][4];
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int seq = seqs[b];
+  const int L = seq_length(cv, seq);
+  if (L < 0) return;
+  int lb;
+  if (start < 0) {
+    start = L - 1;
+    T = 1;
+    lb = start / kBlock;
+  } else {
+    if (start + T > L) return;
+    lb = start / kBlock + blockIdx.x;
+  }
+  const int blk = block_of(cv, seq, lb * kBlock);
+  if (blk < 0) return;
+  const int d = cv.d, hb = d / 2;
+  const int p0 = max(start, lb * kBlock), p1 = min(start + T, lb * kBlock + kBlock);
+  const int r0 = p0 - lb * kBlock, nnew = p1 - p0;
+  const int64_t si = scale_idx(cv, layer, blk, h);
+  uint8_t* K = (uint8_t*)cv.k + si * slab_bytes(KVC_INT4, d);
+  uint8_t* V = (uint8_t*)cv.v + si * slab_bytes(KVC_INT4, d);
+  auto in_idx = [&](int r, int j) -> int64_t {     // slab row r (new), column j
+    return (((int64_t)b * T + (lb * kBlock + r - start)) * cv.n_kv + h) * d + j;
+  };
+  // Old scales are read by every thread before the barrier below; thread 0
+  // overwrites them only after it.
+  const float sk_old = r0 > 0 ? cv.ks[si] : 0.f, sv_old = r0 > 0 ? cv.vs[si] : 0.f;
+  float ka = 0.f, va = 0.f;
+  for (int i = threadIdx.x; i < nnew * d; i += blockDim.x) {
+    const int64_t src = in_idx(r0 + i / d, i % d);
+    ka = fmaxf(ka, fabsf(bf16_to_f32(kin[src])));
+    va = fmaxf(va, fabsf(bf16_to_f32(vin[src])));
+  }
+  ka = wave_max(ka);
+  va = wave_max(va);
+  const int w = threadIdx.x / 64;
+  if ((threadIdx.x & 63) == 0) {
+    red[0][w] = ka;
+    red[1][w] = va;
+  }
+  __syncthreads();
+  ka = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+  va = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+  float sk = ka / 7.0f, sv = va / 7.0f;
+  if (r0 > 0) {
+    sk = fmaxf(sk_old, sk);
+    sv = fmaxf(sv_old, sv);
+  }
+  // K: bytes (row r, pair jb) of the rows that change (older rows only when
+  // the scale grew).
+  const int kr_lo = sk > sk_old || r0 == 0 ? 0 : r0;
+  for (int i = kr_lo * hb + threadIdx.x; i < (r0 + nnew) * hb; i += blockDim.x) {
+    const int r = i / hb, jb = i % hb;
+    const uint32_t old = K[i];
+    float x0 = 0.f, x1 = 0.f;
+    if (r >= r0) {
+      x0 = bf16_to_f32(kin[in_idx(r, 2 * jb)]);
+      x1 = bf16_to_f32(kin[in_idx(r, 2 * jb + 1)]);
+    }
+    const uint32_t lo = int4_update(old & 0xFu, r, r0, nnew, sk_old, sk, x0);
+    const uint32_t hi = int4_update(old >> 4, r, r0, nnew, sk_old, sk, x1);
+    K[i] = (uint8_t)(lo | (hi << 4));
+  }
+  // V: bytes (column j, token pair rb).
+  const int vr_lo = sv > sv_old || r0 == 0 ? 0 : r0;
+  const int rb_lo = vr_lo / 2, rb_hi = (r0 + nnew + 1) / 2, nrb = rb_hi - rb_lo;
+  for (int i = threadIdx.x; i < d * nrb; i += blockDim.x) {
+    const int j = i / nrb, rb = rb_lo + i % nrb;
+    uint8_t* p = V + j * (kBlock / 2) + rb;
+    const uint32_t old = *p;
+    const int ra = 2 * rb, rc = 2 * rb + 1;
+    const float x0 = ra >= r0 && ra < r0 + nnew ? bf16_to_f32(vin[in_idx(ra, j)]) : 0.f;
+    const float x1 = rc >= r0 && rc < r0 + nnew ? bf16_to_f32(vin[in_idx(rc, j)]) : 0.f;
+    const uint32_t lo = int4_update(old & 0xFu, ra, r0, nnew, sv_old, sv, x0);
+    const uint32_t hi = int4_update(old >> 4, rc, r0, nnew, sv_old, sv, x1);
+    *p = (uint8_t)(lo | (hi << 4));
+  }
+  if (threadIdx.x == 0) {
+    cv.ks[si] = sk;
+    cv.vs[si] = sv;
+  }
+}
+
+// Gather of an int4 cache: K and V rows [count][n_kv][d/2] bytes, codes
+// packed along d like the K slabs.  One thread per output byte.
+__global__ __launch_bounds__(256) void k_gather_int4(CacheView cv, int layer, int seq, int start,
+                                                     int count, uint8_t* kout, uint8_t* vout) {
+  const int hb = cv.d / 2;
+  const int64_t total = (int64_t)count * cv.n_kv * hb;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int jb = (int)(i % hb);
+    const int h = (int)((i / hb) % cv.n_kv);
+    const int p = start + (int)(i / ((int64_t)hb * cv.n_kv));
+    const int blk = block_of(cv, seq, p);
+    if (blk < 0) continue;
+    const int64_t base = scale_idx(cv, layer, blk, h) * slab_bytes(KVC_INT4, cv.d);
+    const uint8_t* K = (const uint8_t*)cv.k + base;
+    const uint8_t* V = (const uint8_t*)cv.v + base;
+    const int r = p % kBlock, sh = 4 * (r & 1);
+    kout[i] = K[r * hb + jb];
+    const uint32_t lo = (V[(2 * jb) * (kBlock / 2) + r / 2] >> sh) & 0xFu;
+    const uint32_t hi = (V[(2 * jb + 1) * (kBlock / 2) + r / 2] >> sh) & 0xFu;
+    vout[i] = (uint8_t)(lo | (hi << 4));
+  }
+}
+
 // ---------------------------------------------------------------- gather
 template <typename E>
 __global__ __launch_bounds__(256) void k_gather(CacheView cv, int layer, int seq, int start,
@@ -332,6 +469,10 @@ hipError_t launch_append(const CacheView& cv, int layer, int n, const int32_t* s
       hipLaunchKernelGGL(k_append_copy<uint16_t>, grid, dim3(64), 0, s, cv, layer, seqs,
                          (const uint16_t*)k, (const uint16_t*)v);
       break;
+    case KVC_INT4:
+      hipLaunchKernelGGL(k_write_int4, dim3(1, cv.n_kv, n), dim3(256), 0, s, cv, layer, seqs, -1,
+                         1, (const uint16_t*)k, (const uint16_t*)v);
+      break;
     default:
       hipLaunchKernelGGL(k_append_fp8, grid, dim3(64), 0, s, cv, layer, seqs,
                          (const uint16_t*)k, (const uint16_t*)v);
@@ -353,6 +494,10 @@ hipError_t launch_write(const CacheView& cv, int layer, int n, const int32_t* se
       hipLaunchKernelGGL(k_write_copy<uint16_t>, grid, dim3(256), 0, s, cv, layer, seqs, start, T,
                          (const uint16_t*)k, (const uint16_t*)v);
       break;
+    case KVC_INT4:
+      hipLaunchKernelGGL(k_write_int4, grid, dim3(256), 0, s, cv, layer, seqs, start, T,
+                         (const uint16_t*)k, (const uint16_t*)v);
+      break;
     default:
       hipLaunchKernelGGL(k_write_fp8, grid, dim3(256), 0, s, cv, layer, seqs, start, T,
                          (const uint16_t*)k, (const uint16_t*)v);
@@ -364,12 +509,16 @@ hipError_t launch_gather(const CacheView& cv, int layer, int seq, int start, int
                          void* k_out, void* v_out, hipStream_t s) {
   int64_t total = (int64_t)count * cv.n_kv * cv.d;
   int grid = (int)std::min<int64_t>((total + 255) / 256, 8192);
-  switch (elem_bytes(cv.dtype)) {
+  switch (storage_bits(cv.dtype)) {
     case 4:
+      hipLaunchKernelGGL(k_gather_int4, dim3(grid), dim3(256), 0, s, cv, layer, seq, start,
+                         count, (uint8_t*)k_out, (uint8_t*)v_out);
+      break;
+    case 32:
       hipLaunchKernelGGL(k_gather<uint32_t>, dim3(grid), dim3(256), 0, s, cv, layer, seq, start,
                          count, (uint32_t*)k_out, (uint32_t*)v_out);
       break;
-    case 2:
+    case 16:
       hipLaunchKernelGGL(k_gather<uint16_t>, dim3(grid), dim3(256), 0, s, cv, layer, seq, start,
                          count, (uint16_t*)k_out, (uint16_t*)v_out);
       break;

@@ -234,7 +234,8 @@ hipError_t run_valu_d(const CacheView& cv, int layer, int n, const int32_t* seqs
     case KVC_F32: return run_valu<float, float, D>(cv, layer, n, seqs, q, out, sl2, p, ws, st);
     case KVC_F16: return run_valu<_Float16, _Float16, D>(cv, layer, n, seqs, q, out, sl2, p, ws, st);
     case KVC_BF16: return run_valu<BF16, BF16, D>(cv, layer, n, seqs, q, out, sl2, p, ws, st);
-    default: return run_valu<uint8_t, BF16, D>(cv, layer, n, seqs, q, out, sl2, p, ws, st);
+    case KVC_FP8_E4M3FN: return run_valu<uint8_t, BF16, D>(cv, layer, n, seqs, q, out, sl2, p, ws, st);
+    default: return hipErrorInvalidValue;                // int4 runs on the matrix cores only
   }
 }
 

@@ -75,7 +75,7 @@ int check_config(const kvc_config* c) {
   if (c->n_layers < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->n_blocks < 1 ||
       c->max_seqs < 1 || c->max_blocks_per_seq < 1)
     return fail(KVC_E_INVAL, "config counts must be positive");
-  if (c->kv_dtype < KVC_F32 || c->kv_dtype > KVC_FP8_E4M3FN)
+  if (c->kv_dtype < KVC_F32 || c->kv_dtype > KVC_INT4)
     return fail(KVC_E_INVAL, "unknown kv_dtype");
   if (c->block_size != kBlock) return fail(KVC_E_UNSUPPORTED, "block_size must be 16");
   if (c->d_head != 64 && c->d_head != 128) return fail(KVC_E_UNSUPPORTED, "d_head must be 64 or 128");
@@ -87,8 +87,7 @@ int check_config(const kvc_config* c) {
 }
 
 uint64_t pool_bytes(const kvc_config* c) {
-  return (uint64_t)c->n_layers * c->n_blocks * c->n_kv_heads * kBlock * c->d_head *
-         elem_bytes(c->kv_dtype);
+  return (uint64_t)c->n_layers * c->n_blocks * c->n_kv_heads * slab_bytes(c->kv_dtype, c->d_head);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -202,7 +201,7 @@ int kvc_bytes_per_token(const kvc_config* cfg, uint64_t* out) {
   int r = check_config(cfg);
   if (r) return r;
   if (!out) return fail(KVC_E_INVAL, "out is NULL");
-  *out = 2ull * cfg->n_layers * cfg->n_kv_heads * cfg->d_head * elem_bytes(cfg->kv_dtype);
+  *out = 2ull * cfg->n_layers * cfg->n_kv_heads * cfg->d_head * storage_bits(cfg->kv_dtype) / 8;
   return KVC_OK;
 }
 
@@ -212,7 +211,7 @@ int kvc_required_sizes(const kvc_config* cfg, kvc_sizes* out) {
   if (!out) return fail(KVC_E_INVAL, "out is NULL");
   out->k_pool = out->v_pool = pool_bytes(cfg);
   uint64_t sc = (uint64_t)cfg->n_layers * cfg->n_blocks * cfg->n_kv_heads * sizeof(float);
-  out->k_scale = out->v_scale = cfg->kv_dtype == KVC_FP8_E4M3FN ? sc : 0;
+  out->k_scale = out->v_scale = has_scales(cfg->kv_dtype) ? sc : 0;
   out->block_table = (uint64_t)cfg->max_seqs * cfg->max_blocks_per_seq * sizeof(int32_t);
   out->seq_len = (uint64_t)cfg->max_seqs * sizeof(int32_t);
   return KVC_OK;
@@ -226,8 +225,8 @@ int kvc_create(const kvc_config* cfg, const kvc_buffers* dev, hipStream_t stream
   if (dev) {
     if (!dev->k_pool || !dev->v_pool || !dev->block_table || !dev->seq_len)
       return fail(KVC_E_INVAL, "device buffer is NULL");
-    if (cfg->kv_dtype == KVC_FP8_E4M3FN && (!dev->k_scale || !dev->v_scale))
-      return fail(KVC_E_INVAL, "fp8 cache needs k_scale and v_scale");
+    if (has_scales(cfg->kv_dtype) && (!dev->k_scale || !dev->v_scale))
+      return fail(KVC_E_INVAL, "fp8 and int4 caches need k_scale and v_scale");
     if (!aligned16(dev->k_pool) || !aligned16(dev->v_pool))
       return fail(KVC_E_INVAL, "pools must be 16-byte aligned");
   }
@@ -501,7 +500,7 @@ namespace {
 int check_window(const kvc_cache* c, int32_t window, int32_t sinks) {
   if (window < 0 || sinks < 0) return fail(KVC_E_INVAL, "window and sinks must be >= 0");
   if (window > 0 && c->cfg.kv_dtype == KVC_F32)
-    return fail(KVC_E_UNSUPPORTED, "sliding windows need a bf16, f16 or fp8 cache");
+    return fail(KVC_E_UNSUPPORTED, "sliding windows need a bf16, f16, fp8 or int4 cache");
   return KVC_OK;
 }
 }  // namespace

@@ -15,8 +15,8 @@ constexpr int kTableUpdateMax = 240; // (index, value) pairs carried per update 
 struct CacheView {
   void* k;            // k_pool
   void* v;            // v_pool
-  float* ks;          // k_scale (fp8 only)
-  float* vs;          // v_scale (fp8 only)
+  float* ks;          // k_scale (fp8 and int4 only)
+  float* vs;          // v_scale (fp8 and int4 only)
   int32_t* bt;        // block_table [max_seqs][max_bps]
   int32_t* len;       // seq_len [max_seqs]
   int32_t n_layers, n_q, n_kv, d, n_blocks, max_seqs, max_bps;
@@ -33,7 +33,7 @@ struct TableUpdate {
 };
 
 // Copy-on-write block copies: block src -> dst, every layer, K and V slabs of
-// all kv heads and (fp8) their scales.
+// all kv heads and (fp8, int4) their scales.
 constexpr int kCopyMax = 120;
 struct BlockCopy {
   int32_t n;
@@ -60,10 +60,17 @@ struct DecodePlan {
   uint64_t ws_bytes;  // workspace bytes the call needs
 };
 
-__host__ __device__ inline int elem_bytes(int dtype) {
-  return dtype == KVC_F32 ? 4 : dtype == KVC_FP8_E4M3FN ? 1 : 2;
+__host__ __device__ inline int storage_bits(int dtype) {
+  return dtype == KVC_F32 ? 32 : dtype == KVC_FP8_E4M3FN ? 8 : dtype == KVC_INT4 ? 4 : 16;
 }
-inline int io_dtype(int dtype) { return dtype == KVC_FP8_E4M3FN ? KVC_BF16 : dtype; }
+// Bytes of one (block, kv head) slab of K or V: 16 rows of d elements.
+__host__ __device__ inline int64_t slab_bytes(int dtype, int d) {
+  return (int64_t)kBlock * d * storage_bits(dtype) / 8;
+}
+__host__ __device__ inline bool has_scales(int dtype) {
+  return dtype == KVC_FP8_E4M3FN || dtype == KVC_INT4;
+}
+inline int io_dtype(int dtype) { return has_scales(dtype) ? KVC_BF16 : dtype; }
 
 DecodePlan make_decode_plan(const CacheView& cv, int32_t n, int32_t max_len, int32_t num_splits,
                             int32_t cu_count);

@@ -1,4 +1,5 @@
-// Decode attention on the matrix cores (bf16 / fp16 / fp8 caches, d 64 or 128).
+// Decode attention on the matrix cores (bf16 / fp16 / fp8 / int4 caches, d 64
+// or 128).
 //
 // Work list.  The unit of work is 32 tokens (two 16-token blocks) of one
 // (sequence, kv-head group) segment, where a group is up to 16 query heads
@@ -37,6 +38,17 @@
 // value); the block's K scale multiplies its scores and its V scale the
 // probabilities before they are rounded to bf16; the running sum l uses the
 // unscaled probabilities.
+//
+// int4: a dword of 8 codes becomes 8 bf16 operands with two bit operations
+// per pair: the sign bit of every nibble is flipped (offset binary, n = c + 8)
+// and each nibble is placed in the low mantissa bits of 128.0, giving the
+// exact bf16 value c + 136.  The operands therefore carry a constant offset
+// of 136, removed after the products: the scores lose 136 * sum(q) (per
+// query row, computed once per segment) and the output loses 136 * sum of
+// the rounded probabilities fed to the PV products (accumulated beside O
+// with the same rescaling).  The conversion pairs nibbles k and k+4, so the
+// reduction indices come in the order 0,4,1,5,2,6,3,7; the query operand and
+// the probability operand are permuted to match.
 #include <hip/hip_runtime.h>
 
 #include "common.h"
@@ -50,7 +62,7 @@ typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
-enum { KV_BF16 = 0, KV_F16 = 1, KV_FP8 = 2 };
+enum { KV_BF16 = 0, KV_F16 = 1, KV_FP8 = 2, KV_INT4 = 3 };
 
 template <int KV> struct Op { typedef bf16x8 T; };
 template <> struct Op<KV_F16> { typedef f16x8 T; };
@@ -74,6 +86,41 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
   return r;
 }
 
+// 8 int4 codes (code k in nibble k of x, two's complement) -> 8 bf16 holding
+// code + 136 exactly, in the order of codes 0,4,1,5,2,6,3,7.
+constexpr float kInt4Offset = 136.0f;
+// The sign flip and the exponent bits are one XOR with 0x4308 per half
+// (bits disjoint from the masked nibble except bit 3, which it flips), so a
+// pair costs a shift and one three-input bit operation.
+__device__ __forceinline__ bf16x8 int4x8_to_bf16_off(uint32_t x) {
+  const uint32_t m = 0x000F000Fu, e = 0x43084308u;
+  uint4 r;
+  r.x = (x & m) ^ e;
+  r.y = ((x >> 4) & m) ^ e;
+  r.z = ((x >> 8) & m) ^ e;
+  r.w = ((x >> 12) & m) ^ e;
+  return __builtin_bit_cast(bf16x8, r);
+}
+// Dword i of a uint4 (i a compile-time constant after unrolling).
+__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+// 8 bf16 (a dword per pair, value k at half k) reordered to 0,4,1,5,2,6,3,7.
+__device__ __forceinline__ uint4 interleave_halves(uint4 a) {
+  return make_uint4((a.x & 0xFFFFu) | (a.z << 16), (a.x >> 16) | (a.z & 0xFFFF0000u),
+                    (a.y & 0xFFFFu) | (a.w << 16), (a.y >> 16) | (a.w & 0xFFFF0000u));
+}
+__device__ __forceinline__ float sum8_bf16(bf16x8 a) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bf16x2 t = {a[2 * j], a[2 * j + 1]};
+    s = __builtin_amdgcn_fdot2_f32_bf16(t, one, s, false);
+  }
+  return s;
+}
+
 template <typename T> __device__ __forceinline__ T pack8(const float* p);
 template <> __device__ __forceinline__ bf16x8 pack8<bf16x8>(const float* p) {
   bf16x8 r;
@@ -90,8 +137,10 @@ template <> __device__ __forceinline__ f16x8 pack8<f16x8>(const float* p) {
 
 // Head-dimension offset of the 8 reduction indices of k-step ks, lane group g.
 // 16-bit data: 8 consecutive values per k-step.  fp8: one 16-byte load covers
-// k-steps 2a and 2a+1.
-template <int KV> __device__ __forceinline__ int dmap(int ks, int g) {
+// k-steps 2a and 2a+1.  int4: one load of D/8 bytes covers every k-step
+// (dword ks of it), so lane group g holds dims D/4*g .. D/4*g + D/4 - 1.
+template <int KV, int D> __device__ __forceinline__ int dmap(int ks, int g) {
+  if (KV == KV_INT4) return (D / 4) * g + 8 * ks;
   if (KV == KV_FP8) return 64 * (ks >> 1) + 16 * g + 8 * (ks & 1);
   return 32 * ks + 8 * g;
 }
@@ -108,11 +157,20 @@ __device__ __forceinline__ int tok_slot(int t, int r) { return 8 * ((r >> 2) & 1
 template <int KV, int D> struct Unit {
   static constexpr int KS = D / 32;                    // k-steps of QK^T
   static constexpr int DT = D / 16;                    // 16-row tiles of O^T
-  static constexpr int KL = KV == KV_FP8 ? KS / 2 : KS;  // 16-byte K loads per tile
+  // 16-byte K loads per tile (int4: one load of D/8 bytes)
+  static constexpr int KL = KV == KV_FP8 ? KS / 2 : KV == KV_INT4 ? 1 : KS;
+  // V registers: fp8 two 8-byte loads per uint4, int4 four 4-byte loads
+  static constexpr int VL = KV == KV_FP8 ? DT / 2 : KV == KV_INT4 ? DT / 4 : DT;
   uint4 k[2][KL];
-  uint4 v[KV == KV_FP8 ? DT / 2 : DT];                 // fp8: 8-byte loads, two per uint4
+  uint4 v[VL];
   int64_t sidx[2];                                     // scale index of each block
 };
+
+// Units a wave keeps loaded (ring depth): the smaller int4 and fp8 units
+// need more of them in flight to cover the HBM latency.
+template <int KV> struct DecodeDepth { static constexpr int value = 2; };
+template <> struct DecodeDepth<KV_FP8> { static constexpr int value = 3; };
+template <> struct DecodeDepth<KV_INT4> { static constexpr int value = 4; };
 
 // Workspace of one (sub-)batch: O [slots][16][D] f32, m [slots][16],
 // l [slots][16], then the batch's unit prefix sums [nb+1] (int64) and unit
@@ -126,6 +184,7 @@ struct WorkWs {
 };
 
 constexpr int kUnit = 32;   // tokens per work unit
+constexpr float kStale = 8.0f;   // lazy-rescale threshold of the running max (log2 units)
 
 // Units of one segment that a query at position L-1 can see.  Without a
 // window: all ceil(L/32) units.  With a window w: the units holding sink
@@ -178,7 +237,9 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
   typedef typename Op<KV>::T OpT;
   typedef Unit<KV, D> U;
   constexpr int KS = U::KS, DT = U::DT, KL = U::KL;
-  constexpr int EB = KV == KV_FP8 ? 1 : 2;
+  constexpr int NB = DecodeDepth<KV>::value;
+  constexpr int EB = KV == KV_FP8 ? 1 : 2;            // bytes per element (not int4)
+  constexpr int64_t SB = KV == KV_INT4 ? kBlock * D / 2 : kBlock * D * EB;   // slab bytes
   __shared__ int64_t s_units[kMaxBatch + 1];
   __shared__ int32_t s_counts[kMaxBatch];
   __shared__ int64_t s_wsum[4];
@@ -248,7 +309,6 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
 
   const uint8_t* kpool = (const uint8_t*)cv.k;
   const uint8_t* vpool = (const uint8_t*)cv.v;
-  const int64_t slab_bytes = (int64_t)kBlock * D * EB;
   const int64_t layer_blocks = (int64_t)layer * cv.n_blocks;
 
   while (u < u1) {
@@ -273,15 +333,26 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
       const uint16_t* qr = q + ((int64_t)b * cv.n_q + kvh * G + (qrow ? qi : 0)) * D;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        uint4 raw = qrow ? *(const uint4*)(qr + dmap<KV>(ks, g)) : make_uint4(0, 0, 0, 0);
+        uint4 raw = qrow ? *(const uint4*)(qr + dmap<KV, D>(ks, g)) : make_uint4(0, 0, 0, 0);
+        if (KV == KV_INT4) raw = interleave_halves(raw);
         qop[ks] = __builtin_bit_cast(OpT, raw);
       }
+    }
+    // int4: -136 * sum of the query row's values (the K operands' offset)
+    float qoff = 0.f;
+    if (KV == KV_INT4) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qoff += sum8_bf16(__builtin_bit_cast(bf16x8, qop[ks]));
+      qoff += __shfl_xor(qoff, 16, 64);
+      qoff += __shfl_xor(qoff, 32, 64);
+      qoff *= -kInt4Offset;
     }
 
     f32x4 o[DT];
 #pragma unroll
     for (int i = 0; i < DT; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, lpart = 0.f;
+    float pvs = 0.f;                                  // int4: sum of the PV probabilities
     bool bad = false;
     const int32_t* btrow = cv.bt + (int64_t)seq * cv.max_bps;
     const int last_blk = (L - 1) / kBlock;
@@ -299,28 +370,50 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
           x = 0;
         }
         B.sidx[i] = (layer_blocks + x) * cv.n_kv + kvh;
-        sbase[i] = B.sidx[i] * slab_bytes;
+        sbase[i] = B.sidx[i] * SB;
       }
       const uint8_t* krow = kpool + (tok_block(r16) ? sbase[1] : sbase[0]);
+      if constexpr (KV == KV_INT4) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int a = 0; a < KL; ++a) {
-          const int off = KV == KV_FP8 ? 64 * a + 16 * g : 2 * dmap<KV>(a, g);
-          B.k[t][a] = *(const uint4*)(krow + (int64_t)tok_slot(t, r16) * D * EB + off);
+        for (int t = 0; t < 2; ++t) {
+          const uint8_t* kp = krow + tok_slot(t, r16) * (D / 2) + (D / 8) * g;
+          if (D == 128) {
+            B.k[t][0] = *(const uint4*)kp;
+          } else {
+            const uint2 x = *(const uint2*)kp;
+            B.k[t][0] = make_uint4(x.x, x.y, 0u, 0u);
+          }
         }
-      const uint8_t* vslab = vpool + ((g >> 1) ? sbase[1] : sbase[0]) + 8 * (g & 1) * EB;
-      if (KV == KV_FP8) {
+        // V column j = 16 dt + r16: tokens 8 (g & 1) .. +7 of block g >> 1
+        // are the dword at byte 4 (g & 1) of the column's 8 bytes.
+        const uint8_t* vcol = vpool + ((g >> 1) ? sbase[1] : sbase[0]) + 4 * (g & 1);
+        uint32_t w[DT];
 #pragma unroll
-        for (int dt = 0; dt < DT; dt += 2) {
-          const uint2 lo = *(const uint2*)(vslab + (16 * dt + r16) * kBlock);
-          const uint2 hi = *(const uint2*)(vslab + (16 * (dt + 1) + r16) * kBlock);
-          B.v[dt / 2] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        }
+        for (int dt = 0; dt < DT; ++dt) w[dt] = *(const uint32_t*)(vcol + (16 * dt + r16) * 8);
+#pragma unroll
+        for (int i = 0; i < DT / 4; ++i)
+          B.v[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
       } else {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          B.v[dt] = *(const uint4*)(vslab + 2 * (16 * dt + r16) * kBlock);
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int a = 0; a < KL; ++a) {
+            const int off = KV == KV_FP8 ? 64 * a + 16 * g : 2 * dmap<KV, D>(a, g);
+            B.k[t][a] = *(const uint4*)(krow + (int64_t)tok_slot(t, r16) * D * EB + off);
+          }
+        const uint8_t* vslab = vpool + ((g >> 1) ? sbase[1] : sbase[0]) + 8 * (g & 1) * EB;
+        if constexpr (KV == KV_FP8) {
+#pragma unroll
+          for (int dt = 0; dt < DT; dt += 2) {
+            const uint2 lo = *(const uint2*)(vslab + (16 * dt + r16) * kBlock);
+            const uint2 hi = *(const uint2*)(vslab + (16 * (dt + 1) + r16) * kBlock);
+            B.v[dt / 2] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          }
+        } else {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            B.v[dt] = *(const uint4*)(vslab + 2 * (16 * dt + r16) * kBlock);
+        }
       }
     };
 
@@ -339,7 +432,11 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
         sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int a = 0; a < KL; ++a) {
-          if (KV == KV_FP8) {
+          if constexpr (KV == KV_INT4) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+              sacc[t] = mfma(int4x8_to_bf16_off(word(B.k[t][0], ks)), qop[ks], sacc[t]);
+          } else if constexpr (KV == KV_FP8) {
             sacc[t] = mfma(__builtin_bit_cast(OpT, fp8x8_to_bf16(B.k[t][a].x, B.k[t][a].y)),
                            qop[2 * a], sacc[t]);
             sacc[t] = mfma(__builtin_bit_cast(OpT, fp8x8_to_bf16(B.k[t][a].z, B.k[t][a].w)),
@@ -352,92 +449,124 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
       // ---- online softmax (this lane's S^T column: query r16; its values
       // are tokens 16*(g>>1) + 8*(g&1) + 4t + i of the unit)
       float ksc = 1.f, vsc = 1.f;
-      if (KV == KV_FP8) {
+      if (KV == KV_FP8 || KV == KV_INT4) {
         const int64_t si = (g >> 1) ? B.sidx[1] : B.sidx[0];
         ksc = cv.ks[si];
         vsc = cv.vs[si];
       }
       const int pos0 = 16 * (g >> 1) + 8 * (g & 1);
       float p[2][4];
-      float cmax = -INFINITY;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float x = sacc[t][i] * (sl2 * ksc);
-          if (tail && pos0 + 4 * t + i >= nvalid) x = -INFINITY;
-          if (wedge) {
+        for (int i = 0; i < 4; ++i)
+          p[t][i] = KV == KV_INT4 ? fmaf(sacc[t][i], sl2 * ksc, qoff * (sl2 * ksc))
+                                  : sacc[t][i] * (sl2 * ksc);
+      if (tail || wedge) {                            // wave-uniform: masked units only
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
             const int pos = c * kUnit + pos0 + 4 * t + i;
-            if (pos < wlo && pos >= sinks) x = -INFINITY;
+            if (pos0 + 4 * t + i >= nvalid || (pos < wlo && pos >= sinks)) p[t][i] = -INFINITY;
           }
-          p[t][i] = x;
-          cmax = fmaxf(cmax, x);
-        }
+      }
+      float cmax = fmaxf(fmaxf(fmaxf(p[0][0], p[0][1]), fmaxf(p[0][2], p[0][3])),
+                         fmaxf(fmaxf(p[1][0], p[1][1]), fmaxf(p[1][2], p[1][3])));
       cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
       cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-      const float m_new = fmaxf(m, cmax);
-      const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_new);
+      // Lazy rescale: the running max m moves only when a row's new max
+      // exceeds it by more than kStale (log2 units), so most units skip the
+      // rescale of O; probabilities stay below 2^kStale.  (m, l, O) remain a
+      // consistent triple for the merge whatever m is.
+      if (__any(cmax > m + kStale)) {
+        const float m_new = fmaxf(m, cmax);
+        const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_new);
+        m = m_new;
+        lpart *= alpha;
+        pvs *= alpha;
+#pragma unroll
+        for (int i = 0; i < DT; ++i) o[i] *= alpha;
+      }
       float psum = 0.f, pv[8];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float e = __builtin_amdgcn_exp2f(p[t][i] - m_new);
+          const float e = __builtin_amdgcn_exp2f(p[t][i] - m);
           psum += e;
           pv[4 * t + i] = e * vsc;
         }
-      lpart = lpart * alpha + psum;
-      m = m_new;
-#pragma unroll
-      for (int i = 0; i < DT; ++i) o[i] *= alpha;
+      lpart += psum;
       // ---- O^T += V^T P^T over the unit's 32 tokens; in a sequence's last
       // unit, V slots past its end are zeroed (they may hold stale or
-      // poisoned bytes, and 0 * NaN would poison O)
-      const OpT pop = pack8<OpT>(pv);
-      const int nok = tail ? nvalid - pos0 : 8;       // valid slots among the lane's 8
-      uint32_t keep[4];
+      // poisoned bytes, and 0 * NaN would poison O).  int4 codes are always
+      // finite, so there the zero probabilities suffice.
+      if constexpr (KV == KV_INT4) {
+        const float pvp[8] = {pv[0], pv[4], pv[1], pv[5], pv[2], pv[6], pv[3], pv[7]};
+        const bf16x8 pop = pack8<bf16x8>(pvp);
+        pvs += sum8_bf16(pop);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (KV == KV_FP8) {
-          uint32_t mk = 0;
+        for (int dt = 0; dt < DT; ++dt)
+          o[dt] = mfma(int4x8_to_bf16_off(word(B.v[dt / 4], dt & 3)), pop, o[dt]);
+      } else {
+        const OpT pop = pack8<OpT>(pv);
+        const int nok = tail ? nvalid - pos0 : 8;       // valid slots among the lane's 8
+        uint32_t keep[4];
 #pragma unroll
-          for (int y = 0; y < 4; ++y) mk |= ((4 * (e & 1) + y) < nok ? 0xFFu : 0u) << (8 * y);
-          keep[e] = mk;
-        } else {
-          keep[e] = (2 * e < nok ? 0xFFFFu : 0u) | (2 * e + 1 < nok ? 0xFFFF0000u : 0u);
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (KV == KV_FP8) {
+            uint32_t mk = 0;
+#pragma unroll
+            for (int y = 0; y < 4; ++y) mk |= ((4 * (e & 1) + y) < nok ? 0xFFu : 0u) << (8 * y);
+            keep[e] = mk;
+          } else {
+            keep[e] = (2 * e < nok ? 0xFFFFu : 0u) | (2 * e + 1 < nok ? 0xFFFF0000u : 0u);
+          }
         }
-      }
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        OpT vop;
-        if (KV == KV_FP8) {
-          const uint4 w4 = B.v[dt / 2];
-          const uint32_t lo = ((dt & 1) ? w4.z : w4.x) & keep[0];
-          const uint32_t hi = ((dt & 1) ? w4.w : w4.y) & keep[1];
-          vop = __builtin_bit_cast(OpT, fp8x8_to_bf16(lo, hi));
-        } else {
-          const uint4 raw = B.v[dt];
-          vop = __builtin_bit_cast(OpT, make_uint4(raw.x & keep[0], raw.y & keep[1],
-                                                   raw.z & keep[2], raw.w & keep[3]));
+        for (int dt = 0; dt < DT; ++dt) {
+          OpT vop;
+          if constexpr (KV == KV_FP8) {
+            const uint4 w4 = B.v[dt / 2];
+            const uint32_t lo = ((dt & 1) ? w4.z : w4.x) & keep[0];
+            const uint32_t hi = ((dt & 1) ? w4.w : w4.y) & keep[1];
+            vop = __builtin_bit_cast(OpT, fp8x8_to_bf16(lo, hi));
+          } else {
+            const uint4 raw = B.v[dt];
+            vop = __builtin_bit_cast(OpT, make_uint4(raw.x & keep[0], raw.y & keep[1],
+                                                     raw.z & keep[2], raw.w & keep[3]));
+          }
+          o[dt] = mfma(vop, pop, o[dt]);
         }
-        o[dt] = mfma(vop, pop, o[dt]);
       }
     };
 
-    // Two buffers, alternating: unit c+1's loads go out before unit c is
-    // computed.
-    U A, Bb;
-    issue(A, c0);
-    for (int c = c0; c < c1; c += 2) {
-      if (c + 1 < c1) issue(Bb, c + 1);
-      compute(A, c);
-      if (c + 2 < c1) issue(A, c + 2);
-      if (c + 1 < c1) compute(Bb, c + 1);
+    // NB register buffers in a ring: the loads of unit c+NB-1 go out before
+    // unit c is computed, so NB-1 units are in flight while the wave computes.
+    U buf[NB];
+#pragma unroll
+    for (int j = 0; j < NB - 1; ++j)
+      if (c0 + j < c1) issue(buf[j], c0 + j);
+    for (int c = c0; c < c1; c += NB) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if (c + j + NB - 1 < c1) issue(buf[(j + NB - 1) % NB], c + j + NB - 1);
+        if (c + j < c1) compute(buf[j], c + j);
+      }
     }
 
     // ---- piece done: (m, l, O) of this wave's query rows to slot (segment + wave)
     float l = lpart + __shfl_xor(lpart, 16, 64);
     l += __shfl_xor(l, 32, 64);
+    if constexpr (KV == KV_INT4) {                   // remove the V operands' offset
+      float ps = pvs + __shfl_xor(pvs, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[dt][i] = fmaf(-kInt4Offset, ps, o[dt][i]);
+    }
     if (bad) l = __builtin_nanf("");
     const int64_t slot = (int64_t)b * nkvg + kvg + gw;
     if (qrow) {
@@ -599,10 +728,12 @@ int work_list_waves_per_cu(const CacheView& cv) {
   if (cv.d == 128) {
     if (cv.dtype == KVC_BF16) return occupancy_waves<KV_BF16, 128>();
     if (cv.dtype == KVC_F16) return occupancy_waves<KV_F16, 128>();
+    if (cv.dtype == KVC_INT4) return occupancy_waves<KV_INT4, 128>();
     return occupancy_waves<KV_FP8, 128>();
   }
   if (cv.dtype == KVC_BF16) return occupancy_waves<KV_BF16, 64>();
   if (cv.dtype == KVC_F16) return occupancy_waves<KV_F16, 64>();
+  if (cv.dtype == KVC_INT4) return occupancy_waves<KV_INT4, 64>();
   return occupancy_waves<KV_FP8, 64>();
 }
 
@@ -614,10 +745,12 @@ hipError_t launch_decode_mfma(const CacheView& cv, int layer, int n, const int32
   if (cv.d == 128) {
     if (cv.dtype == KVC_BF16) return run<KV_BF16, 128>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st);
     if (cv.dtype == KVC_F16) return run<KV_F16, 128>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st);
+    if (cv.dtype == KVC_INT4) return run<KV_INT4, 128>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st);
     return run<KV_FP8, 128>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st);
   }
   if (cv.dtype == KVC_BF16) return run<KV_BF16, 64>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st);
   if (cv.dtype == KVC_F16) return run<KV_F16, 64>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st);
+  if (cv.dtype == KVC_INT4) return run<KV_INT4, 64>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st);
   return run<KV_FP8, 64>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st);
 }
 

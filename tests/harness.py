@@ -8,6 +8,7 @@ import torch
 
 import kv_cache_flashattention_amd as kv
 from oracle import attention as A
+from oracle.codecs import int4_pack
 from oracle.paged import PagedCacheModel
 
 # Attention tolerances: max |y - r| <= 2e-2 and, per output row (one token
@@ -28,6 +29,34 @@ def bits(t):
 
 def f64(t):
     return t.detach().cpu().double().numpy()
+
+
+SCALED = ("fp8", "int4")
+
+
+def stored_pools(m):
+    """The model's pools as the library lays them out (int4: two codes per byte)."""
+    return m.packed_pools() if m.dtype == "int4" else (m.K, m.V)
+
+
+def pools_match(c, m):
+    """GPU pools (and scales) equal the model's, byte for byte."""
+    K, V = stored_pools(m)
+    ok = np.array_equal(bits(c.k_pool), K) and np.array_equal(bits(c.v_pool), V)
+    if m.dtype in SCALED:
+        ok &= np.array_equal(bits(c.k_scale.view(torch.int32)).view(np.uint32),
+                             m.Ks.view(np.uint32))
+        ok &= np.array_equal(bits(c.v_scale.view(torch.int32)).view(np.uint32),
+                             m.Vs.view(np.uint32))
+    return bool(ok)
+
+
+def stored_rows(m, layer, seq, start=0, count=None):
+    """Rows of one sequence as kvc_gather returns them (int4: packed along d)."""
+    K, V = m.logical_raw(layer, seq, start, count)
+    if m.dtype == "int4":
+        return int4_pack(K, -1), int4_pack(V, -1)
+    return K, V
 
 
 # Mantissa bits of each output type: a correctly rounded output differs from
@@ -65,14 +94,14 @@ class Built:
 
     @property
     def io_name(self):
-        return {"bf16": "bf16", "f16": "f16", "fp8": "bf16", "f32": "f32"}[self.dt]
+        return {"bf16": "bf16", "f16": "f16", "fp8": "bf16", "int4": "bf16", "f32": "f32"}[self.dt]
 
     def __init__(self, w, n_layers=1, layer=0, poison=True, identity_tables=False):
         """Populate every sequence of workload w in `layer`: its first L-1
         rows by one bulk write, then a grow of every sequence by one token
         and one kv_append of the last row for all of them together."""
         self.w, self.layer = w, layer
-        dt = {"bf16": "bf16", "fp16": "f16", "fp8": "fp8", "f32": "f32"}[w.kv_dtype]
+        dt = {"bf16": "bf16", "fp16": "f16", "fp8": "fp8", "int4": "int4", "f32": "f32"}[w.kv_dtype]
         self.dt = dt
         L = w.lengths
         max_bps = int(w.blocks_per_seq.max()) + 1
@@ -116,24 +145,17 @@ class Built:
         torch.cuda.synchronize()
 
     def _mirror(self, layer, b, start, kt, vt):
-        if self.dt == "fp8":
+        if self.dt in SCALED:
             self.m.write_rows(layer, b, start, kt.float().cpu().numpy(), vt.float().cpu().numpy())
         else:
             self.m.write_rows(layer, b, start, bits(kt), bits(vt))
 
     def pools_equal(self):
-        ok = np.array_equal(bits(self.c.k_pool), self.m.K) and \
-            np.array_equal(bits(self.c.v_pool), self.m.V)
-        if self.dt == "fp8":
-            ok &= np.array_equal(bits(self.c.k_scale.view(torch.int32)).view(np.uint32),
-                                 self.m.Ks.view(np.uint32))
-            ok &= np.array_equal(bits(self.c.v_scale.view(torch.int32)).view(np.uint32),
-                                 self.m.Vs.view(np.uint32))
-        return bool(ok)
+        return pools_match(self.c, self.m)
 
     def oracle_decode(self, q_io, b=None):
         """Oracle decode rows for every sequence (or one) from the model's
-        stored values (dequantised for fp8)."""
+        stored values (dequantised for fp8 and int4)."""
         qd = f64(q_io)
         scale = 1 / math.sqrt(self.w.d)
         bs = range(self.w.batch) if b is None else [b]

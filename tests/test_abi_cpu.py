@@ -40,6 +40,8 @@ def test_bytes_per_token_through_the_abi():
     fp8 = kv.make_config(80, 64, 8, 128, 16, 1, 1, "fp8")
     f16 = kv.make_config(80, 64, 8, 128, 16, 1, 1, "f16")
     assert kv.bytes_per_token(f16) == 2 * kv.bytes_per_token(fp8)
+    i4 = kv.make_config(80, 64, 8, 128, 16, 1, 1, "int4")
+    assert kv.bytes_per_token(fp8) == 2 * kv.bytes_per_token(i4) == 80 * 8 * 128 * 2
 
 
 def test_required_sizes():
@@ -50,6 +52,17 @@ def test_required_sizes():
     assert s["block_table"] == 3 * 5 * 4 and s["seq_len"] == 3 * 4
     s = kv.required_sizes(kv.make_config(1, 4, 4, 128, 7, 2, 2, "bf16"))
     assert s["k_pool"] == 7 * 4 * 16 * 128 * 2 and s["k_scale"] == 0
+    s = kv.required_sizes(kv.make_config(2, 8, 2, 64, 10, 3, 5, "int4"))
+    assert s["k_pool"] == s["v_pool"] == 2 * 10 * 2 * 16 * 64 // 2
+    assert s["k_scale"] == s["v_scale"] == 2 * 10 * 2 * 4
+
+
+def test_unknown_dtype_rejected():
+    cfg = kv.make_config(1, 8, 2, 64, 4, 2, 4, "int4")
+    cfg.kv_dtype = 5
+    with pytest.raises(kv.KvcError) as e:
+        kv.required_sizes(cfg)
+    assert e.value.code == kv.KVC_E_INVAL
 
 
 @pytest.mark.parametrize("bad", [dict(d_head=96), dict(n_q_heads=6, n_kv_heads=4),

@@ -21,7 +21,7 @@ def populate(w, append_from=None):
     chunks), then one grow + kv_append of row L-1 for every sequence.  With
     append_from=P, rows P..L-2 are added one token at a time (grow +
     kv_append), the way a decode loop fills the cache."""
-    dt = {"bf16": "bf16", "fp16": "f16", "fp8": "fp8"}[w.kv_dtype]
+    dt = {"bf16": "bf16", "fp16": "f16", "fp8": "fp8", "int4": "int4"}[w.kv_dtype]
     io = kv.IO_TORCH[dt]
     max_bps = int(w.blocks_per_seq.max()) + 1
     c = kv.KvCache(1, w.n_q, w.n_kv, w.d, w.n_blocks + w.batch, w.batch, max_bps, dt)
@@ -101,7 +101,8 @@ def test_long_mha_decode_full_sampled_heads():
                        torch.from_numpy(kk).to(io).view(torch.int16))
 
 
-@pytest.mark.parametrize("name", ["llama70b_decode_bf16", "llama70b_decode_fp8"])
+@pytest.mark.parametrize("name", ["llama70b_decode_bf16", "llama70b_decode_fp8",
+                                  "llama70b_decode_int4"])
 def test_llama70b_decode_full_sampled(name):
     w = decode_workload(name)
     c, seqs, io = populate(w)
@@ -115,9 +116,10 @@ def test_llama70b_decode_full_sampled(name):
             Ks, Vs = source_rows(w, b, io, head=g)
             heads = list(range(g * G, (g + 1) * G))
             ref_src = np.array([A.attention(qd[b, h][None], Ks, Vs, scale)[0] for h in heads])
-            if w.kv_dtype == "fp8":
+            if w.kv_dtype in ("fp8", "int4"):
+                dt = w.kv_dtype
                 L = int(w.lengths[b])
-                m = PagedCacheModel(1, 1, w.d, "fp8", -(-L // 16) + 1, 1, -(-L // 16) + 1,
+                m = PagedCacheModel(1, 1, w.d, dt, -(-L // 16) + 1, 1, -(-L // 16) + 1,
                                     poison=False)
                 m.alloc(0, L - 1)
                 m.write_rows(0, 0, 0, Ks[:L - 1, None].astype(np.float32),
@@ -130,14 +132,14 @@ def test_llama70b_decode_full_sampled(name):
                                   for h in heads])
                 # kernel error: against the oracle on the values the cache holds
                 a, _ = errors(y[b, heads], ref_q, "bf16")
-                assert a <= FP8_ABS_TOL, f"fp8 kernel seq {b} kv {g}: abs {a:.3e}"
-                assert_close(y[b, heads], ref_q, what=f"fp8 kernel seq {b} kv {g}")
+                assert a <= FP8_ABS_TOL, f"{dt} kernel seq {b} kv {g}: abs {a:.3e}"
+                assert_close(y[b, heads], ref_q, what=f"{dt} kernel seq {b} kv {g}")
                 # end to end: never further from the unquantised rows than the
                 # format itself (the oracle on dequantised rows) plus 2e-2
                 fmt = np.abs(ref_q - ref_src)
                 dev = np.abs(y[b, heads] - ref_src)
                 assert np.all(dev <= fmt + 2e-2 + np.abs(ref_src) * 2.0 ** -8), \
-                    f"fp8 end-to-end seq {b} kv {g}: {dev.max():.3e} vs format {fmt.max():.3e}"
+                    f"{dt} end-to-end seq {b} kv {g}: {dev.max():.3e} vs format {fmt.max():.3e}"
             else:
                 assert_close(y[b, heads], ref_src, what=f"seq {b} kv {g}")
 

@@ -1,6 +1,6 @@
 """Prefix sharing with copy-on-write on the GPU: after shares, copies and
 appends, both pools equal the oracle model's byte for byte (poisoned slots,
-fp8 scales included), every sequence gathers its own rows, and decode of
+fp8 and int4 scales included), every sequence gathers its own rows, and decode of
 every sequence matches the oracle on its rows."""
 import math
 
@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import kv_cache_flashattention_amd as kv
-from harness import FP8_ABS_TOL, assert_close, bits, f64
+from harness import FP8_ABS_TOL, SCALED, assert_close, bits, f64, pools_match, stored_rows
 from oracle import attention as A
 from oracle.paged import PagedCacheModel
 
@@ -32,7 +32,7 @@ class Pair:
         return r(), r()
 
     def _mirror(self, seq, start, k, v):
-        if self.dt == "fp8":
+        if self.dt in SCALED:
             self.m.write_rows(0, seq, start, k.float().cpu().numpy(), v.float().cpu().numpy())
         else:
             self.m.write_rows(0, seq, start, bits(k), bits(v))
@@ -66,17 +66,10 @@ class Pair:
         self.write(seq, start, k, v)
 
     def pools_equal(self):
-        ok = np.array_equal(bits(self.c.k_pool), self.m.K) and \
-            np.array_equal(bits(self.c.v_pool), self.m.V)
-        if self.dt == "fp8":
-            ok &= np.array_equal(bits(self.c.k_scale.view(torch.int32)).view(np.uint32),
-                                 self.m.Ks.view(np.uint32))
-            ok &= np.array_equal(bits(self.c.v_scale.view(torch.int32)).view(np.uint32),
-                                 self.m.Vs.view(np.uint32))
-        return bool(ok)
+        return pools_match(self.c, self.m)
 
 
-@pytest.mark.parametrize("dt", ["bf16", "fp8", "f16"])
+@pytest.mark.parametrize("dt", ["bf16", "fp8", "f16", "int4"])
 def test_share_copy_on_write_append(dt):
     P = Pair(dt)
     perm = P.rng.permutation(24).astype(np.int32)
@@ -94,14 +87,14 @@ def test_share_copy_on_write_append(dt):
     assert P.pools_equal()
     for s in range(4):
         gk, gv = P.c.gather(0, s, 0, P.m.length[s])
-        mk, mv = P.m.logical_raw(0, s)
+        mk, mv = stored_rows(P.m, 0, s)
         assert np.array_equal(bits(gk), mk) and np.array_equal(bits(gv), mv)
     q = torch.from_numpy(P.rng.standard_normal((4, P.n_q, P.d), dtype=np.float32)).to(
-        torch.bfloat16 if dt == "fp8" else P.io).cuda()
+        P.io).cuda()
     out = P.c.attn_decode(0, torch.arange(4, dtype=torch.int32, device="cuda"), q)
     torch.cuda.synchronize()
     scale = 1 / math.sqrt(P.d)
-    io = "bf16" if dt == "fp8" else dt
+    io = "bf16" if dt in SCALED else dt
     for s in range(4):
         K, V = P.m.logical_values(0, s)
         ref = A.decode_attention(f64(q[s]), K, V, scale)

@@ -122,15 +122,15 @@ def decode_workload(name, small=False, seed=0):
     """The paged-decode workloads at full size, or shrunk for quick parity tests.
 
     name: 'llama8b_decode' (40 sequences, 32 q / 8 kv heads, d 128, bf16,
-    lengths uniform in [512, 4096]); 'llama70b_decode_bf16' / '_fp8' (8 x
-    32,768 tokens, 64 q / 8 kv heads, outliers); 'long_mha_decode' (one
+    lengths uniform in [512, 4096]); 'llama70b_decode_bf16' / '_fp8' / '_int4'
+    (8 x 32,768 tokens, 64 q / 8 kv heads, outliers); 'long_mha_decode' (one
     128,000-token sequence, 32 / 32 heads, fp16).
     """
     if name == "llama8b_decode":
         return DecodeWorkload(name, 40 if not small else 6, 32, 8, 128, "bf16",
                               (512, 4096) if not small else (1, 300), seed=seed)
-    if name in ("llama70b_decode_bf16", "llama70b_decode_fp8"):
-        dt = "bf16" if name.endswith("bf16") else "fp8"
+    if name in ("llama70b_decode_bf16", "llama70b_decode_fp8", "llama70b_decode_int4"):
+        dt = name.rsplit("_", 1)[1]
         return DecodeWorkload("llama70b_decode", 8 if not small else 3, 64, 8, 128, dt,
                               32768 if not small else 531, outliers=True, seed=seed)
     if name == "long_mha_decode":
