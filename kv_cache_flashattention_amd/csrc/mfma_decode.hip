@@ -163,14 +163,13 @@ template <int KV, int D> struct Unit {
   static constexpr int VL = KV == KV_FP8 ? DT / 2 : KV == KV_INT4 ? DT / 4 : DT;
   uint4 k[2][KL];
   uint4 v[VL];
-  int64_t sidx[2];                                     // scale index of each block
+  float ksc, vsc;                                      // fp8/int4: this lane's block scales
 };
 
-// Units a wave keeps loaded (ring depth): the smaller int4 and fp8 units
-// need more of them in flight to cover the HBM latency.
+// Units a wave keeps loaded (ring depth).  Deeper rings cost registers and
+// with them resident waves; on the 70B-shaped workloads a depth of 3 gained
+// nothing for fp8 and int4 and a depth of 4 lost 14% for int4.
 template <int KV> struct DecodeDepth { static constexpr int value = 2; };
-template <> struct DecodeDepth<KV_FP8> { static constexpr int value = 3; };
-template <> struct DecodeDepth<KV_INT4> { static constexpr int value = 4; };
 
 // Workspace of one (sub-)batch: O [slots][16][D] f32, m [slots][16],
 // l [slots][16], then the batch's unit prefix sums [nb+1] (int64) and unit
@@ -184,6 +183,7 @@ struct WorkWs {
 };
 
 constexpr int kUnit = 32;   // tokens per work unit
+constexpr int kTabUnits = 32;   // units per block-table chunk (64 lanes, two blocks each)
 constexpr float kStale = 8.0f;   // lazy-rescale threshold of the running max (log2 units)
 
 // Units of one segment that a query at position L-1 can see.  Without a
@@ -357,20 +357,55 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
     const int32_t* btrow = cv.bt + (int64_t)seq * cv.max_bps;
     const int last_blk = (L - 1) / kBlock;
 
-    // Issue every load of unit c into buffer B (table entries past the
-    // sequence's end are clamped to its last block; their tokens are masked).
-    auto issue = [&](U& B, int cs) {
-      const int c = umap.unit(cs);
-      int64_t sbase[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        int x = btrow[min(2 * c + i, last_blk)];
+    // Block table of the piece, 32 units at a time: lane l holds the block of
+    // unit tab0 + l/2, slot l&1 (entries past the sequence's end clamped to
+    // its last block, whose extra tokens are masked), and for fp8/int4 that
+    // block's scales.  Units then read their block ids with readlane, so the
+    // data loads do not wait on a table load and addresses are scalar.
+    constexpr bool SCALED = KV == KV_FP8 || KV == KV_INT4;
+    int tab = 0, tab0 = c0;
+    float tks = 1.f, tvs = 1.f;
+    auto load_tab = [&](int cs0) {
+      tab0 = cs0;
+      const int cs = cs0 + (lane >> 1);
+      int x = 0;
+      if (cs < c1) {
+        x = btrow[min(2 * umap.unit(cs) + (lane & 1), last_blk)];
         if (x < 0 || x >= cv.n_blocks) {
           bad = true;
           x = 0;
         }
-        B.sidx[i] = (layer_blocks + x) * cv.n_kv + kvh;
-        sbase[i] = B.sidx[i] * SB;
+      }
+      tab = x;
+      if constexpr (SCALED) {
+        const int64_t si = (layer_blocks + x) * cv.n_kv + kvh;
+        tks = cv.ks[si];
+        tvs = cv.vs[si];
+      }
+    };
+    load_tab(c0);
+
+    // Issue every load of unit cs into buffer B.
+    auto issue = [&](U& B, int cs) {
+      if (cs - tab0 >= kTabUnits) load_tab(cs);       // wave-uniform
+      const int j = 2 * (cs - tab0);
+      int64_t sbase[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int x = __builtin_amdgcn_readlane(tab, j + i);
+        sbase[i] = ((layer_blocks + x) * cv.n_kv + kvh) * SB;
+      }
+      if constexpr (SCALED) {
+        const float k0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                             __builtin_bit_cast(int, tks), j));
+        const float k1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                             __builtin_bit_cast(int, tks), j + 1));
+        const float v0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                             __builtin_bit_cast(int, tvs), j));
+        const float v1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                             __builtin_bit_cast(int, tvs), j + 1));
+        B.ksc = (g >> 1) ? k1 : k0;
+        B.vsc = (g >> 1) ? v1 : v0;
       }
       const uint8_t* krow = kpool + (tok_block(r16) ? sbase[1] : sbase[0]);
       if constexpr (KV == KV_INT4) {
@@ -449,10 +484,9 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
       // ---- online softmax (this lane's S^T column: query r16; its values
       // are tokens 16*(g>>1) + 8*(g&1) + 4t + i of the unit)
       float ksc = 1.f, vsc = 1.f;
-      if (KV == KV_FP8 || KV == KV_INT4) {
-        const int64_t si = (g >> 1) ? B.sidx[1] : B.sidx[0];
-        ksc = cv.ks[si];
-        vsc = cv.vs[si];
+      if constexpr (SCALED) {
+        ksc = B.ksc;
+        vsc = B.vsc;
       }
       const int pos0 = 16 * (g >> 1) + 8 * (g & 1);
       float p[2][4];
@@ -567,7 +601,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[dt][i] = fmaf(-kInt4Offset, ps, o[dt][i]);
     }
-    if (bad) l = __builtin_nanf("");
+    if (__any(bad)) l = __builtin_nanf("");
     const int64_t slot = (int64_t)b * nkvg + kvg + gw;
     if (qrow) {
       float* Orow = W_.O + (slot * 16 + r16) * D;
