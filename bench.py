@@ -6,8 +6,9 @@ Default workload: the Llama-3-8B-shaped decode step -- 40 sequences, 32 query
 and 8 kv heads of 128, bf16 cache in 16-token blocks behind shuffled block
 tables, context lengths uniform in [512, 4096].  One step is one pass of the
 decode hot path over that batch: grow every sequence by one token (host
-allocator + table update), kv_append of the new K/V rows, then attn_decode
-(split-context partials and their (m, l) merge).  The headline `value` is
+allocator + table update), then kvc_attn_decode_append: kv_append of the new
+K/V rows and attn_decode (split-context partials and their (m, l) merge) in
+one call, the append fused into the decode kernel for bf16 caches.  The headline `value` is
 the decode's algorithmic HBM bytes per step (K/V rows read through the
 tables, queries, outputs, table entries) divided by the wall-clock time per
 step.  The same JSON line carries a `prefill` object for the causal-prefill
@@ -15,7 +16,9 @@ workload (4 x 8,192 tokens, 32/8 heads of 128, bf16) and an `extend` object
 for chunked prefill (the last 512-token chunk of those prompts against the
 7,680 rows already cached), both in algorithmic TFLOP/s, and a
 `decode_window` object: the decode batch under a 1,024-row sliding window
-with 4 sink rows, in GB/s of the rows it can see.
+with 4 sink rows, in GB/s of the rows it can see; `prefix_share` (blocks and
+copy-on-write bytes of 40 sequences sharing a prompt) and `decode_int4` (the
+70B-shaped decode on an int4 cache).
 
 `roofline` is measured for the dominant call of each workload with HIP
 events recorded on the stream the library launches on: for decode, the same
@@ -201,10 +204,9 @@ def bench_decode(name, steps, warmup, torch, kv, with_cpu):
 
     def step(ev=None):
         c.seq_grow(seqs_host)
-        c.append(0, seqs, knew, vnew)
         if ev is not None:
             ev[0].record(stream)
-        c.attn_decode(0, seqs, q, out=out, ws=ws)
+        c.attn_decode_append(0, seqs, knew, vnew, q, out=out, ws=ws)
         if ev is not None:
             ev[1].record(stream)
 
@@ -254,7 +256,7 @@ def bench_decode(name, steps, warmup, torch, kv, with_cpu):
                      "kernel": "kvc_attn_decode (split partial + merge)",
                      "avg_call_us": kern_avg_s * 1e6, "bytes_per_call": per_call,
                      "cache_evicted_before_each_call": True,
-                     "avg_call_us_warm": warm_avg_s * 1e6},
+                     "avg_call_us_warm_with_append": warm_avg_s * 1e6},
         "shape": {"batch": w.batch, "n_q": w.n_q, "n_kv": w.n_kv, "d": w.d,
                   "kv_dtype": w.kv_dtype, "mean_len": float(np.mean(lens0 + 1))},
     }
@@ -502,7 +504,8 @@ def bench_prefix_share(torch, kv, n_seq=40, prompt=600, n_layers=32):
 
 DECODE_WORKLOADS = {
     "llama8b_decode": "40 sequences, 32 q / 8 kv heads, d 128, bf16 cache, 16-token blocks, "
-                      "shuffled tables, lengths uniform in [512, 4096]; grow + kv_append + decode",
+                      "shuffled tables, lengths uniform in [512, 4096]; step = grow + "
+                      "kvc_attn_decode_append (kv_append fused into the decode call)",
     "llama70b_decode_bf16": "8 x 32,768-token contexts, 64 q / 8 kv heads, d 128, bf16 cache, "
                             "1% outliers x8",
     "llama70b_decode_fp8": "8 x 32,768-token contexts, 64 q / 8 kv heads, d 128, fp8-e4m3 cache "

@@ -285,6 +285,22 @@ int kvc_attn_extend_window(kvc_cache* cache, int32_t layer, int32_t n, const int
                            int32_t T, const void* q_dev, void* out_dev, float scale,
                            int32_t window, int32_t sinks, hipStream_t stream);
 
+/* kv_append followed by attn_decode in one call (kvcache-7e2 KV cache
+ * section: the new token's K and V rows join the cache, then its query
+ * attends over every row of its sequence).  Same contract as kvc_append
+ * (call kvc_seq_grow first; k_new_dev, v_new_dev [n][n_kv_heads][d_head] in
+ * the io type, 16-byte aligned) and as kvc_attn_decode_window (window = 0:
+ * full attention).  Outputs and cache contents equal those of kvc_append
+ * then kvc_attn_decode_window.  For bf16 and f16 caches the row is stored
+ * and attended inside the decode kernel (one launch fewer); other caches run
+ * the append kernel first.  The workspace is sized by
+ * kvc_decode_workspace_bytes as for kvc_attn_decode. */
+int kvc_attn_decode_append(kvc_cache* cache, int32_t layer, int32_t n, const int32_t* seqs_dev,
+                           const void* k_new_dev, const void* v_new_dev, const void* q_dev,
+                           void* out_dev, float scale, int32_t window, int32_t sinks,
+                           int32_t num_splits, void* ws_dev, uint64_t ws_bytes,
+                           hipStream_t stream);
+
 /* Block-table gather: copy the stored bit patterns of positions start ..
  * start+count-1 of `seq` in logical order into k_out_dev, v_out_dev, each
  * [count][n_kv_heads][d_head] of the storage type (fp8: raw codes; int4:

@@ -83,6 +83,8 @@ _SIGS = {
                                ctypes.c_uint64, _P],
     "kvc_attn_prefill_window": [_P, _I, _I, _P, _I, _P, _P, _P, _P, ctypes.c_float, _I, _I, _P],
     "kvc_attn_extend_window": [_P, _I, _I, _P, _I, _P, _P, ctypes.c_float, _I, _I, _P],
+    "kvc_attn_decode_append": [_P, _I, _I, _P, _P, _P, _P, _P, ctypes.c_float, _I, _I, _I, _P,
+                               ctypes.c_uint64, _P],
     "kvc_gather": [_P, _I, _I, _I, _I, _P, _P, _P],
     "kvc_last_error": [],
 }
@@ -326,6 +328,25 @@ class KvCache:
             _check(lib().kvc_attn_decode(
                 self._h, layer, n, self._seqs(seqs), qp, op, ctypes.c_float(scale), num_splits,
                 wsp, wsb, _stream()))
+        return out
+
+    def attn_decode_append(self, layer, seqs, k, v, q, scale=None, num_splits=0, out=None,
+                           ws=None, window=0, sinks=0):
+        """kv_append of the newest rows k, v [n, n_kv, d] (after seq_grow),
+        then attn_decode, in one library call."""
+        n = seqs.numel()
+        scale = 1.0 / math.sqrt(self.d) if scale is None else scale
+        if out is None:
+            out = torch.empty((n, self.n_q, self.d), dtype=self.io_dtype, device=q.device)
+        if ws is None:
+            nb = self.decode_workspace_bytes(n, num_splits)
+            ws = torch.empty((max(nb, 16),), dtype=torch.uint8, device=q.device)
+        kp = self._io(k, (n, self.n_kv, self.d), "k")
+        vp = self._io(v, (n, self.n_kv, self.d), "v")
+        qp, op = self._io(q, (n, self.n_q, self.d), "q"), self._io(out, (n, self.n_q, self.d), "out")
+        _check(lib().kvc_attn_decode_append(
+            self._h, layer, n, self._seqs(seqs), kp, vp, qp, op, ctypes.c_float(scale), window,
+            sinks, num_splits, _ptr(ws), ws.numel() * ws.element_size(), _stream()))
         return out
 
     def gather(self, layer, seq, start, count):

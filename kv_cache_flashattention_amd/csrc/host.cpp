@@ -580,9 +580,11 @@ int kvc_attn_decode(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs,
                                 stream);
 }
 
-int kvc_attn_decode_window(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs,
-                           const void* q, void* out, float scale, int32_t window, int32_t sinks,
-                           int32_t num_splits, void* ws, uint64_t ws_bytes, hipStream_t stream) {
+namespace {
+int decode_impl(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs, const void* knew,
+                const void* vnew, const void* q, void* out, float scale, int32_t window,
+                int32_t sinks, int32_t num_splits, void* ws, uint64_t ws_bytes,
+                hipStream_t stream) {
   if (!c) return fail(KVC_E_INVAL, "cache is NULL");
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(KVC_E_INVAL, "scale must be finite and positive");
@@ -595,6 +597,8 @@ int kvc_attn_decode_window(kvc_cache* c, int32_t layer, int32_t n, const int32_t
   if (n == 0) return KVC_OK;
   if (!seqs || !q || !out) return fail(KVC_E_INVAL, "NULL device pointer");
   if (!aligned16(q) || !aligned16(out)) return fail(KVC_E_INVAL, "q/out must be 16-byte aligned");
+  if (knew && (!vnew || !aligned16(knew) || !aligned16(vnew)))
+    return fail(KVC_E_INVAL, "k_new/v_new must be non-NULL and 16-byte aligned");
   int32_t max_len = live_max_len(c);
   if (max_len <= 0) return fail(KVC_E_STATE, "no live sequence holds any token");
   DecodePlan p = make_decode_plan(c->view(), n, max_len, num_splits, c->cu_count);
@@ -603,8 +607,25 @@ int kvc_attn_decode_window(kvc_cache* c, int32_t layer, int32_t n, const int32_t
                                      " bytes");
   if (p.ws_bytes > 0 && !aligned16(ws)) return fail(KVC_E_INVAL, "workspace must be 16-byte aligned");
   hipError_t e = launch_decode(c->view(), layer, n, seqs, q, out, scale, p, ws, window, sinks,
-                               stream);
+                               knew, vnew, stream);
   return e == hipSuccess ? KVC_OK : hip_fail(e, "decode launch");
+}
+}  // namespace
+
+int kvc_attn_decode_window(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs,
+                           const void* q, void* out, float scale, int32_t window, int32_t sinks,
+                           int32_t num_splits, void* ws, uint64_t ws_bytes, hipStream_t stream) {
+  return decode_impl(c, layer, n, seqs, nullptr, nullptr, q, out, scale, window, sinks,
+                     num_splits, ws, ws_bytes, stream);
+}
+
+int kvc_attn_decode_append(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs,
+                           const void* k_new, const void* v_new, const void* q, void* out,
+                           float scale, int32_t window, int32_t sinks, int32_t num_splits,
+                           void* ws, uint64_t ws_bytes, hipStream_t stream) {
+  if (!k_new || !v_new) return fail(KVC_E_INVAL, "k_new/v_new is NULL");
+  return decode_impl(c, layer, n, seqs, k_new, v_new, q, out, scale, window, sinks, num_splits,
+                     ws, ws_bytes, stream);
 }
 
 int kvc_gather(const kvc_cache* c, int32_t layer, int32_t seq, int32_t start, int32_t count,

@@ -87,9 +87,11 @@ hipError_t launch_write(const CacheView& cv, int layer, int n, const int32_t* se
                         int T, const void* k, const void* v, hipStream_t s);
 hipError_t launch_gather(const CacheView& cv, int layer, int seq, int start, int count,
                          void* k_out, void* v_out, hipStream_t s);
+// knew / vnew non-null: append those rows (kv_append) as part of the call.
 hipError_t launch_decode(const CacheView& cv, int layer, int n, const int32_t* seqs,
                          const void* q, void* out, float scale, const DecodePlan& plan,
-                         void* ws, int window, int sinks, hipStream_t s);
+                         void* ws, int window, int sinks, const void* knew, const void* vnew,
+                         hipStream_t s);
 // window > 0: key j visible to position p iff p - window < j <= p or
 // j < sinks; window = 0: full causal attention.
 hipError_t launch_prefill(const CacheView& cv, int n, int T, const void* q, const void* k,

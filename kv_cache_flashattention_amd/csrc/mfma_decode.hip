@@ -225,17 +225,35 @@ __device__ __forceinline__ WorkWs work_ws(void* ws, int64_t slots, int D, int nb
   return w;
 }
 
+// Wave-uniform values read from LDS or memory, moved to scalar registers.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uni64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // floor(a * W / P) without overflow: W = qP + r.
 __device__ __forceinline__ int64_t share(int64_t a, int64_t W, int64_t P) {
   return a * (W / P) + (a * (W % P)) / P;
 }
 
 
-template <int KV, int D>
-__global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
+// APPEND (16-bit caches): the call also appends each sequence's newest K/V
+// row, knew / vnew [nb][n_kv][D], at position L-1.  The wave that computes a
+// segment's last unit takes that token's operands from knew / vnew instead
+// of the cache (no other wave reads position L-1), and for the first query
+// group of the kv head it also stores the row into the cache.
+// The APPEND variant runs only on 16-bit caches, whose work list uses one
+// workgroup per CU, so it may use the whole register file.
+template <int KV, int D, bool APPEND>
+__global__ __launch_bounds__(256, APPEND ? 1 : 2) void k_decode_work(CacheView cv, int layer,
                                                         const int32_t* seqs, const uint16_t* q,
                                                         void* ws, int nb, int qgroups, int waves,
-                                                        float sl2, int window, int sinks) {
+                                                        float sl2, int window, int sinks,
+                                                        const uint16_t* knew,
+                                                        const uint16_t* vnew) {
+  static_assert(!APPEND || KV == KV_BF16 || KV == KV_F16, "append fusion: 16-bit caches");
   typedef typename Op<KV>::T OpT;
   typedef Unit<KV, D> U;
   constexpr int KS = U::KS, DT = U::DT, KL = U::KL;
@@ -306,7 +324,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
       const int mid = (lo + hi + 1) >> 1;
       if (s_units[mid] <= u) lo = mid; else hi = mid - 1;
     }
-    b = lo;
+    b = uni(lo);
   }
 
   const uint8_t* kpool = (const uint8_t*)cv.k;
@@ -314,18 +332,35 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
   const int64_t layer_blocks = (int64_t)layer * cv.n_blocks;
 
   while (u < u1) {
-    while (s_units[b + 1] <= u) ++b;                 // skip to the entry holding u
-    const int cb = s_counts[b];
-    const int64_t rem = u - s_units[b];
+    while (uni64(s_units[b + 1]) <= u) ++b;           // skip to the entry holding u
+    const int cb = uni(s_counts[b]);
+    const int64_t sb = uni64(s_units[b]);
+    const int64_t rem = u - sb;
     const int kvg = (int)(rem / cb);
     const int c0 = (int)(rem % cb);
-    const int64_t segend = s_units[b] + (int64_t)(kvg + 1) * cb;
+    const int64_t segend = sb + (int64_t)(kvg + 1) * cb;
     const int64_t pend = u1 < segend ? u1 : segend;
     const int c1 = c0 + (int)(pend - u);
     const int kvh = kvg / qgroups, qg = kvg % qgroups;
-    const int seq = seqs[b];
-    const int L = valid_len(cv, seq);                  // > 0: the entry has units
+    const int seq = uni(seqs[b]);
+    const int L = uni(valid_len(cv, seq));             // > 0: the entry has units
     const UnitMap umap(L, window, sinks);
+    // APPEND: the newest row of this (sequence, kv head), and the last unit
+    // (the one holding position L-1) of the segment's visible units
+    const uint16_t* knew_row = APPEND ? knew + ((int64_t)b * cv.n_kv + kvh) * D : nullptr;
+    const uint16_t* vnew_row = APPEND ? vnew + ((int64_t)b * cv.n_kv + kvh) * D : nullptr;
+    const int cs_last = umap.count - 1;
+    // ... and, when this piece ends with that unit, the newest V row's
+    // elements this lane patches in (column 16 dt + r16, two per register),
+    // loaded now so that the last unit does not wait for them
+    uint32_t vpatch[DT / 2];
+    if constexpr (APPEND) {
+      if (c1 == umap.count) {
+#pragma unroll
+        for (int i = 0; i < DT / 2; ++i)
+          vpatch[i] = (uint32_t)vnew_row[32 * i + r16] | ((uint32_t)vnew_row[32 * i + 16 + r16] << 16);
+      }
+    }
 
     // Query operand (B of S^T = K Q^T): column r16 = query row qg*16 + r16.
     const int qi = qg * 16 + r16;
@@ -375,12 +410,12 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
         x = btrow[min(2 * umap.unit(cs) + (lane & 1), last_blk)];
         if (x < 0 || x >= cv.n_blocks) {
           bad = true;
-          x = 0;
+          x = -1;
         }
       }
       tab = x;
       if constexpr (SCALED) {
-        const int64_t si = (layer_blocks + x) * cv.n_kv + kvh;
+        const int64_t si = (layer_blocks + max(x, 0)) * cv.n_kv + kvh;
         tks = cv.ks[si];
         tvs = cv.vs[si];
       }
@@ -394,7 +429,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
       int64_t sbase[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int x = __builtin_amdgcn_readlane(tab, j + i);
+        const int x = max(__builtin_amdgcn_readlane(tab, j + i), 0);   // invalid: NaN rows later
         sbase[i] = ((layer_blocks + x) * cv.n_kv + kvh) * SB;
       }
       if constexpr (SCALED) {
@@ -432,12 +467,19 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
           B.v[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
       } else {
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t) {
+          const uint8_t* rp = krow + (int64_t)tok_slot(t, r16) * D * EB;
+          if constexpr (APPEND) {
+            if (cs == cs_last &&
+                umap.unit(cs) * kUnit + 16 * tok_block(r16) + tok_slot(t, r16) == L - 1)
+              rp = (const uint8_t*)knew_row;
+          }
 #pragma unroll
           for (int a = 0; a < KL; ++a) {
             const int off = KV == KV_FP8 ? 64 * a + 16 * g : 2 * dmap<KV, D>(a, g);
-            B.k[t][a] = *(const uint4*)(krow + (int64_t)tok_slot(t, r16) * D * EB + off);
+            B.k[t][a] = *(const uint4*)(rp + off);
           }
+        }
         const uint8_t* vslab = vpool + ((g >> 1) ? sbase[1] : sbase[0]) + 8 * (g & 1) * EB;
         if constexpr (KV == KV_FP8) {
 #pragma unroll
@@ -569,11 +611,53 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
             const uint32_t hi = ((dt & 1) ? w4.w : w4.y) & keep[1];
             vop = __builtin_bit_cast(OpT, fp8x8_to_bf16(lo, hi));
           } else {
-            const uint4 raw = B.v[dt];
+            uint4 raw = B.v[dt];
+            if constexpr (APPEND) {
+              // the newest token's V element comes from vnew
+              const int np = L - 1 - (c * kUnit + pos0);
+              if (cs == cs_last && np >= 0 && np < 8) {
+                const uint32_t val = (dt & 1) ? vpatch[dt / 2] >> 16 : vpatch[dt / 2] & 0xFFFFu;
+                const uint32_t lo = (raw.x & 0xFFFF0000u) | val, hi = (raw.x & 0xFFFFu) | (val << 16);
+                const uint32_t lo1 = (raw.y & 0xFFFF0000u) | val, hi1 = (raw.y & 0xFFFFu) | (val << 16);
+                const uint32_t lo2 = (raw.z & 0xFFFF0000u) | val, hi2 = (raw.z & 0xFFFFu) | (val << 16);
+                const uint32_t lo3 = (raw.w & 0xFFFF0000u) | val, hi3 = (raw.w & 0xFFFFu) | (val << 16);
+                raw.x = np == 0 ? lo : np == 1 ? hi : raw.x;
+                raw.y = np == 2 ? lo1 : np == 3 ? hi1 : raw.y;
+                raw.z = np == 4 ? lo2 : np == 5 ? hi2 : raw.z;
+                raw.w = np == 6 ? lo3 : np == 7 ? hi3 : raw.w;
+              }
+            }
             vop = __builtin_bit_cast(OpT, make_uint4(raw.x & keep[0], raw.y & keep[1],
                                                      raw.z & keep[2], raw.w & keep[3]));
           }
           o[dt] = mfma(vop, pop, o[dt]);
+        }
+      }
+      // APPEND: the first query group of the kv head stores the newest row
+      // into the cache (slot (L-1) % 16 of its block; skipped if the table
+      // entry is invalid): K from the operand registers of the lanes that
+      // loaded it, V from the patch values of lane group 0.
+      if constexpr (APPEND) {
+        if (cs == cs_last && qg == 0) {
+          const int x = __builtin_amdgcn_readlane(tab, 2 * (cs - tab0) + (((L - 1) / kBlock) & 1));
+          if (x >= 0) {
+            const int64_t base = ((layer_blocks + x) * cv.n_kv + kvh) * SB;
+            const int r = (L - 1) % kBlock;
+            uint8_t* kdst = (uint8_t*)cv.k + base + (int64_t)r * D * 2;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+              if (c * kUnit + 16 * tok_block(r16) + tok_slot(t, r16) == L - 1) {
+#pragma unroll
+                for (int a = 0; a < KL; ++a) *(uint4*)(kdst + 2 * dmap<KV, D>(a, g)) = B.k[t][a];
+              }
+            if (g == 0) {
+              uint16_t* vdst = (uint16_t*)((uint8_t*)cv.v + base) + r;
+#pragma unroll
+              for (int dt = 0; dt < DT; ++dt)
+                vdst[(16 * dt + r16) * kBlock] =
+                    (uint16_t)((dt & 1) ? vpatch[dt / 2] >> 16 : vpatch[dt / 2] & 0xFFFFu);
+            }
+          }
         }
       }
     };
@@ -712,10 +796,10 @@ __global__ __launch_bounds__(256) void k_decode_work_merge(CacheView cv, const v
   }
 }
 
-template <int KV, int D>
+template <int KV, int D, bool APPEND = false>
 hipError_t run(const CacheView& cv, int layer, int n, const int32_t* seqs, const void* q,
                void* out, float sl2, const DecodePlan& p, void* ws, int window, int sinks,
-               hipStream_t st) {
+               hipStream_t st, const void* knew = nullptr, const void* vnew = nullptr) {
   const int G = cv.n_q / cv.n_kv;
   const int qgroups = (G + 15) / 16;
   const int grid = (p.waves + 3) / 4;
@@ -723,8 +807,10 @@ hipError_t run(const CacheView& cv, int layer, int n, const int32_t* seqs, const
     const int nb = n - b0 < kMaxBatch ? n - b0 : kMaxBatch;
     const uint16_t* qb = (const uint16_t*)q + (int64_t)b0 * cv.n_q * D;
     uint16_t* ob = (uint16_t*)out + (int64_t)b0 * cv.n_q * D;
-    hipLaunchKernelGGL((k_decode_work<KV, D>), dim3(grid), dim3(256), 0, st, cv, layer,
-                       seqs + b0, qb, ws, nb, qgroups, p.waves, sl2, window, sinks);
+    const uint16_t* kb = APPEND ? (const uint16_t*)knew + (int64_t)b0 * cv.n_kv * D : nullptr;
+    const uint16_t* vb = APPEND ? (const uint16_t*)vnew + (int64_t)b0 * cv.n_kv * D : nullptr;
+    hipLaunchKernelGGL((k_decode_work<KV, D, APPEND>), dim3(grid), dim3(256), 0, st, cv, layer,
+                       seqs + b0, qb, ws, nb, qgroups, p.waves, sl2, window, sinks, kb, vb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_decode_work_merge<KV == KV_F16, D>), dim3(cv.n_q, nb), dim3(256), 0, st,
@@ -740,7 +826,8 @@ int occupancy_waves() {
   static int waves = 0;
   if (waves == 0) {
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, (const void*)k_decode_work<KV, D>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks,
+                                                     (const void*)k_decode_work<KV, D, false>,
                                                      256, 0) != hipSuccess || blocks < 1)
       blocks = 2;
     waves = 4 * blocks;
@@ -787,19 +874,27 @@ int work_list_waves_per_cu(const CacheView& cv) {
 
 hipError_t launch_decode_mfma(const CacheView& cv, int layer, int n, const int32_t* seqs,
                               const void* q, void* out, float sl2, const DecodePlan& p, void* ws,
-                              int window, int sinks, hipStream_t st, bool* handled) {
+                              int window, int sinks, const void* knew, const void* vnew,
+                              hipStream_t st, bool* handled) {
   *handled = p.work_list != 0;
   if (!*handled) return hipSuccess;
+  const bool fuse = knew != nullptr;
+  if (fuse && cv.dtype != KVC_BF16 && cv.dtype != KVC_F16) return hipErrorInvalidValue;
+#define KVFA_RUN(KVT, DD) run<KVT, DD>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st)
+#define KVFA_RUN_APPEND(KVT, DD) \
+  run<KVT, DD, true>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st, knew, vnew)
   if (cv.d == 128) {
-    if (cv.dtype == KVC_BF16) return run<KV_BF16, 128>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st);
-    if (cv.dtype == KVC_F16) return run<KV_F16, 128>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st);
-    if (cv.dtype == KVC_INT4) return run<KV_INT4, 128>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st);
-    return run<KV_FP8, 128>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st);
+    if (cv.dtype == KVC_BF16) return fuse ? KVFA_RUN_APPEND(KV_BF16, 128) : KVFA_RUN(KV_BF16, 128);
+    if (cv.dtype == KVC_F16) return fuse ? KVFA_RUN_APPEND(KV_F16, 128) : KVFA_RUN(KV_F16, 128);
+    if (cv.dtype == KVC_INT4) return KVFA_RUN(KV_INT4, 128);
+    return KVFA_RUN(KV_FP8, 128);
   }
-  if (cv.dtype == KVC_BF16) return run<KV_BF16, 64>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st);
-  if (cv.dtype == KVC_F16) return run<KV_F16, 64>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st);
-  if (cv.dtype == KVC_INT4) return run<KV_INT4, 64>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st);
-  return run<KV_FP8, 64>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st);
+  if (cv.dtype == KVC_BF16) return fuse ? KVFA_RUN_APPEND(KV_BF16, 64) : KVFA_RUN(KV_BF16, 64);
+  if (cv.dtype == KVC_F16) return fuse ? KVFA_RUN_APPEND(KV_F16, 64) : KVFA_RUN(KV_F16, 64);
+  if (cv.dtype == KVC_INT4) return KVFA_RUN(KV_INT4, 64);
+  return KVFA_RUN(KV_FP8, 64);
+#undef KVFA_RUN
+#undef KVFA_RUN_APPEND
 }
 
 }  // namespace kvfa
