@@ -168,3 +168,35 @@ def test_int4_unsupported_calls():
     with pytest.raises(kv.KvcError) as e:
         c.attn_extend(0, seqs, q, 0.125)
     assert e.value.code == kv.KVC_E_UNSUPPORTED
+
+
+@pytest.mark.parametrize("dtype", ["int4", "fp8"])
+def test_prefill_with_scaled_cache_writes_codes_and_attends_in_bf16(dtype):
+    """Prefill on an fp8 / int4 cache: attention runs on the bf16 inputs
+    (oracle tolerance), and the cache holds exactly the codes and scales of
+    the oracle's slab rule applied to the prompt rows, after which decode
+    against the cache matches the oracle on the dequantised values."""
+    from workloads import prefill_workload
+    w = prefill_workload(small=True)
+    qn, kn, vn = w.qkv()
+    q, k, v = (torch.from_numpy(a).to(torch.bfloat16).cuda() for a in (qn, kn, vn))
+    nb = -(-w.T // 16)
+    c = kv.KvCache(1, w.n_q, w.n_kv, w.d, w.batch * nb + 3, w.batch, nb + 1, dtype, poison=True)
+    m = PagedCacheModel(1, w.n_kv, w.d, dtype, w.batch * nb + 3, w.batch, nb + 1, poison=True)
+    for s in range(w.batch):
+        c.seq_alloc(s, w.T)
+        m.alloc(s, w.T)
+    seqs = torch.arange(w.batch, dtype=torch.int32, device="cuda")
+    out = c.attn_prefill(0, q, k, v, seqs=seqs)
+    torch.cuda.synchronize()
+    scale = 1 / math.sqrt(w.d)
+    for s in range(w.batch):
+        ref = A.prefill_attention(f64(q[s]), f64(k[s]), f64(v[s]), scale)
+        assert_close(f64(out[s]), ref, what=f"prefill seq {s}")
+        m.write_rows(0, s, 0, k[s].float().cpu().numpy(), v[s].float().cpu().numpy())
+    assert pools_match(c, m)
+    qd = q[:, -1].contiguous()                            # decode the last prompt row again
+    y = f64(c.attn_decode(0, seqs, qd))
+    for s in range(w.batch):
+        K, V = m.logical_values(0, s)
+        assert_close(y[s], A.decode_attention(f64(qd[s]), K, V, scale), what=f"decode seq {s}")
