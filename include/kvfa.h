@@ -235,8 +235,10 @@ int kvc_attn_prefill(kvc_cache* cache, int32_t layer, int32_t n, const int32_t* 
  * continuous-batching section: chunked prefill; abhishekpatel.co: long
  * prefills split into chunks), or the target's pass over T drafted tokens
  * (kvcache-7e2 speculative-decoding section).  q_dev, out_dev:
- * [n][T][n_q_heads][d_head] in the io type, 16-byte aligned.  bf16 and f16
- * caches (KVC_E_UNSUPPORTED otherwise); scale finite and > 0.  A device
+ * [n][T][n_q_heads][d_head] in the io type, 16-byte aligned.  bf16, f16
+ * and fp8 caches (KVC_E_UNSUPPORTED for f32 and int4); for fp8 each cached
+ * value is taken as bf16(decode(code) * block scale).  scale finite and > 0.
+ * A device
  * entry that is out of range, has len < T, or whose table holds an invalid
  * block id among its first ceil(len/16) entries gets NaN rows.  No
  * workspace. */

@@ -153,7 +153,11 @@ __device__ __forceinline__ int row_key(int r) {
 // against the len(s) rows the paged cache holds for it (the new rows'
 // K/V included), query t at position len(s) - T + t; K/V tiles are staged
 // straight from the (block, kv head) slabs through the block table.
-template <int D, bool F16, bool PAGED, bool WIN>
+// FP8 (paged only): the slabs hold E4M3FN codes with one float scale per
+// (block, kv head); staging widens each code exactly to float, multiplies by
+// its block's scale and rounds to bf16, so the tiles in LDS are bf16 as for
+// a bf16 cache.
+template <int D, bool F16, bool PAGED, bool WIN, bool FP8 = false>
 __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int T,
                                                          const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ k,
@@ -270,6 +274,26 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
   const uint16_t* kpool = (const uint16_t*)cv.k + ((int64_t)layer * cv.n_blocks * n_kv + g) * kBlock * D;
   const uint16_t* vpool = (const uint16_t*)cv.v + ((int64_t)layer * cv.n_blocks * n_kv + g) * kBlock * D;
   const int32_t* btab = cv.bt + (int64_t)seq * cv.max_bps;
+  // fp8: byte pools with the same slab arithmetic, and the scale index base
+  const uint8_t* kpool8 = (const uint8_t*)cv.k + ((int64_t)layer * cv.n_blocks * n_kv + g) * kBlock * D;
+  const uint8_t* vpool8 = (const uint8_t*)cv.v + ((int64_t)layer * cv.n_blocks * n_kv + g) * kBlock * D;
+  const int64_t sc0 = (int64_t)layer * cv.n_blocks * n_kv + g;   // + block * n_kv
+  // 8 fp8 codes (two dwords) times a scale, rounded to 8 bf16 (four dwords)
+  auto widen8 = [&](uint32_t lo, uint32_t hi, float sc) {
+    typedef __attribute__((ext_vector_type(2))) float f2;
+    const f2 x[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 1.0f, false),
+                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 1.0f, true),
+                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 1.0f, false),
+                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 1.0f, true)};
+    u32x4 r;
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) {
+      const uint32_t a = __builtin_bit_cast(uint16_t, (__bf16)(x[w2].x * sc));
+      const uint32_t b2 = __builtin_bit_cast(uint16_t, (__bf16)(x[w2].y * sc));
+      r[w2] = a | (b2 << 16);
+    }
+    return r;
+  };
   auto load_k = [&](int li) {
     const int i = tile_of(li);
     const int lim = L - 1 - BN * i;                    // last valid row of the tile
@@ -278,8 +302,14 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
 #pragma unroll
       for (int c0 = 0; c0 < KCH; ++c0) {
         const int kp = BN * i + min(t / KG + c0 * (256 / KG), lim);
-        const uint16_t* sl = kpool + btab[kp >> 4] * slab;
-        sreg[c0] = *(const u32x4*)(sl + (kp & (kBlock - 1)) * D + 8 * (t % KG));
+        const int e = btab[kp >> 4];
+        if constexpr (FP8) {
+          const uint2 x = *(const uint2*)(kpool8 + e * slab + (kp & (kBlock - 1)) * D + 8 * (t % KG));
+          sreg[c0] = u32x4{x.x, x.y, __float_as_uint(cv.ks[sc0 + (int64_t)e * n_kv]), 0u};
+        } else {
+          const uint16_t* sl = kpool + e * slab;
+          sreg[c0] = *(const u32x4*)(sl + (kp & (kBlock - 1)) * D + 8 * (t % KG));
+        }
       }
     } else {
       const uint16_t* tb = kbase + (int64_t)(BN * i) * kvstride;
@@ -293,8 +323,11 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
   auto store_k = [&](int buf) {
     const int t = opaque_tid() & 255;
 #pragma unroll
-    for (int c0 = 0; c0 < KCH; ++c0)
-      *(u32x4*)&Ks[buf][(t / KG + c0 * (256 / KG)) * KP + 8 * (t % KG)] = sreg[c0];
+    for (int c0 = 0; c0 < KCH; ++c0) {
+      u32x4 x = sreg[c0];
+      if constexpr (FP8) x = widen8(x[0], x[1], __uint_as_float(x[2]));
+      *(u32x4*)&Ks[buf][(t / KG + c0 * (256 / KG)) * KP + 8 * (t % KG)] = x;
+    }
   };
   // Prompt V: thread (kg, dg) moves keys 4kg..4kg+3 of d-granule dg,
   // transposing them; the 16 lanes of one LDS write pass cover one whole
@@ -310,8 +343,14 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
       for (int c0 = 0; c0 < VCH; ++c0) {
         const int c = t + 256 * c0, rr = c >> 3, j = (c >> 1) & 3, h = c & 1;
         const int kb = min(BN * i + kBlock * j, L - 1) >> 4;
-        const uint16_t* sl = vpool + btab[kb] * slab;
-        sreg[c0] = *(const u32x4*)(sl + rr * kBlock + 8 * h);
+        const int e = btab[kb];
+        if constexpr (FP8) {
+          const uint2 x = *(const uint2*)(vpool8 + e * slab + rr * kBlock + 8 * h);
+          sreg[c0] = u32x4{x.x, x.y, __float_as_uint(cv.vs[sc0 + (int64_t)e * n_kv]), 0u};
+        } else {
+          const uint16_t* sl = vpool + e * slab;
+          sreg[c0] = *(const u32x4*)(sl + rr * kBlock + 8 * h);
+        }
       }
     } else if (t < VBL) {
       const int kg = t % (BN / 4), dg = t / (BN / 4);
@@ -333,6 +372,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
         const int c = t + 256 * c0, rr = c >> 3, j = (c >> 1) & 3, h = c & 1;
         const int nvalid = L - (BN * i + kBlock * j + 8 * h);   // keys of the chunk below L
         u32x4 x = sreg[c0];
+        if constexpr (FP8) x = widen8(x[0], x[1], __uint_as_float(x[2]));
         if (nvalid < 8) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -537,7 +577,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
     }
 }
 
-template <int D, bool F16, bool PAGED>
+template <int D, bool F16, bool PAGED, bool FP8 = false>
 hipError_t run(const CacheView& cv, int layer, int n, const int32_t* seqs, int T, const void* q,
                const void* k, const void* v, void* out, float sl2, int window, int sinks,
                hipStream_t s) {
@@ -546,12 +586,12 @@ hipError_t run(const CacheView& cv, int layer, int n, const int32_t* seqs, int T
   if (units > INT32_MAX) return hipErrorInvalidValue;
   const int xcd_split = units % 8 == 0 ? 1 : 0;
   if (window > 0)
-    hipLaunchKernelGGL((k_prefill_mfma<D, F16, PAGED, true>), dim3((uint32_t)units), dim3(512), 0,
+    hipLaunchKernelGGL((k_prefill_mfma<D, F16, PAGED, true, FP8>), dim3((uint32_t)units), dim3(512), 0,
                        s, cv.n_q, cv.n_kv, T, (const uint16_t*)q, (const uint16_t*)k,
                        (const uint16_t*)v, (uint16_t*)out, sl2, ntiles, n, (int)units, xcd_split,
                        cv, layer, seqs, window, sinks);
   else
-    hipLaunchKernelGGL((k_prefill_mfma<D, F16, PAGED, false>), dim3((uint32_t)units), dim3(512),
+    hipLaunchKernelGGL((k_prefill_mfma<D, F16, PAGED, false, FP8>), dim3((uint32_t)units), dim3(512),
                        0, s, cv.n_q, cv.n_kv, T, (const uint16_t*)q, (const uint16_t*)k,
                        (const uint16_t*)v, (uint16_t*)out, sl2, ntiles, n, (int)units, xcd_split,
                        cv, layer, seqs, 0, 0);
@@ -567,6 +607,9 @@ hipError_t dispatch(const CacheView& cv, int layer, int n, const int32_t* seqs, 
   if (io == KVC_BF16 && (!PAGED || cv.dtype == KVC_BF16)) {
     if (cv.d == 128) return run<128, false, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);
     if (cv.d == 64) return run<64, false, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);
+  } else if (PAGED && cv.dtype == KVC_FP8_E4M3FN) {
+    if (cv.d == 128) return run<128, false, true, true>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);
+    if (cv.d == 64) return run<64, false, true, true>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);
   } else if (io == KVC_F16) {
     if (cv.d == 128) return run<128, true, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);
     if (cv.d == 64) return run<64, true, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);

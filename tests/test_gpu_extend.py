@@ -125,3 +125,43 @@ def test_extend_llama8b_chunk_sampled_rows():
         sample = np.unique(np.concatenate([[0, 1, 255, 256, T - 1], rng.integers(0, T, 6)]))
         ref = A.gqa_attention(f64(q[b])[sample], f64(k), f64(v), scale, q_pos=L - T + sample)
         assert_close(f64(out[b])[sample], ref, what=f"chunk of 512 at L={L}")
+
+
+@pytest.mark.parametrize("n_q,n_kv,d,T,lengths,window,sinks", [
+    (32, 8, 128, 64, [64, 100, 700], 0, 0),
+    (8, 2, 64, 33, [33, 290, 1030], 0, 0),
+    (32, 8, 128, 100, [100, 400, 900], 128, 4),
+])
+def test_extend_fp8_cache_vs_dequantised_oracle(n_q, n_kv, d, T, lengths, window, sinks):
+    """fp8 cache: the staged tiles are bf16(decode(code) * block scale); the
+    result matches the oracle on the exactly dequantised values the cache
+    holds (the oracle's paged model fed the same rows) within the bf16
+    tolerances."""
+    from oracle.paged import PagedCacheModel
+    rng = np.random.default_rng([T, d, window])
+    nbs = [-(-L // 16) for L in lengths]
+    n_blocks = sum(nbs) + 5
+    c = kv.KvCache(1, n_q, n_kv, d, n_blocks, len(lengths), max(nbs) + 1, "fp8", poison=True)
+    m = PagedCacheModel(1, n_kv, d, "fp8", n_blocks, len(lengths), max(nbs) + 1, poison=True)
+    perm = rng.permutation(n_blocks).astype(np.int32)
+    o = 0
+    for b, L in enumerate(lengths):
+        c.set_block_table(b, perm[o:o + nbs[b]], L)
+        m.set_table(b, perm[o:o + nbs[b]], L)
+        o += nbs[b]
+        k = _rows(rng, (1, L, n_kv, d), torch.bfloat16)
+        v = _rows(rng, (1, L, n_kv, d), torch.bfloat16)
+        c.write(0, torch.tensor([b], dtype=torch.int32, device="cuda"), 0, k, v)
+        m.write_rows(0, b, 0, k[0].float().cpu().numpy(), v[0].float().cpu().numpy())
+    q = _rows(rng, (len(lengths), T, n_q, d), torch.bfloat16)
+    seqs = torch.arange(len(lengths), dtype=torch.int32, device="cuda")
+    out = c.attn_extend(0, seqs, q, window=window, sinks=sinks)
+    torch.cuda.synchronize()
+    scale = 1 / math.sqrt(d)
+    for b in range(len(lengths)):
+        K, V = m.logical_values(0, b)
+        ref = A.extend_attention(f64(q[b]), K, V, scale, window=window, sinks=sinks)
+        # one more bf16 rounding per cached value (relative 2^-9 for K and
+        # for V) than a bf16 cache has: the row-relative bound is doubled
+        assert_close(f64(out[b]), ref, rel_tol=2e-2,
+                     what=f"fp8 extend T={T} L={lengths[b]} w={window}")
