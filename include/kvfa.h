@@ -49,9 +49,7 @@
  * place of 448: absmax/7 per (layer, block, kv head), a code holds
  * rint(x / scale) (ties to even) clamped to +-7, and a growing absmax
  * re-encodes the block's earlier rows as encode(fl(code * s_old) / s_new).
- * The io type is bf16.  Only kv_append, kvc_write, the decode calls
- * (kvc_attn_decode, kvc_attn_decode_window), kvc_gather and the
- * cache-independent prefill calls take an int4 cache.
+ * The io type is bf16.
  *
  * Conventions.  Every function returns KVC_OK (0) or a negative status and
  * never throws; kvc_last_error() gives a message for the calling thread.
@@ -235,9 +233,10 @@ int kvc_attn_prefill(kvc_cache* cache, int32_t layer, int32_t n, const int32_t* 
  * continuous-batching section: chunked prefill; abhishekpatel.co: long
  * prefills split into chunks), or the target's pass over T drafted tokens
  * (kvcache-7e2 speculative-decoding section).  q_dev, out_dev:
- * [n][T][n_q_heads][d_head] in the io type, 16-byte aligned.  bf16, f16
- * and fp8 caches (KVC_E_UNSUPPORTED for f32 and int4); for fp8 each cached
- * value is taken as bf16(decode(code) * block scale).  scale finite and > 0.
+ * [n][T][n_q_heads][d_head] in the io type, 16-byte aligned.  bf16, f16,
+ * fp8 and int4 caches (KVC_E_UNSUPPORTED for f32); for fp8 and int4 each
+ * cached value is taken as bf16(decode(code) * block scale).  scale finite
+ * and > 0.
  * A device
  * entry that is out of range, has len < T, or whose table holds an invalid
  * block id among its first ceil(len/16) entries gets NaN rows.  No

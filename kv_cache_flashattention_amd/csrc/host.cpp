@@ -547,9 +547,8 @@ int kvc_attn_extend_window(kvc_cache* c, int32_t layer, int32_t n, const int32_t
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(KVC_E_INVAL, "scale must be finite and positive");
   if (window < 0 || sinks < 0) return fail(KVC_E_INVAL, "window and sinks must be >= 0");
-  if (c->cfg.kv_dtype != KVC_BF16 && c->cfg.kv_dtype != KVC_F16 &&
-      c->cfg.kv_dtype != KVC_FP8_E4M3FN)
-    return fail(KVC_E_UNSUPPORTED, "attn_extend needs a bf16, f16 or fp8 cache");
+  if (c->cfg.kv_dtype == KVC_F32)
+    return fail(KVC_E_UNSUPPORTED, "attn_extend needs a bf16, f16, fp8 or int4 cache");
   int r = need_dev(c);
   if (r) return r;
   if (layer < 0 || layer >= c->cfg.n_layers) return fail(KVC_E_STATE, "layer out of range");

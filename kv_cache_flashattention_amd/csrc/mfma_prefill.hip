@@ -153,11 +153,11 @@ __device__ __forceinline__ int row_key(int r) {
 // against the len(s) rows the paged cache holds for it (the new rows'
 // K/V included), query t at position len(s) - T + t; K/V tiles are staged
 // straight from the (block, kv head) slabs through the block table.
-// FP8 (paged only): the slabs hold E4M3FN codes with one float scale per
-// (block, kv head); staging widens each code exactly to float, multiplies by
-// its block's scale and rounds to bf16, so the tiles in LDS are bf16 as for
-// a bf16 cache.
-template <int D, bool F16, bool PAGED, bool WIN, bool FP8 = false>
+// SC (paged only): a scaled cache, KVC_FP8_E4M3FN or KVC_INT4, whose slabs
+// hold codes with one float scale per (block, kv head); staging widens each
+// code exactly to float, multiplies by its block's scale and rounds to bf16,
+// so the tiles in LDS are bf16 as for a bf16 cache.
+template <int D, bool F16, bool PAGED, bool WIN, int SC = 0>
 __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int T,
                                                          const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ k,
@@ -274,9 +274,13 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
   const uint16_t* kpool = (const uint16_t*)cv.k + ((int64_t)layer * cv.n_blocks * n_kv + g) * kBlock * D;
   const uint16_t* vpool = (const uint16_t*)cv.v + ((int64_t)layer * cv.n_blocks * n_kv + g) * kBlock * D;
   const int32_t* btab = cv.bt + (int64_t)seq * cv.max_bps;
-  // fp8: byte pools with the same slab arithmetic, and the scale index base
-  const uint8_t* kpool8 = (const uint8_t*)cv.k + ((int64_t)layer * cv.n_blocks * n_kv + g) * kBlock * D;
-  const uint8_t* vpool8 = (const uint8_t*)cv.v + ((int64_t)layer * cv.n_blocks * n_kv + g) * kBlock * D;
+  // scaled caches: byte pools (fp8 one byte per code, int4 two codes per
+  // byte) and the scale index base
+  constexpr bool FP8 = SC == KVC_FP8_E4M3FN, I4 = SC == KVC_INT4;
+  constexpr int CB = I4 ? 2 : 1;                       // codes per byte
+  const int64_t slab8 = slab / CB;                     // slab bytes
+  const uint8_t* kpool8 = (const uint8_t*)cv.k + ((int64_t)layer * cv.n_blocks * n_kv + g) * slab8 / n_kv;
+  const uint8_t* vpool8 = (const uint8_t*)cv.v + ((int64_t)layer * cv.n_blocks * n_kv + g) * slab8 / n_kv;
   const int64_t sc0 = (int64_t)layer * cv.n_blocks * n_kv + g;   // + block * n_kv
   // 8 fp8 codes (two dwords) times a scale, rounded to 8 bf16 (four dwords)
   auto widen8 = [&](uint32_t lo, uint32_t hi, float sc) {
@@ -294,6 +298,19 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
     }
     return r;
   };
+  // 8 int4 codes (one dword, code k in nibble k) times a scale -> 8 bf16
+  auto widen8_i4 = [&](uint32_t x, float sc) {
+    u32x4 r;
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) {
+      // the builtin is typed unsigned: the signed field goes through int
+      const float lo = (float)(int)__builtin_amdgcn_sbfe((int)x, 8 * w2, 4) * sc;
+      const float hi = (float)(int)__builtin_amdgcn_sbfe((int)x, 8 * w2 + 4, 4) * sc;
+      r[w2] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
+              ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+    }
+    return r;
+  };
   auto load_k = [&](int li) {
     const int i = tile_of(li);
     const int lim = L - 1 - BN * i;                    // last valid row of the tile
@@ -304,8 +321,12 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
         const int kp = BN * i + min(t / KG + c0 * (256 / KG), lim);
         const int e = btab[kp >> 4];
         if constexpr (FP8) {
-          const uint2 x = *(const uint2*)(kpool8 + e * slab + (kp & (kBlock - 1)) * D + 8 * (t % KG));
+          const uint2 x = *(const uint2*)(kpool8 + e * slab8 + (kp & (kBlock - 1)) * D + 8 * (t % KG));
           sreg[c0] = u32x4{x.x, x.y, __float_as_uint(cv.ks[sc0 + (int64_t)e * n_kv]), 0u};
+        } else if constexpr (I4) {
+          const uint32_t x = *(const uint32_t*)(kpool8 + e * slab8 + (kp & (kBlock - 1)) * (D / 2) +
+                                                4 * (t % KG));
+          sreg[c0] = u32x4{x, 0u, __float_as_uint(cv.ks[sc0 + (int64_t)e * n_kv]), 0u};
         } else {
           const uint16_t* sl = kpool + e * slab;
           sreg[c0] = *(const u32x4*)(sl + (kp & (kBlock - 1)) * D + 8 * (t % KG));
@@ -326,6 +347,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
     for (int c0 = 0; c0 < KCH; ++c0) {
       u32x4 x = sreg[c0];
       if constexpr (FP8) x = widen8(x[0], x[1], __uint_as_float(x[2]));
+      if constexpr (I4) x = widen8_i4(x[0], __uint_as_float(x[2]));
       *(u32x4*)&Ks[buf][(t / KG + c0 * (256 / KG)) * KP + 8 * (t % KG)] = x;
     }
   };
@@ -345,8 +367,11 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
         const int kb = min(BN * i + kBlock * j, L - 1) >> 4;
         const int e = btab[kb];
         if constexpr (FP8) {
-          const uint2 x = *(const uint2*)(vpool8 + e * slab + rr * kBlock + 8 * h);
+          const uint2 x = *(const uint2*)(vpool8 + e * slab8 + rr * kBlock + 8 * h);
           sreg[c0] = u32x4{x.x, x.y, __float_as_uint(cv.vs[sc0 + (int64_t)e * n_kv]), 0u};
+        } else if constexpr (I4) {
+          const uint32_t x = *(const uint32_t*)(vpool8 + e * slab8 + rr * (kBlock / 2) + 4 * h);
+          sreg[c0] = u32x4{x, 0u, __float_as_uint(cv.vs[sc0 + (int64_t)e * n_kv]), 0u};
         } else {
           const uint16_t* sl = vpool + e * slab;
           sreg[c0] = *(const u32x4*)(sl + rr * kBlock + 8 * h);
@@ -373,6 +398,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
         const int nvalid = L - (BN * i + kBlock * j + 8 * h);   // keys of the chunk below L
         u32x4 x = sreg[c0];
         if constexpr (FP8) x = widen8(x[0], x[1], __uint_as_float(x[2]));
+        if constexpr (I4) x = widen8_i4(x[0], __uint_as_float(x[2]));
         if (nvalid < 8) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -577,7 +603,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
     }
 }
 
-template <int D, bool F16, bool PAGED, bool FP8 = false>
+template <int D, bool F16, bool PAGED, int SC = 0>
 hipError_t run(const CacheView& cv, int layer, int n, const int32_t* seqs, int T, const void* q,
                const void* k, const void* v, void* out, float sl2, int window, int sinks,
                hipStream_t s) {
@@ -586,12 +612,12 @@ hipError_t run(const CacheView& cv, int layer, int n, const int32_t* seqs, int T
   if (units > INT32_MAX) return hipErrorInvalidValue;
   const int xcd_split = units % 8 == 0 ? 1 : 0;
   if (window > 0)
-    hipLaunchKernelGGL((k_prefill_mfma<D, F16, PAGED, true, FP8>), dim3((uint32_t)units), dim3(512), 0,
+    hipLaunchKernelGGL((k_prefill_mfma<D, F16, PAGED, true, SC>), dim3((uint32_t)units), dim3(512), 0,
                        s, cv.n_q, cv.n_kv, T, (const uint16_t*)q, (const uint16_t*)k,
                        (const uint16_t*)v, (uint16_t*)out, sl2, ntiles, n, (int)units, xcd_split,
                        cv, layer, seqs, window, sinks);
   else
-    hipLaunchKernelGGL((k_prefill_mfma<D, F16, PAGED, false, FP8>), dim3((uint32_t)units), dim3(512),
+    hipLaunchKernelGGL((k_prefill_mfma<D, F16, PAGED, false, SC>), dim3((uint32_t)units), dim3(512),
                        0, s, cv.n_q, cv.n_kv, T, (const uint16_t*)q, (const uint16_t*)k,
                        (const uint16_t*)v, (uint16_t*)out, sl2, ntiles, n, (int)units, xcd_split,
                        cv, layer, seqs, 0, 0);
@@ -608,8 +634,11 @@ hipError_t dispatch(const CacheView& cv, int layer, int n, const int32_t* seqs, 
     if (cv.d == 128) return run<128, false, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);
     if (cv.d == 64) return run<64, false, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);
   } else if (PAGED && cv.dtype == KVC_FP8_E4M3FN) {
-    if (cv.d == 128) return run<128, false, true, true>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);
-    if (cv.d == 64) return run<64, false, true, true>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);
+    if (cv.d == 128) return run<128, false, true, KVC_FP8_E4M3FN>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);
+    if (cv.d == 64) return run<64, false, true, KVC_FP8_E4M3FN>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);
+  } else if (PAGED && cv.dtype == KVC_INT4) {
+    if (cv.d == 128) return run<128, false, true, KVC_INT4>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);
+    if (cv.d == 64) return run<64, false, true, KVC_INT4>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);
   } else if (io == KVC_F16) {
     if (cv.d == 128) return run<128, true, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);
     if (cv.d == 64) return run<64, true, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);

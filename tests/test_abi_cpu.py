@@ -246,7 +246,7 @@ def test_decode_workspace_plan():
     assert f.decode_workspace_bytes(40, num_splits=4) == 40 * 32 * 4 * 130 * 4
 
 
-@pytest.mark.parametrize("dtype", ["f32", "int4"])
+@pytest.mark.parametrize("dtype", ["f32"])
 def test_extend_refuses_cache_types_without_a_kernel(dtype):
     c = kv.KvCache(1, 8, 2, 128, 16, 2, 4, dtype, device=None)
     p = ctypes.c_void_p(16)

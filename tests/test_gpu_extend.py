@@ -127,13 +127,15 @@ def test_extend_llama8b_chunk_sampled_rows():
         assert_close(f64(out[b])[sample], ref, what=f"chunk of 512 at L={L}")
 
 
+@pytest.mark.parametrize("dtype", ["fp8", "int4"])
 @pytest.mark.parametrize("n_q,n_kv,d,T,lengths,window,sinks", [
     (32, 8, 128, 64, [64, 100, 700], 0, 0),
     (8, 2, 64, 33, [33, 290, 1030], 0, 0),
     (32, 8, 128, 100, [100, 400, 900], 128, 4),
 ])
-def test_extend_fp8_cache_vs_dequantised_oracle(n_q, n_kv, d, T, lengths, window, sinks):
-    """fp8 cache: the staged tiles are bf16(decode(code) * block scale); the
+def test_extend_scaled_cache_vs_dequantised_oracle(dtype, n_q, n_kv, d, T, lengths, window,
+                                                   sinks):
+    """fp8 / int4 cache: the staged tiles are bf16(decode(code) * block scale); the
     result matches the oracle on the exactly dequantised values the cache
     holds (the oracle's paged model fed the same rows) within the bf16
     tolerances."""
@@ -141,8 +143,8 @@ def test_extend_fp8_cache_vs_dequantised_oracle(n_q, n_kv, d, T, lengths, window
     rng = np.random.default_rng([T, d, window])
     nbs = [-(-L // 16) for L in lengths]
     n_blocks = sum(nbs) + 5
-    c = kv.KvCache(1, n_q, n_kv, d, n_blocks, len(lengths), max(nbs) + 1, "fp8", poison=True)
-    m = PagedCacheModel(1, n_kv, d, "fp8", n_blocks, len(lengths), max(nbs) + 1, poison=True)
+    c = kv.KvCache(1, n_q, n_kv, d, n_blocks, len(lengths), max(nbs) + 1, dtype, poison=True)
+    m = PagedCacheModel(1, n_kv, d, dtype, n_blocks, len(lengths), max(nbs) + 1, poison=True)
     perm = rng.permutation(n_blocks).astype(np.int32)
     o = 0
     for b, L in enumerate(lengths):
@@ -164,4 +166,4 @@ def test_extend_fp8_cache_vs_dequantised_oracle(n_q, n_kv, d, T, lengths, window
         # one more bf16 rounding per cached value (relative 2^-9 for K and
         # for V) than a bf16 cache has: the row-relative bound is doubled
         assert_close(f64(out[b]), ref, rel_tol=2e-2,
-                     what=f"fp8 extend T={T} L={lengths[b]} w={window}")
+                     what=f"{dtype} extend T={T} L={lengths[b]} w={window}")

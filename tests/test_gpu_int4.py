@@ -160,16 +160,6 @@ def test_int4_decode_window_and_sinks():
             assert_close(y[s], r, what=f"int4 decode w={window} s={sinks} seq {s}")
 
 
-def test_int4_unsupported_calls():
-    c = kv.KvCache(1, 8, 2, 64, 8, 2, 4, "int4")
-    c.seq_alloc(0, 16)
-    q = torch.zeros(1, 4, 8, 64, dtype=torch.bfloat16, device="cuda")
-    seqs = torch.zeros(1, dtype=torch.int32, device="cuda")
-    with pytest.raises(kv.KvcError) as e:
-        c.attn_extend(0, seqs, q, 0.125)
-    assert e.value.code == kv.KVC_E_UNSUPPORTED
-
-
 @pytest.mark.parametrize("dtype", ["int4", "fp8"])
 def test_prefill_with_scaled_cache_writes_codes_and_attends_in_bf16(dtype):
     """Prefill on an fp8 / int4 cache: attention runs on the bf16 inputs
