@@ -80,6 +80,43 @@ def test_llama8b_decode_full_all_outputs():
     print(f"llama8b decode: worst abs {worst[0]:.2e} rel {worst[1]:.2e}")
 
 
+def test_llama8b_fused_append_decode_full_all_outputs():
+    """The bench's step at full size: rows 0..L-2 written in bulk, a grow,
+    then kvc_attn_decode_append with row L-1 (appended inside the decode
+    kernel); every output against the oracle, and the appended rows read
+    back through the gather bit for bit."""
+    w = decode_workload("llama8b_decode")
+    io = torch.bfloat16
+    max_bps = int(w.blocks_per_seq.max()) + 1
+    c = kv.KvCache(1, w.n_q, w.n_kv, w.d, w.n_blocks + w.batch, w.batch, max_bps, "bf16")
+    tables = w.block_tables()
+    last_k, last_v = [], []
+    for b in range(w.batch):
+        L = int(w.lengths[b])
+        c.set_block_table(b, tables[b][:-(-(L - 1) // 16)], L - 1)
+        k, v = w.kv_rows(b, 0, L)
+        sel = torch.tensor([b], dtype=torch.int32, device="cuda")
+        if L > 1:
+            c.write(0, sel, 0, torch.from_numpy(k[:L - 1]).to(io).cuda()[None],
+                    torch.from_numpy(v[:L - 1]).to(io).cuda()[None])
+        last_k.append(torch.from_numpy(k[L - 1]).to(io).cuda())
+        last_v.append(torch.from_numpy(v[L - 1]).to(io).cuda())
+    c.seq_grow(list(range(w.batch)))
+    seqs = torch.arange(w.batch, dtype=torch.int32, device="cuda")
+    kn, vn = torch.stack(last_k).contiguous(), torch.stack(last_v).contiguous()
+    q = torch.from_numpy(w.q()).to(io).cuda()
+    y = f64(c.attn_decode_append(0, seqs, kn, vn, q))
+    scale = 1 / math.sqrt(w.d)
+    qd = f64(q)
+    for b in range(w.batch):
+        K, V = source_rows(w, b, io)
+        assert_close(y[b], A.decode_attention(qd[b], K, V, scale), what=f"seq {b}")
+        L = int(w.lengths[b])
+        gk, gv = c.gather(0, b, L - 1, 1)
+        assert torch.equal(gk[0].view(torch.int16), kn[b].view(torch.int16))
+        assert torch.equal(gv[0].view(torch.int16), vn[b].view(torch.int16))
+
+
 def test_long_mha_decode_full_sampled_heads():
     """One 128,000-token fp16 sequence: 2,000 rows written in bulk, then
     125,999 single-token grow + kv_append steps, then the new token."""
