@@ -154,9 +154,11 @@ __device__ __forceinline__ int row_key(int r) {
 // K/V included), query t at position len(s) - T + t; K/V tiles are staged
 // straight from the (block, kv head) slabs through the block table.
 // SC (paged only): a scaled cache, KVC_FP8_E4M3FN or KVC_INT4, whose slabs
-// hold codes with one float scale per (block, kv head); staging widens each
-// code exactly to float, multiplies by its block's scale and rounds to bf16,
-// so the tiles in LDS are bf16 as for a bf16 cache.
+// hold codes with one float scale per (block, kv head).  Staging widens each
+// code exactly to bf16 (every E4M3FN value and every int4 code is a bf16
+// value); the tile's four K scales multiply the scores of their blocks'
+// keys and its four V scales the probabilities before they are rounded for
+// the PV products, while the row sum l adds the unscaled probabilities.
 template <int D, bool F16, bool PAGED, bool WIN, int SC = 0>
 __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int T,
                                                          const uint16_t* __restrict__ q,
@@ -175,6 +177,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
   constexpr int VP = BN + 8;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KP];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VP];
+  __shared__ float Ssc[2][8];       // scaled caches: K scales [0..3], V scales [4..7] of a tile
 
   // ---- work assignment.  Workgroup L runs on XCD L % 8; the work list is
   // cut into 8 contiguous parts, one per XCD, ordered (kv head, sequence,
@@ -283,34 +286,34 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
   const uint8_t* vpool8 = (const uint8_t*)cv.v + ((int64_t)layer * cv.n_blocks * n_kv + g) * slab8 / n_kv;
   const int64_t sc0 = (int64_t)layer * cv.n_blocks * n_kv + g;   // + block * n_kv
   // 8 fp8 codes (two dwords) times a scale, rounded to 8 bf16 (four dwords)
-  auto widen8 = [&](uint32_t lo, uint32_t hi, float sc) {
-    typedef __attribute__((ext_vector_type(2))) float f2;
-    const f2 x[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 1.0f, false),
-                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 1.0f, true),
-                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 1.0f, false),
-                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 1.0f, true)};
+  // 8 fp8 codes (two dwords) -> 8 bf16, exactly
+  auto widen8 = [&](uint32_t lo, uint32_t hi) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 b2;
+    const b2 x[4] = {__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false),
+                     __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true),
+                     __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false),
+                     __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true)};
     u32x4 r;
 #pragma unroll
-    for (int w2 = 0; w2 < 4; ++w2) {
-      const uint32_t a = __builtin_bit_cast(uint16_t, (__bf16)(x[w2].x * sc));
-      const uint32_t b2 = __builtin_bit_cast(uint16_t, (__bf16)(x[w2].y * sc));
-      r[w2] = a | (b2 << 16);
-    }
+    for (int w2 = 0; w2 < 4; ++w2) r[w2] = __builtin_bit_cast(uint32_t, x[w2]);
     return r;
   };
-  // 8 int4 codes (one dword, code k in nibble k) times a scale -> 8 bf16
-  auto widen8_i4 = [&](uint32_t x, float sc) {
+  // 8 int4 codes (one dword, code k in nibble k) -> 8 bf16, exactly
+  auto widen8_i4 = [&](uint32_t x) {
     u32x4 r;
 #pragma unroll
     for (int w2 = 0; w2 < 4; ++w2) {
       // the builtin is typed unsigned: the signed field goes through int
-      const float lo = (float)(int)__builtin_amdgcn_sbfe((int)x, 8 * w2, 4) * sc;
-      const float hi = (float)(int)__builtin_amdgcn_sbfe((int)x, 8 * w2 + 4, 4) * sc;
+      const float lo = (float)(int)__builtin_amdgcn_sbfe((int)x, 8 * w2, 4);
+      const float hi = (float)(int)__builtin_amdgcn_sbfe((int)x, 8 * w2 + 4, 4);
       r[w2] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
               ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
     }
     return r;
   };
+  // scaled caches: the K and V scales of the tile's four blocks, loaded by
+  // group threads 0..3 with the K tile and written to LDS beside it
+  float scK = 1.f, scV = 1.f;
   auto load_k = [&](int li) {
     const int i = tile_of(li);
     const int lim = L - 1 - BN * i;                    // last valid row of the tile
@@ -322,14 +325,21 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
         const int e = btab[kp >> 4];
         if constexpr (FP8) {
           const uint2 x = *(const uint2*)(kpool8 + e * slab8 + (kp & (kBlock - 1)) * D + 8 * (t % KG));
-          sreg[c0] = u32x4{x.x, x.y, __float_as_uint(cv.ks[sc0 + (int64_t)e * n_kv]), 0u};
+          sreg[c0] = u32x4{x.x, x.y, 0u, 0u};
         } else if constexpr (I4) {
           const uint32_t x = *(const uint32_t*)(kpool8 + e * slab8 + (kp & (kBlock - 1)) * (D / 2) +
                                                 4 * (t % KG));
-          sreg[c0] = u32x4{x, 0u, __float_as_uint(cv.ks[sc0 + (int64_t)e * n_kv]), 0u};
+          sreg[c0] = u32x4{x, 0u, 0u, 0u};
         } else {
           const uint16_t* sl = kpool + e * slab;
           sreg[c0] = *(const u32x4*)(sl + (kp & (kBlock - 1)) * D + 8 * (t % KG));
+        }
+      }
+      if constexpr (SC != 0) {
+        if (t < 4) {
+          const int e = btab[min(BN * i + kBlock * t, L - 1) >> 4];
+          scK = cv.ks[sc0 + (int64_t)e * n_kv];
+          scV = cv.vs[sc0 + (int64_t)e * n_kv];
         }
       }
     } else {
@@ -346,9 +356,15 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
 #pragma unroll
     for (int c0 = 0; c0 < KCH; ++c0) {
       u32x4 x = sreg[c0];
-      if constexpr (FP8) x = widen8(x[0], x[1], __uint_as_float(x[2]));
-      if constexpr (I4) x = widen8_i4(x[0], __uint_as_float(x[2]));
+      if constexpr (FP8) x = widen8(x[0], x[1]);
+      if constexpr (I4) x = widen8_i4(x[0]);
       *(u32x4*)&Ks[buf][(t / KG + c0 * (256 / KG)) * KP + 8 * (t % KG)] = x;
+    }
+    if constexpr (SC != 0) {
+      if (t < 4) {
+        Ssc[buf][t] = scK;
+        Ssc[buf][4 + t] = scV;
+      }
     }
   };
   // Prompt V: thread (kg, dg) moves keys 4kg..4kg+3 of d-granule dg,
@@ -368,10 +384,10 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
         const int e = btab[kb];
         if constexpr (FP8) {
           const uint2 x = *(const uint2*)(vpool8 + e * slab8 + rr * kBlock + 8 * h);
-          sreg[c0] = u32x4{x.x, x.y, __float_as_uint(cv.vs[sc0 + (int64_t)e * n_kv]), 0u};
+          sreg[c0] = u32x4{x.x, x.y, 0u, 0u};
         } else if constexpr (I4) {
           const uint32_t x = *(const uint32_t*)(vpool8 + e * slab8 + rr * (kBlock / 2) + 4 * h);
-          sreg[c0] = u32x4{x, 0u, __float_as_uint(cv.vs[sc0 + (int64_t)e * n_kv]), 0u};
+          sreg[c0] = u32x4{x, 0u, 0u, 0u};
         } else {
           const uint16_t* sl = vpool + e * slab;
           sreg[c0] = *(const u32x4*)(sl + rr * kBlock + 8 * h);
@@ -397,8 +413,8 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
         const int c = t + 256 * c0, rr = c >> 3, j = (c >> 1) & 3, h = c & 1;
         const int nvalid = L - (BN * i + kBlock * j + 8 * h);   // keys of the chunk below L
         u32x4 x = sreg[c0];
-        if constexpr (FP8) x = widen8(x[0], x[1], __uint_as_float(x[2]));
-        if constexpr (I4) x = widen8_i4(x[0], __uint_as_float(x[2]));
+        if constexpr (FP8) x = widen8(x[0], x[1]);
+        if constexpr (I4) x = widen8_i4(x[0]);
         if (nvalid < 8) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -450,8 +466,20 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
     interleave_lds_mfma<2 * KS, 3>();
   };
   // online softmax of tile i, first half: mask, row max, rescale of O and l
+  float vsc_r[4] = {1.f, 1.f, 1.f, 1.f};             // scaled caches: V scales of tile i
   auto rowmax = [&](int i) {
     const int k0 = BN * tile_of(i);
+    if constexpr (SC != 0) {
+      // scores of the keys of block j (elements jj < 2 of sacc[st]: block
+      // 2 st, jj >= 2: block 2 st + 1) times that block's K scale
+      const float* sc = Ssc[i & 1];
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[st][e] *= sc[2 * st + ((e >> 2) >= 2 ? 1 : 0)];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vsc_r[j] = sc[4 + j];
+    }
     // the tile reaches past the wave's first row, or (window) holds a
     // non-sink key at or before the last row's window start
     const bool diag = k0 + BN - 1 > pw;
@@ -501,13 +529,22 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[st][8 * kb + e], sl2, -msub));
+        if constexpr (SC != 0) {                       // l: unscaled; PV: times the V scale
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            lsum += p[e];
+            p[e] *= vsc_r[2 * st + kb];
+          }
+        }
         pop[2 * st + kb] = pack8<OpT>(p);
       }
   };
   // l += row sums of P_i; O^T += V^T P^T of tile i over 4 k-steps of 16 keys
   auto pv = [&](int i) {
+    if constexpr (SC == 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) lsum = sum8(pop[j], lsum);
+      for (int j = 0; j < 4; ++j) lsum = sum8(pop[j], lsum);
+    }
     const int buf = i & 1, t = opaque_tid(), c = t & 31, h = (t >> 5) & 1;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
