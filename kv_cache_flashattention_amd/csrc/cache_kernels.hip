@@ -198,16 +198,47 @@ __global__ __launch_bounds__(256) void k_write_copy(CacheView cv, int layer, con
   const int64_t base = slab_elems(cv, layer, blk, h);
   E* K = (E*)cv.k + base;
   E* V = (E*)cv.v + base;
-  for (int i = threadIdx.x; i < (p1 - p0) * d; i += blockDim.x) {
-    const int p = p0 + i / d, j = i % d;
-    const int64_t src = (((int64_t)b * T + (p - start)) * cv.n_kv + h) * d + j;
-    K[(p % kBlock) * d + j] = kin[src];
-    vt[(p % kBlock) * d + j] = vin[src];
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < d * kBlock; i += blockDim.x) {
-    const int j = i / kBlock, r = i % kBlock, p = lb * kBlock + r;
-    if (p >= p0 && p < p1) V[j * kBlock + r] = vt[r * d + j];
+  if constexpr (sizeof(E) == 2) {
+    // 16-bit rows move in 16-byte chunks (8 values): K straight to its slab
+    // rows, V into a padded LDS tile, then out as 16-byte columns of 8 tokens
+    // (element by element where the 8 tokens straddle the written range).
+    __shared__ __attribute__((aligned(16))) uint16_t vt2[kBlock][128 + 8];
+    const int G8 = d / 8;
+    for (int i = threadIdx.x; i < kBlock * G8; i += blockDim.x) {
+      const int r = i / G8, gk = i % G8, p = lb * kBlock + r;
+      if (p >= p0 && p < p1) {
+        const int64_t src = (((int64_t)b * T + (p - start)) * cv.n_kv + h) * d + 8 * gk;
+        *(uint4*)(K + r * d + 8 * gk) = *(const uint4*)(kin + src);
+        *(uint4*)&vt2[r][8 * gk] = *(const uint4*)(vin + src);
+      }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < d * 2; i += blockDim.x) {
+      const int j = i >> 1, r0 = 8 * (i & 1), pr = lb * kBlock + r0;
+      if (pr >= p0 && pr + 8 <= p1) {
+        uint4 x;
+        x.x = (uint32_t)vt2[r0][j] | ((uint32_t)vt2[r0 + 1][j] << 16);
+        x.y = (uint32_t)vt2[r0 + 2][j] | ((uint32_t)vt2[r0 + 3][j] << 16);
+        x.z = (uint32_t)vt2[r0 + 4][j] | ((uint32_t)vt2[r0 + 5][j] << 16);
+        x.w = (uint32_t)vt2[r0 + 6][j] | ((uint32_t)vt2[r0 + 7][j] << 16);
+        *(uint4*)(V + j * kBlock + r0) = x;
+      } else {
+        for (int e = 0; e < 8; ++e)
+          if (pr + e >= p0 && pr + e < p1) V[j * kBlock + r0 + e] = vt2[r0 + e][j];
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < (p1 - p0) * d; i += blockDim.x) {
+      const int p = p0 + i / d, j = i % d;
+      const int64_t src = (((int64_t)b * T + (p - start)) * cv.n_kv + h) * d + j;
+      K[(p % kBlock) * d + j] = kin[src];
+      vt[(p % kBlock) * d + j] = vin[src];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < d * kBlock; i += blockDim.x) {
+      const int j = i / kBlock, r = i % kBlock, p = lb * kBlock + r;
+      if (p >= p0 && p < p1) V[j * kBlock + r] = vt[r * d + j];
+    }
   }
 }
 
