@@ -496,23 +496,36 @@ def bench_prefix_share(torch, kv, n_seq=40, prompt=600, n_layers=32):
     cache shape: 32 layers, 8 kv heads of 128, bf16).  Sharing holds the
     prompt's 38 blocks once; the first grow of every sequence copies the
     shared, partly filled last block (copy-on-write).  Reports the blocks
-    held and the copy kernel's rate (bytes copied / GPU time of the grow)."""
+    held and the copy kernel's rate (bytes copied / GPU time of the grow,
+    median of 7 repetitions after 3 untimed ones)."""
     n_kv, d = 8, 128
     nb_prompt = -(-prompt // 16)
     c = kv.KvCache(n_layers, 32, n_kv, d, nb_prompt + 2 * n_seq + 8, n_seq + 1, nb_prompt + 4,
                    "bf16")
     c.seq_alloc(0, prompt)
-    for s in range(1, n_seq + 1):
-        c.seq_share_prefix(0, s, prompt)
-    held = c.cfg.n_blocks - c.free_blocks()
     stream = torch.cuda.current_stream()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record(stream)
-    c.seq_grow(list(range(1, n_seq + 1)))
-    b.record(stream)
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) * 1e3
+    held = None
+
+    def share_grow_release():
+        """Share the prompt with every sequence, time their first grow (the
+        block copies), release them again."""
+        nonlocal held
+        for s in range(1, n_seq + 1):
+            c.seq_share_prefix(0, s, prompt)
+        held = c.cfg.n_blocks - c.free_blocks()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        c.seq_grow(list(range(1, n_seq + 1)))
+        b.record(stream)
+        torch.cuda.synchronize()
+        for s in range(1, n_seq + 1):
+            c.seq_release(s)
+        return a.elapsed_time(b) * 1e3
+
+    for _ in range(3):                                         # kernels loaded, clocks up
+        share_grow_release()
+    us = float(np.median([share_grow_release() for _ in range(7)]))
     copied = n_seq * n_layers * 2 * n_kv * 16 * d * 2          # K and V of each copied block
     return {"workload": f"{n_seq} sequences sharing a {prompt}-token prompt, Llama-8B cache shape "
                         f"({n_layers} layers, {n_kv} kv heads of {d}, bf16)",

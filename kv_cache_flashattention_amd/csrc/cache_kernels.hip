@@ -88,9 +88,26 @@ __global__ __launch_bounds__(256) void k_copy_blocks(CacheView cv, BlockCopy u) 
   const uint4* vs = (const uint4*)((const uint8_t*)cv.v + so);
   uint4* kd = (uint4*)((uint8_t*)cv.k + dof);
   uint4* vd = (uint4*)((uint8_t*)cv.v + dof);
-  for (int64_t i = threadIdx.x; i < bytes / 16; i += blockDim.x) {
-    kd[i] = ks[i];
-    vd[i] = vs[i];
+  // eight 16-byte chunks of K and of V in flight per thread before the stores
+  const int64_t n16 = bytes / 16;
+  for (int64_t i0 = threadIdx.x; i0 < n16; i0 += 8 * (int64_t)blockDim.x) {
+    uint4 a[8], c[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = i0 + u * (int64_t)blockDim.x;
+      if (i < n16) {
+        a[u] = ks[i];
+        c[u] = vs[i];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = i0 + u * (int64_t)blockDim.x;
+      if (i < n16) {
+        kd[i] = a[u];
+        vd[i] = c[u];
+      }
+    }
   }
   if (has_scales(cv.dtype) && threadIdx.x < cv.n_kv) {
     const int64_t s0 = ((int64_t)layer * cv.n_blocks + src) * cv.n_kv + threadIdx.x;
