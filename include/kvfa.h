@@ -54,7 +54,10 @@
  * Conventions.  Every function returns KVC_OK (0) or a negative status and
  * never throws; kvc_last_error() gives a message for the calling thread.
  * The caller owns all device memory (pools, tables, inputs, outputs,
- * workspace) and all streams; a handle owns only host metadata.  Pointers
+ * workspace) and all streams it passes; a handle owns host metadata and,
+ * when it has device buffers, one internal stream and two events (made by
+ * kvc_create, released by kvc_destroy) on which kvc_attn_prefill runs its
+ * cache write beside the attention kernel.  Pointers
  * named *_dev are device pointers, *_host host pointers.  Work is enqueued
  * asynchronously on the given stream (0 = the default stream); argument
  * errors are detected before anything is enqueued, launch failures give
@@ -217,8 +220,10 @@ int kvc_write(kvc_cache* cache, int32_t layer, int32_t n, const int32_t* seqs_de
  * k_dev, v_dev [n][T][n_kv_heads][d_head], out_dev [n][T][n_q_heads][d_head],
  * all in the io type.  When seqs_dev is not NULL the prompt's K/V rows are
  * also stored as positions 0..T-1 of those sequences (as kvc_write with
- * start 0; each sequence needs length >= T).  seqs_dev == NULL: attention
- * only.  scale is the score multiplier (1/sqrt(d_head) in the pages); it
+ * start 0; each sequence needs length >= T), by a write that runs on the
+ * handle's internal stream beside the attention kernel and is joined back
+ * into `stream` before the call returns (later work on `stream` sees the
+ * rows).  seqs_dev == NULL: attention only.  scale is the score multiplier (1/sqrt(d_head) in the pages); it
  * must be finite and > 0 (KVC_E_INVAL otherwise): the kernels take each row
  * maximum on unscaled scores. */
 int kvc_attn_prefill(kvc_cache* cache, int32_t layer, int32_t n, const int32_t* seqs_dev,

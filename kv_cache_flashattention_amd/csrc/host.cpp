@@ -37,6 +37,17 @@ struct kvc_cache {
   std::vector<uint8_t> live;                    // per sequence
   std::vector<int32_t> refs;                    // per block: sequences holding it (0 = free)
   int32_t cu_count = 256;                       // compute units of the device (decode plan)
+  // A prompt's cache write runs on `side`, beside the attention kernel on the
+  // caller's stream: fork / join events order it after the caller's earlier
+  // work and before its later work.  Created with the handle (not during a
+  // call, which may be under graph capture).
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  ~kvc_cache() {
+    if (fork) (void)hipEventDestroy(fork);
+    if (join) (void)hipEventDestroy(join);
+    if (side) (void)hipStreamDestroy(side);
+  }
   CacheView view() const {
     CacheView v{};
     v.k = dev.k_pool;
@@ -247,7 +258,14 @@ int kvc_create(const kvc_config* cfg, const kvc_buffers* dev, hipStream_t stream
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess &&
         cus > 0)
       c->cu_count = cus;
-    hipError_t e = launch_fill_tables(c->view(), stream);
+    hipError_t e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->join, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      delete c;
+      return hip_fail(e, "side stream / events");
+    }
+    e = launch_fill_tables(c->view(), stream);
     if (e != hipSuccess) {
       delete c;
       return hip_fail(e, "table fill launch");
@@ -529,9 +547,19 @@ int kvc_attn_prefill_window(kvc_cache* c, int32_t layer, int32_t n, const int32_
     return fail(KVC_E_INVAL, "q/k/v/out must be 16-byte aligned");
   if (seqs && (int64_t)T > (int64_t)c->cfg.max_blocks_per_seq * kBlock)
     return fail(KVC_E_INVAL, "prompt longer than the table width");
+  // The cache write (HBM-bound) and the attention (matrix-core-bound) read the
+  // same inputs and write disjoint outputs, so they run side by side: the
+  // write on the handle's side stream, forked from and joined back into the
+  // caller's stream.
   hipError_t e = hipSuccess;
-  if (seqs) e = launch_write(c->view(), layer, n, seqs, 0, T, k, v, stream);
+  if (seqs) {
+    e = hipEventRecord(c->fork, stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(c->side, c->fork, 0);
+    if (e == hipSuccess) e = launch_write(c->view(), layer, n, seqs, 0, T, k, v, c->side);
+    if (e == hipSuccess) e = hipEventRecord(c->join, c->side);
+  }
   if (e == hipSuccess) e = launch_prefill(c->view(), n, T, q, k, v, out, scale, window, sinks, stream);
+  if (seqs && e == hipSuccess) e = hipStreamWaitEvent(stream, c->join, 0);
   return e == hipSuccess ? KVC_OK : hip_fail(e, "prefill launch");
 }
 

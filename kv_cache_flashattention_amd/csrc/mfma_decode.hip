@@ -262,6 +262,7 @@ __global__ __launch_bounds__(256, APPEND ? 1 : 2) void k_decode_work(CacheView c
   constexpr int64_t SB = KV == KV_INT4 ? kBlock * D / 2 : kBlock * D * EB;   // slab bytes
   __shared__ int64_t s_units[kMaxBatch + 1];
   __shared__ int32_t s_counts[kMaxBatch];
+  __shared__ int32_t s_seq[kMaxBatch], s_len[kMaxBatch];   // each entry's sequence and length
   __shared__ int64_t s_wsum[4];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
@@ -278,9 +279,12 @@ __global__ __launch_bounds__(256, APPEND ? 1 : 2) void k_decode_work(CacheView c
       const int b = tid * 8 + i;
       int c = 0;
       if (b < nb) {
-        const int L = valid_len(cv, seqs[b]);
+        const int sq = seqs[b];
+        const int L = valid_len(cv, sq);
         c = L > 0 ? UnitMap(L, window, sinks).count : 0;
         s_counts[b] = c;
+        s_seq[b] = sq;
+        s_len[b] = L;
       }
       loc[i] = (int64_t)c * nkvg;
       tsum += loc[i];
@@ -342,8 +346,8 @@ __global__ __launch_bounds__(256, APPEND ? 1 : 2) void k_decode_work(CacheView c
     const int64_t pend = u1 < segend ? u1 : segend;
     const int c1 = c0 + (int)(pend - u);
     const int kvh = kvg / qgroups, qg = kvg % qgroups;
-    const int seq = uni(seqs[b]);
-    const int L = uni(valid_len(cv, seq));             // > 0: the entry has units
+    const int seq = uni(s_seq[b]);
+    const int L = uni(s_len[b]);                       // > 0: the entry has units
     const UnitMap umap(L, window, sinks);
     // APPEND: the newest row of this (sequence, kv head), and the last unit
     // (the one holding position L-1) of the segment's visible units
