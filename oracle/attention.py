@@ -96,25 +96,46 @@ def gqa_attention(q, k, v, scale, q_pos=None, window=0, sinks=0):
     return out
 
 
+def tile_summary(block):
+    """The softmax summary of one tile of scores on its own: its maximum m_t
+    and l_t = sum over the tile of exp(x - m_t)."""
+    m_t = max(block)
+    return m_t, sum(math.exp(x - m_t) for x in block)
+
+
+def combine_summaries(a, b):
+    """Two (m, l) summaries of disjoint score sets -> the summary of their union.
+
+    Both sums are brought to the common maximum M = max(m_a, m_b): a sum taken
+    against m is multiplied by exp(m - M), the correction [KVFA] (online
+    softmax section) and [DF] (running-summary paragraph) apply whenever the
+    running maximum rises.  The empty summary (-inf, 0) is the identity: its
+    factor is taken as 0, since exp(-inf - M) is 0.
+    """
+    (m_a, l_a), (m_b, l_b) = a, b
+    M = max(m_a, m_b)
+    if M == -math.inf:
+        return M, 0.0
+    f_a = 0.0 if m_a == -math.inf else math.exp(m_a - M)
+    f_b = 0.0 if m_b == -math.inf else math.exp(m_b - M)
+    return M, l_a * f_a + l_b * f_b
+
+
 def online_softmax_trace(scores, tile):
     """Single pass over a row of scores in tiles, keeping (m, l).
 
-    After each tile the running maximum m grows to cover the tile and the
-    running sum l, which was measured against the old maximum, is multiplied
-    by exp(m_old - m_new) before the tile's own exp(x - m_new) terms are added
-    ([KVFA] online softmax section; [DF] running-summary paragraph).  Before
-    any tile m is -inf and l is 0, and the rescale factor of that empty state
-    is taken as 0.  Returns the list of (m, l) after each tile.
+    The running state starts as the empty summary (-inf, 0); each tile's own
+    summary is folded into it with ``combine_summaries``, so after tile t the
+    state is the (max, sum of exp(x - max)) of every score seen so far,
+    without the earlier scores being revisited ([KVFA] online softmax
+    section; [DF] running-summary paragraph; [KPF] worked example in "Flash
+    attention").  Returns the state after each tile.
     """
-    m, l = -math.inf, 0.0
+    state = (-math.inf, 0.0)
     trace = []
-    for s in range(0, len(scores), tile):
-        block = [float(x) for x in scores[s:s + tile]]
-        m_new = max([m] + block)
-        rescale = math.exp(m - m_new) if m != -math.inf else 0.0
-        l = l * rescale + sum(math.exp(x - m_new) for x in block)
-        m = m_new
-        trace.append((m, l))
+    for t0 in range(0, len(scores), tile):
+        state = combine_summaries(state, tile_summary([float(x) for x in scores[t0:t0 + tile]]))
+        trace.append(state)
     return trace
 
 

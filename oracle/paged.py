@@ -71,10 +71,15 @@ class PagedCacheModel:
         return b
 
     def alloc(self, seq, n_tokens):
-        n = -(-n_tokens // BLOCK)                      # ceil-div
-        if n > len(self.free):
+        """Make seq live with n_tokens rows: as many blocks as it takes to
+        hold them, i.e. the least count c with 16 c >= n_tokens."""
+        count = (n_tokens + BLOCK - 1) // BLOCK
+        if count > len(self.free):
             raise MemoryError("no free blocks")
-        self.table[seq] = [self._take() for _ in range(n)]
+        blocks = []
+        while len(blocks) < count:
+            blocks.append(self._take())
+        self.table[seq] = blocks
         self.length[seq] = n_tokens
 
     def _shared_partial(self, s):
@@ -112,12 +117,14 @@ class PagedCacheModel:
             self.grow([seq])
 
     def share_prefix(self, src, dst, prefix_len):
-        """dst holds the first prefix_len rows of src through the same blocks."""
+        """dst holds the first prefix_len rows of src through the same blocks:
+        its table lists the blocks of src that hold positions 0 .. prefix_len-1,
+        and each of them gains one holder."""
         assert dst not in self.table and 0 <= prefix_len <= self.length[src]
-        n = -(-prefix_len // BLOCK)
-        self.table[dst] = self.table[src][:n].copy()
-        for b in self.table[dst]:
+        held = [self.physical(src, p)[0] for p in range(0, prefix_len, BLOCK)]
+        for b in held:
             self.refs[b] += 1
+        self.table[dst] = held
         self.length[dst] = prefix_len
 
     def release(self, seq):

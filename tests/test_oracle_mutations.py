@@ -9,35 +9,41 @@ from oracle import attention as A
 from oracle import codecs as C
 
 
+def _fold(scores, tile, combine):
+    """online_softmax_trace with a planted combine rule."""
+    state, tr = (-math.inf, 0.0), []
+    for t0 in range(0, len(scores), tile):
+        state = combine(state, A.tile_summary([float(x) for x in scores[t0:t0 + tile]]))
+        tr.append(state)
+    return tr
+
+
 def test_online_softmax_without_rescale_is_caught():
-    def no_rescale(scores, tile):
-        m, l, tr = -math.inf, 0.0, []
-        for s in range(0, len(scores), tile):
-            block = list(scores[s:s + tile])
-            m = max([m] + block)
-            l = l + sum(math.exp(x - m) for x in block)      # old l not rescaled
-            tr.append((m, l))
-        return tr
-    assert not pins.check_worked_example(no_rescale)
+    def no_rescale(a, b):                              # sums added without the exp factors
+        return max(a[0], b[0]), a[1] + b[1]
+    assert not pins.check_worked_example(lambda s, t: _fold(s, t, no_rescale))
 
 
 def test_online_softmax_wrong_sign_is_caught():
-    def wrong_sign(scores, tile):
-        m, l, tr = -math.inf, 0.0, []
-        for s in range(0, len(scores), tile):
-            block = list(scores[s:s + tile])
-            m_new = max([m] + block)
-            f = math.exp(m_new - m) if m != -math.inf else 0.0   # exp(m_new - m_old)
-            l = l * f + sum(math.exp(x - m_new) for x in block)
-            m = m_new
-            tr.append((m, l))
-        return tr
-    assert not pins.check_worked_example(wrong_sign)
+    def wrong_sign(a, b):                              # exp(M - m) instead of exp(m - M)
+        M = max(a[0], b[0])
+        fa = math.exp(M - a[0]) if a[0] != -math.inf else 0.0
+        fb = math.exp(M - b[0]) if b[0] != -math.inf else 0.0
+        return M, a[1] * fa + b[1] * fb
+    assert not pins.check_worked_example(lambda s, t: _fold(s, t, wrong_sign))
 
     def online(scores, tile):
-        m, l = wrong_sign(scores, tile)[-1]
+        m, l = _fold(scores, tile, wrong_sign)[-1]
         return np.array([math.exp(x - m) / l for x in scores])
     assert not pins.check_online_every_split(online)
+
+
+def test_online_softmax_stale_maximum_is_caught():
+    def stale_max(a, b):                               # keeps the first tile's maximum
+        if a[0] == -math.inf:
+            return b
+        return a[0], a[1] + b[1] * math.exp(b[0] - a[0])
+    assert not pins.check_worked_example(lambda s, t: _fold(s, t, stale_max))
 
 
 def test_missing_scale_is_caught():
