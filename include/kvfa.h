@@ -144,14 +144,16 @@ int kvc_create(const kvc_config* cfg, const kvc_buffers* dev, hipStream_t stream
 int kvc_destroy(kvc_cache* cache);
 
 /* Make `seq` live with n_tokens tokens: ceil(n_tokens / 16) blocks popped from
- * the free list (the page's allocate).  The rows themselves are written later
+ * the free list (kvcache-7e2, PagedAttention section: `allocate` takes
+ * ceil(n / 16) blocks for a new sequence).  The rows themselves are written later
  * (kvc_write, kvc_attn_prefill).  KVC_E_STATE if seq is already live,
  * KVC_E_NO_BLOCKS if the free list is too short (state unchanged). */
 int kvc_seq_alloc(kvc_cache* cache, int32_t seq, int32_t n_tokens, hipStream_t stream);
 
-/* Grow each of n live sequences by one token (the page's append_token): a
- * sequence whose length is a multiple of 16 first takes one block from the
- * free list.  Ids must be distinct.  All-or-nothing: KVC_E_NO_BLOCKS leaves
+/* Grow each of n live sequences by one token (kvcache-7e2, PagedAttention
+ * section: `append_token` takes a new block only when the sequence's length
+ * is a multiple of 16, i.e. its last block is full): a sequence whose length
+ * is a multiple of 16 first takes one block from the free list.  Ids must be distinct.  All-or-nothing: KVC_E_NO_BLOCKS leaves
  * every sequence as it was.  The device copy of the table and lengths is
  * updated on `stream`. */
 int kvc_seq_grow(kvc_cache* cache, int32_t n, const int32_t* seqs_host, hipStream_t stream);
@@ -162,13 +164,15 @@ int kvc_seq_grow(kvc_cache* cache, int32_t n, const int32_t* seqs_host, hipStrea
  * All or nothing: KVC_E_NO_BLOCKS or KVC_E_INVAL leave the state unchanged. */
 int kvc_seq_grow_by(kvc_cache* cache, int32_t seq, int32_t n_tokens, hipStream_t stream);
 
-/* Return all blocks of `seq` to the free list, in table order (the page's
- * release), and mark it not live (device length 0, table entries -1). */
+/* Return all blocks of `seq` to the free list, in table order (kvcache-7e2,
+ * PagedAttention section: `release` hands every block of a finished sequence
+ * back), and mark it not live (device length 0, table entries -1). */
 int kvc_seq_release(kvc_cache* cache, int32_t seq, hipStream_t stream);
 
-/* Prefix sharing (kvcache-7e2 PagedAttention `share_prefix`; kvcache-7e2 and
- * abhishekpatel.co: sequences with a common beginning point at the same
- * physical blocks, copying only when one of them would change a block).
+/* Prefix sharing (kvcache-7e2, PagedAttention section, `share_prefix`;
+ * abhishekpatel, "Paged attention: stop reserving empty tables": sequences
+ * that start alike refer to the same physical blocks, and a block is
+ * duplicated only when a write would alter it).
  * `dst` (not live) becomes live holding the first prefix_len rows of `src`
  * (live, 0 <= prefix_len <= len(src)) by sharing its first
  * ceil(prefix_len/16) blocks; no data moves.  Every block counts the
@@ -198,7 +202,12 @@ int kvc_seq_blocks(const kvc_cache* cache, int32_t seq, int32_t* blocks_host, in
 int kvc_free_blocks(const kvc_cache* cache, int32_t* out);
 
 /* kv_append: store the newest token's K and V rows of one layer for each of n
- * sequences, at position seq_len[seq] - 1 (call kvc_seq_grow first).
+ * sequences, at position seq_len[seq] - 1 (call kvc_seq_grow first).  Each
+ * decoded token adds exactly one K row and one V row per layer to its
+ * sequence's cache before its query attends (kvcache-7e2, KV cache section;
+ * deepforge, first section; abhishekpatel, "Following one new token through
+ * the cache").  The row lands in slot (len-1) % 16 of block
+ * table[(len-1) / 16] (kvcache-7e2, PagedAttention section, `physical`).
  * k_dev, v_dev: [n][n_kv_heads][d_head] in the io type.  16/32-bit caches
  * store the bits unchanged; fp8 and int4 caches apply their scale rule. */
 int kvc_append(kvc_cache* cache, int32_t layer, int32_t n, const int32_t* seqs_dev,
@@ -239,9 +248,12 @@ int kvc_attn_prefill(kvc_cache* cache, int32_t layer, int32_t n, const int32_t* 
  * prefills split into chunks), or the target's pass over T drafted tokens
  * (kvcache-7e2 speculative-decoding section).  q_dev, out_dev:
  * [n][T][n_q_heads][d_head] in the io type, 16-byte aligned.  bf16, f16,
- * fp8 and int4 caches (KVC_E_UNSUPPORTED for f32); for fp8 and int4 each
- * cached value is taken as bf16(decode(code) * block scale).  scale finite
- * and > 0.
+ * fp8 and int4 caches (KVC_E_UNSUPPORTED for f32).  For fp8 and int4 the
+ * stored codes are used exactly (every E4M3FN value and every int4 code is
+ * a bf16 value); each block's K scale multiplies the scores of that block's
+ * keys, its V scale multiplies their probabilities before they are rounded
+ * to bf16 for the PV product, and the row sum adds the unscaled
+ * probabilities in fp32.  scale finite and > 0.
  * A device
  * entry that is out of range, has len < T, or whose table holds an invalid
  * block id among its first ceil(len/16) entries gets NaN rows.  No
@@ -257,7 +269,15 @@ int kvc_decode_workspace_bytes(const kvc_cache* cache, int32_t n, int32_t num_sp
                                uint64_t* out);
 
 /* attn_decode: one query row per sequence against all of its cached rows
- * (every row visible: the newest token's own row was appended first).
+ * (every row visible: the newest token's own row was appended first), the
+ * step the cache exists for: the new token's query against the stored K and
+ * V instead of recomputing them (kvcache-7e2, naive decoding and KV cache
+ * sections; abhishekpatel, "Following one new token through the cache").
+ * The rows are read through the block table (kvcache-7e2, PagedAttention
+ * section: the kernel gathers K and V from the physical blocks when it
+ * attends), once per group of query heads sharing a kv head; the pass is
+ * bound by how fast the cache can be read (deepforge: decoding is
+ * memory-bound).
  * q_dev, out_dev: [n][n_q_heads][d_head] in the io type.  Long contexts are
  * cut into splits swept in parallel, each keeping its own (m, l, O), and
  * merged afterwards with weights exp(m_s - max m) -- the online softmax's
@@ -307,8 +327,11 @@ int kvc_attn_decode_append(kvc_cache* cache, int32_t layer, int32_t n, const int
                            int32_t num_splits, void* ws_dev, uint64_t ws_bytes,
                            hipStream_t stream);
 
-/* Block-table gather: copy the stored bit patterns of positions start ..
- * start+count-1 of `seq` in logical order into k_out_dev, v_out_dev, each
+/* Block-table gather (kvcache-7e2, PagedAttention section: `physical` maps
+ * a logical position p to (table[p / 16], p % 16), and attention gathers K
+ * and V from those physical blocks): copy the stored bit patterns of
+ * positions start .. start+count-1 of `seq` in logical order into
+ * k_out_dev, v_out_dev, each
  * [count][n_kv_heads][d_head] of the storage type (fp8: raw codes; int4:
  * [count][n_kv_heads][d_head / 2] bytes, codes packed along d_head as in
  * the pools' K rows, for V as well). */

@@ -109,11 +109,13 @@ __global__ __launch_bounds__(256) void k_copy_blocks(CacheView cv, BlockCopy u) 
       }
     }
   }
-  if (has_scales(cv.dtype) && threadIdx.x < cv.n_kv) {
-    const int64_t s0 = ((int64_t)layer * cv.n_blocks + src) * cv.n_kv + threadIdx.x;
-    const int64_t d0 = ((int64_t)layer * cv.n_blocks + dst) * cv.n_kv + threadIdx.x;
-    cv.ks[d0] = cv.ks[s0];
-    cv.vs[d0] = cv.vs[s0];
+  if (has_scales(cv.dtype)) {
+    for (int h = threadIdx.x; h < cv.n_kv; h += blockDim.x) {
+      const int64_t s0 = ((int64_t)layer * cv.n_blocks + src) * cv.n_kv + h;
+      const int64_t d0 = ((int64_t)layer * cv.n_blocks + dst) * cv.n_kv + h;
+      cv.ks[d0] = cv.ks[s0];
+      cv.vs[d0] = cv.vs[s0];
+    }
   }
 }
 

@@ -10,9 +10,11 @@
 // (kvcache-7e2 PagedAttention `share_prefix`); each block counts the
 // sequences holding it, and a release returns only the blocks nobody holds
 // any more.  A shared block is copied before a sequence writes into it
-// (abhishekpatel.co: blocks are shared "copying only if one of them would
-// change a block"): a grow whose new rows land in a shared, partly filled
-// last block first gives the growing sequence its own copy.  Every change
+// ("KV cache, paged, flash and sparse attention" (abhishekpatel), "Paged
+// attention: stop reserving empty tables": sharing stays safe because a block
+// is duplicated only when a write would alter it): a grow whose new rows land
+// in a shared, partly filled last block first gives the growing sequence its
+// own copy.  Every change
 // is mirrored to the caller's device tables by a small
 // kernel whose arguments carry the changed entries, enqueued on the caller's
 // stream, so attention kernels later on that stream see it.
@@ -552,14 +554,24 @@ int kvc_attn_prefill_window(kvc_cache* c, int32_t layer, int32_t n, const int32_
   // write on the handle's side stream, forked from and joined back into the
   // caller's stream.
   hipError_t e = hipSuccess;
+  bool forked = false;
   if (seqs) {
     e = hipEventRecord(c->fork, stream);
     if (e == hipSuccess) e = hipStreamWaitEvent(c->side, c->fork, 0);
-    if (e == hipSuccess) e = launch_write(c->view(), layer, n, seqs, 0, T, k, v, c->side);
-    if (e == hipSuccess) e = hipEventRecord(c->join, c->side);
+    if (e == hipSuccess) {
+      forked = true;
+      e = launch_write(c->view(), layer, n, seqs, 0, T, k, v, c->side);
+    }
   }
   if (e == hipSuccess) e = launch_prefill(c->view(), n, T, q, k, v, out, scale, window, sinks, stream);
-  if (seqs && e == hipSuccess) e = hipStreamWaitEvent(stream, c->join, 0);
+  if (forked) {
+    // Whatever failed above, the caller's stream waits for everything enqueued
+    // on the side stream, which may still read k and v.
+    hipError_t j = hipEventRecord(c->join, c->side);
+    if (j == hipSuccess) j = hipStreamWaitEvent(stream, c->join, 0);
+    if (j != hipSuccess) j = hipStreamSynchronize(c->side);
+    if (e == hipSuccess) e = j;
+  }
   return e == hipSuccess ? KVC_OK : hip_fail(e, "prefill launch");
 }
 
