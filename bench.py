@@ -2,23 +2,29 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
 
-Default workload: the Llama-3-8B-shaped decode step -- 40 sequences, 32 query
-and 8 kv heads of 128, bf16 cache in 16-token blocks behind shuffled block
-tables, context lengths uniform in [512, 4096].  One step is one pass of the
-decode hot path over that batch: grow every sequence by one token (host
-allocator + table update), then kvc_attn_decode_append: kv_append of the new
-K/V rows and attn_decode (split-context partials and their (m, l) merge) in
-one call, the append fused into the decode kernel for bf16 caches.  The headline `value` is
-the decode's algorithmic HBM bytes per step (K/V rows read through the
-tables, queries, outputs, table entries) divided by the wall-clock time per
-step.  The same JSON line carries a `prefill` object for the causal-prefill
-workload (4 x 8,192 tokens, 32/8 heads of 128, bf16) and an `extend` object
-for chunked prefill (the last 512-token chunk of those prompts against the
-7,680 rows already cached), both in algorithmic TFLOP/s, and a
-`decode_window` object: the decode batch under a 1,024-row sliding window
-with 4 sink rows, in GB/s of the rows it can see; `prefix_share` (blocks and
-copy-on-write bytes of 40 sequences sharing a prompt) and `decode_int4` (the
-70B-shaped decode on an int4 cache).
+Default workload (the headline): the Llama-3-8B-shaped decode step -- 40
+sequences, 32 query and 8 kv heads of 128, bf16 cache in 16-token blocks
+behind shuffled block tables, context lengths uniform in [512, 4096].  One
+step is one pass of the decode hot path over that batch: grow every sequence
+by one token (host allocator + table update), then kvc_attn_decode_append:
+kv_append of the new K/V rows and attn_decode (work-list partials and their
+(m, l) merge) in one call, the append fused into the decode kernel for 16-bit
+caches.  The headline `value` is the decode's algorithmic HBM bytes per step
+(K/V rows read through the tables, queries, outputs, table entries) divided
+by the wall-clock time per step.
+
+The same JSON line carries one object per other workload, each with its own
+`roofline` (and, where the oracle is timed, `cpu_baseline`):
+  prefill               causal prefill, 4 x 8,192 tokens, 32/8 heads of 128,
+                        bf16, K/V appended to the cache (TFLOP/s)
+  decode_llama70b_bf16  8 x 32,768-token contexts, 64/8 heads, bf16 cache
+  decode_llama70b_fp8   the same rows on an fp8-e4m3 cache with block scales
+  decode_long_mha       one 128,000-token context, 32/32 heads, fp16 cache
+  decode_int4           the 70B-shaped rows on an int4 cache
+  extend                chunked prefill: the last 512-token chunk of the
+                        prefill prompts against the 7,680 rows cached before
+  decode_window         the headline batch under a 1,024-row window + 4 sinks
+  prefix_share          40 sequences sharing a 600-token prompt
 
 `roofline` is measured for the dominant call of each workload with HIP
 events recorded on the stream the library launches on: for decode, the same
@@ -111,6 +117,32 @@ def warm_up_clocks(call, torch, seconds=0.05):
 
 
 # ---------------------------------------------------------------- decode
+# Source rows of the decode workloads, rounded to the io type on the host,
+# kept for the run: the three 70B-shaped legs (bf16, fp8 and int4 caches)
+# read the same rows, and the CPU baseline takes its float64 inputs from them.
+_ROWS = {}
+
+
+def source_rows(w, b, torch, io):
+    """All L_b rows of sequence b of workload w, as host tensors of the io
+    type [L, n_kv, d] (drawn once per (rows tag, sequence))."""
+    key = (w.tag, w.seed, b, str(io))
+    if key not in _ROWS:
+        L = int(w.lengths[b])
+        ks, vs = [], []
+        for s0 in range(0, L, 8192):
+            k, v = w.kv_rows(b, s0, min(8192, L - s0))
+            ks.append(torch.from_numpy(k).to(io))
+            vs.append(torch.from_numpy(v).to(io))
+        _ROWS[key] = (torch.cat(ks), torch.cat(vs))
+    return _ROWS[key]
+
+
+def drop_rows(tag):
+    for key in [k for k in _ROWS if k[0] == tag]:
+        del _ROWS[key]
+
+
 def build_decode(name, torch, kv):
     from workloads import decode_workload
     w = decode_workload(name)
@@ -123,13 +155,11 @@ def build_decode(name, torch, kv):
     for b in range(w.batch):
         c.set_block_table(b, tables[b], int(w.lengths[b]))
     for b in range(w.batch):
-        L = int(w.lengths[b])
+        K, V = source_rows(w, b, torch, io)
         sel = torch.tensor([b], dtype=torch.int32, device="cuda")
-        for s0 in range(0, L, 8192):
-            n = min(8192, L - s0)
-            k, v = w.kv_rows(b, s0, n)
-            c.write(0, sel, s0, torch.from_numpy(k).to(io).cuda()[None],
-                    torch.from_numpy(v).to(io).cuda()[None])
+        for s0 in range(0, K.shape[0], 8192):
+            n = min(8192, K.shape[0] - s0)
+            c.write(0, sel, s0, K[s0:s0 + n].cuda()[None], V[s0:s0 + n].cuda()[None])
     torch.cuda.synchronize()
     return w, c, io
 
@@ -161,6 +191,26 @@ def window_rows(L, window, sinks):
     return len(pos), len(np.unique(pos // 16))
 
 
+def evict_and_time(call, steps, torch):
+    """Mean HIP-event time (s) of `call` over `steps` launches on the current
+    stream, each launch preceded by a full read of a separate 1 GiB buffer: the
+    read evicts the 256 MB Infinity Cache without leaving dirty lines, so the
+    call's K/V bytes all come from HBM."""
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        torch.sum(flush, dim=0, out=sink)
+        ev[i][0].record(stream)
+        call()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+
+
 def bench_decode_window(steps, torch, kv, window=1024, sinks=4):
     """The Llama-8B decode batch with a 1,024-row sliding window and 4 sink
     rows: only the visible rows are read.  Algorithmic bytes count the
@@ -175,20 +225,11 @@ def bench_decode_window(steps, torch, kv, window=1024, sinks=4):
     vis = [window_rows(int(L), window, sinks) for L in w.lengths]
     rows, blocks = sum(r for r, _ in vis), sum(b for _, b in vis)
     per_call = 2 * rows * w.n_kv * w.d * 2 + 2 * w.batch * w.n_q * w.d * 2 + 4 * blocks
-    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-    sink = torch.empty((), dtype=torch.float32, device="cuda")
-    stream = torch.cuda.current_stream()
-    warm_up_clocks(lambda: c.attn_decode(0, seqs, q, out=out, ws=ws, window=window, sinks=sinks),
-                   torch)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    for i in range(steps):
-        torch.sum(flush, dim=0, out=sink)
-        ev[i][0].record(stream)
+
+    def call():
         c.attn_decode(0, seqs, q, out=out, ws=ws, window=window, sinks=sinks)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    call_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    warm_up_clocks(call, torch)
+    call_s = evict_and_time(call, steps, torch)
     achieved = per_call / call_s / 1e9
     return {"workload": f"llama8b_decode, window {window} + {sinks} sink rows",
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
@@ -200,6 +241,11 @@ def bench_decode_window(steps, torch, kv, window=1024, sinks=4):
 
 
 def bench_decode(name, steps, warmup, torch, kv, with_cpu):
+    """One workload of the decode path.  A step grows every sequence by one
+    token (host allocator + table update) and runs kvc_attn_decode_append
+    (kv_append of the new rows, then the decode); `value` is the decode's
+    algorithmic bytes per step over the wall-clock time of the K steps.  The
+    roofline times kvc_attn_decode alone after an Infinity-Cache eviction."""
     w, c, io = build_decode(name, torch, kv)
     kv_elem = KV_ELEM_BYTES[w.kv_dtype]
     seqs_host = list(range(w.batch))
@@ -209,10 +255,10 @@ def bench_decode(name, steps, warmup, torch, kv, with_cpu):
     knew = torch.from_numpy(rng.standard_normal((w.batch, w.n_kv, w.d), dtype=np.float32)).to(io).cuda()
     vnew = torch.from_numpy(rng.standard_normal((w.batch, w.n_kv, w.d), dtype=np.float32)).to(io).cuda()
     out = torch.empty((w.batch, w.n_q, w.d), dtype=io, device="cuda")
-    max_len = int(w.lengths.max()) + warmup + steps + 1
-    # workspace for the longest context the run reaches
-    ws_bytes = w.batch * w.n_q * (max_len // 64 + 2) * (w.d + 2) * 4
-    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device="cuda")
+    # the library's own figure; the work-list plan does not depend on the
+    # lengths, so it covers every step of the run
+    ws_bytes = c.decode_workspace_bytes(w.batch)
+    ws = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -223,9 +269,12 @@ def bench_decode(name, steps, warmup, torch, kv, with_cpu):
         if ev is not None:
             ev[1].record(stream)
 
+    def call():
+        c.attn_decode(0, seqs, q, out=out, ws=ws)
+
     # pre-heat: the same decode call, which changes no state, until the clocks
     # have left their idle level (the first launches also load the kernels)
-    warm_up_clocks(lambda: c.attn_decode(0, seqs, q, out=out, ws=ws), torch)
+    warm_up_clocks(call, torch)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -240,36 +289,21 @@ def bench_decode(name, steps, warmup, torch, kv, with_cpu):
     wall = time.perf_counter() - t0
     # algorithmic bytes of each timed decode: lengths lens0+1 .. lens0+steps
     total_bytes = sum(decode_bytes(w, lens0 + i + 1, kv_elem) for i in range(steps))
-    kern_ms = [a.elapsed_time(b) for a, b in events]
-    warm_avg_s = float(np.mean(kern_ms)) / 1e3
-    # Roofline: the same decode call (state after the timed steps), each
-    # launch preceded by a full read of a separate 1 GiB buffer, which evicts
-    # the 256 MB Infinity Cache without leaving dirty lines behind, so that
-    # every K/V byte of the call comes from HBM.
+    warm_avg_s = float(np.mean([a.elapsed_time(b) for a, b in events])) / 1e3
+    # roofline: the same decode call (state after the timed steps), cold
     lens1 = lens0 + steps
     per_call = decode_bytes(w, lens1, kv_elem)
-    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-    sink = torch.empty((), dtype=torch.float32, device="cuda")
-    torch.cuda.synchronize()
-    cold = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(steps)]
-    for i in range(steps):
-        torch.sum(flush, dim=0, out=sink)
-        cold[i][0].record(stream)
-        c.attn_decode(0, seqs, q, out=out, ws=ws)
-        cold[i][1].record(stream)
-    torch.cuda.synchronize()
-    del flush, sink
-    kern_avg_s = float(np.mean([a.elapsed_time(b) for a, b in cold])) / 1e3
+    kern_avg_s = evict_and_time(call, steps, torch)
     achieved = per_call / kern_avg_s / 1e9
     res = {
         "workload": name,
         "value": total_bytes / wall / 1e9,
+        "unit": "GB/s",
         "ms_per_step": wall / steps * 1e3,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": counter_traffic("decode_" + name),
-                     "kernel": "kvc_attn_decode (split partial + merge)",
+                     "kernel": "kvc_attn_decode (work-list partials + merge)",
                      "avg_call_us": kern_avg_s * 1e6, "bytes_per_call": per_call,
                      "cache_evicted_before_each_call": True,
                      "avg_call_us_warm_with_append": warm_avg_s * 1e6},
@@ -277,41 +311,68 @@ def bench_decode(name, steps, warmup, torch, kv, with_cpu):
                   "kv_dtype": w.kv_dtype, "mean_len": float(np.mean(lens0 + 1))},
     }
     if with_cpu:
-        res["cpu_baseline"] = cpu_decode(w, q, kv_elem, torch)
+        res["cpu_baseline"] = cpu_decode(w, q, kv_elem, torch, io)
     return res
 
 
-def cpu_decode(w, q, kv_elem, torch, budget_s=12.0):
-    """Time the float64 oracle's decode on whole sequences of the workload,
-    pass after pass over the batch, until the budget is used; report the same
-    algorithmic bytes per second.  Inputs (the cached rows rounded to the
-    storage type, widened to float64) are prepared once, outside the timed
-    region."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_fields():
+    return {"cores": cpu_cores(), "blas_threads": blas_threads(), "cpu_model": cpu_model(),
+            "kind": "oracle"}
+
+
+def cpu_decode(w, q, kv_elem, torch, io, budget_s=10.0, prep_budget_s=15.0):
+    """Time the float64 oracle's decode on the workload, one (sequence, kv
+    head) unit at a time: the G query rows of that kv head against all L_b
+    cached rows.  Passes run over the units in order (sequence-major) until
+    `budget_s` of oracle time is spent; each unit's inputs (the source rows
+    rounded to the io type, widened to float64) are prepared outside the timed
+    region, at most `prep_budget_s` worth of them.  Reported in the same
+    algorithmic bytes per second as the GPU: a unit carries 2 L_b d element
+    bytes of K/V, its query and output rows, and its share of the table
+    entries and block scales."""
     from oracle import attention as A
-    io = q.dtype
     scale = 1.0 / math.sqrt(w.d)
+    G = w.n_q // w.n_kv
     qd = q.detach().cpu().double().numpy()
-    seqs = []
+    units, prep = [], 0.0
     for b in range(w.batch):
-        L = int(w.lengths[b])
-        k, v = w.kv_rows(b, 0, L)
-        seqs.append((torch.from_numpy(k).to(io).double().numpy(),
-                     torch.from_numpy(v).to(io).double().numpy()))
-    done_bytes, spent, nseq = 0, 0.0, 0
-    while spent < budget_s:
-        for b, (K, V) in enumerate(seqs):
+        K, V = source_rows(w, b, torch, io)
+        for g in range(w.n_kv):
+            if prep >= prep_budget_s:
+                break
             t0 = time.perf_counter()
-            A.decode_attention(qd[b], K, V, scale)
+            units.append((b, g, K[:, g:g + 1].double().numpy(), V[:, g:g + 1].double().numpy()))
+            prep += time.perf_counter() - t0
+    done_bytes, spent, n_done = 0.0, 0.0, 0
+    while spent < budget_s:
+        for b, g, Kd, Vd in units:
+            t0 = time.perf_counter()
+            A.decode_attention(qd[b, g * G:(g + 1) * G], Kd, Vd, scale)
             spent += time.perf_counter() - t0
-            L = K.shape[0]
-            done_bytes += 2 * L * w.n_kv * w.d * kv_elem + 2 * w.n_q * w.d * 2 + (-(-L // 16)) * 4
-            nseq += 1
+            L = Kd.shape[0]
+            nblk = -(-L // 16)
+            done_bytes += (2 * L * w.d * kv_elem + 2 * G * w.d * 2 + nblk * 4 / w.n_kv
+                           + (2 * nblk * 4 if kv_elem < 2 else 0))
+            n_done += 1
             if spent >= budget_s:
                 break
-    return {"value": done_bytes / spent / 1e9, "unit": "GB/s", "cores": cpu_cores(),
-            "blas_threads": blas_threads(), "kind": "oracle",
-            "sample": f"float64 oracle decode of {nseq} sequences, passes over the "
-                      f"{w.batch}-sequence batch ({spent:.1f} s)"}
+    src = "bf16-rounded source rows (the oracle's cost does not depend on the values)" \
+        if w.kv_dtype in ("fp8", "int4") else "the cached rows"
+    return dict(value=done_bytes / spent / 1e9, unit="GB/s", **cpu_fields(),
+                sample=f"float64 oracle decode of {n_done} (sequence, kv head) units of "
+                       f"{w.batch} x {w.n_kv}, passes over the first {len(units)} units, "
+                       f"on {src} ({spent:.1f} s)")
 
 
 # ---------------------------------------------------------------- prefill
@@ -386,10 +447,9 @@ def cpu_prefill(w, q, k, v, torch, budget_s=12.0):
         if spent >= budget_s:
             break
     flops = heads * 4 * w.d * w.T * (w.T + 1) // 2
-    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": cpu_cores(),
-            "blas_threads": blas_threads(), "kind": "oracle",
-            "sample": f"float64 oracle causal attention of {heads} of {w.batch * w.n_q} "
-                      f"(sequence, head) pairs ({spent:.1f} s)"}
+    return dict(value=flops / spent / 1e12, unit="TFLOP/s", **cpu_fields(),
+                sample=f"float64 oracle causal attention of {heads} of {w.batch * w.n_q} "
+                       f"(sequence, head) pairs ({spent:.1f} s)")
 
 
 # ---------------------------------------------------------------- extend
@@ -484,10 +544,9 @@ def cpu_extend(w, ctx, q, k, v, budget_s=12.0):
             if spent >= budget_s:
                 break
     flops = extend_flops(1, ctx, EXTEND_CHUNK, 1, w.d) * heads
-    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": cpu_cores(),
-            "blas_threads": blas_threads(), "kind": "oracle",
-            "sample": f"float64 oracle chunk attention of {heads} (sequence, head) pairs, "
-                      f"passes over the {w.batch * w.n_q} pairs ({spent:.1f} s)"}
+    return dict(value=flops / spent / 1e12, unit="TFLOP/s", **cpu_fields(),
+                sample=f"float64 oracle chunk attention of {heads} (sequence, head) pairs, "
+                       f"passes over the {w.batch * w.n_q} pairs ({spent:.1f} s)")
 
 
 # ---------------------------------------------------------------- prefix sharing
@@ -620,12 +679,21 @@ def main():
                        "mean_context": dec["shape"]["mean_len"]},
             "roofline": dec["roofline"], "cpu_baseline": dec.get("cpu_baseline")}
     if args.workload == "llama8b_decode" and not args.no_prefill:
-        line["prefill"] = bench_prefill(max(5, args.steps // 2), 2, torch, kv, with_cpu)
-        line["extend"] = bench_extend(max(5, args.steps // 2), 2, torch, kv, with_cpu)
-        line["decode_window"] = bench_decode_window(max(5, args.steps // 2), torch, kv)
+        k2 = max(5, args.steps // 2)
+        line["decode_window"] = bench_decode_window(k2, torch, kv)
+        drop_rows("llama8b_decode")
+        line["prefill"] = bench_prefill(k2, 2, torch, kv, with_cpu)
+        for key, name in (("decode_llama70b_bf16", "llama70b_decode_bf16"),
+                          ("decode_llama70b_fp8", "llama70b_decode_fp8"),
+                          ("decode_int4", "llama70b_decode_int4"),
+                          ("decode_long_mha", "long_mha_decode")):
+            line[key] = bench_decode(name, k2, 2, torch, kv, with_cpu and "int4" not in name)
+            line[key]["config"] = DECODE_WORKLOADS[name]
+            if name == "llama70b_decode_int4":
+                drop_rows("llama70b_decode")
+        drop_rows("long_mha_decode")
+        line["extend"] = bench_extend(k2, 2, torch, kv, with_cpu)
         line["prefix_share"] = bench_prefix_share(torch, kv)
-        line["decode_int4"] = bench_decode("llama70b_decode_int4", max(5, args.steps // 2), 2,
-                                           torch, kv, False)
     print(json.dumps(line))
 
 
