@@ -117,9 +117,10 @@ def test_llama8b_fused_append_decode_full_all_outputs():
         assert torch.equal(gv[0].view(torch.int16), vn[b].view(torch.int16))
 
 
-def test_long_mha_decode_full_sampled_heads():
+def test_long_mha_decode_full_all_heads():
     """One 128,000-token fp16 sequence: 2,000 rows written in bulk, then
-    125,999 single-token grow + kv_append steps, then the new token."""
+    125,999 single-token grow + kv_append steps, then the new token; every
+    one of the 32 heads against the oracle."""
     w = decode_workload("long_mha_decode")
     c, seqs, io = populate(w, append_from=2000)
     assert c.seq_len(0) == 128000
@@ -127,8 +128,11 @@ def test_long_mha_decode_full_sampled_heads():
     y = f64(c.attn_decode(0, seqs, q))
     qd = f64(q)
     scale = 1 / math.sqrt(w.d)
-    for h in (0, 7, 19, 31):
-        K, V = source_rows(w, 0, io, head=h)
+    k, v = w.kv_rows(0, 0, int(w.lengths[0]))
+    kt, vt = torch.from_numpy(k).to(io), torch.from_numpy(v).to(io)
+    del k, v
+    for h in range(w.n_q):
+        K, V = kt[:, h].double().numpy(), vt[:, h].double().numpy()
         r = A.attention(qd[0, h][None], K, V, scale)[0]
         assert_close(y[0, h][None], r[None], what=f"head {h}", io="f16")
     # the single-token path wrote the same bytes as a bulk write would
@@ -140,7 +144,12 @@ def test_long_mha_decode_full_sampled_heads():
 
 @pytest.mark.parametrize("name", ["llama70b_decode_bf16", "llama70b_decode_fp8",
                                   "llama70b_decode_int4"])
-def test_llama70b_decode_full_sampled(name):
+def test_llama70b_decode_full(name):
+    """8 x 32,768-token decode.  bf16: all 64 query heads of all 8 sequences.
+    fp8 / int4: for every sequence, the query group of kv head 0 and of kv
+    head b (so all 8 sequences and all 8 kv heads are covered), against the
+    oracle on the values the cache holds; end to end, never further from the
+    unquantised rows than the format's own deviation plus 2e-2."""
     w = decode_workload(name)
     c, seqs, io = populate(w)
     q = torch.from_numpy(w.q()).to(io).cuda()
@@ -148,9 +157,14 @@ def test_llama70b_decode_full_sampled(name):
     qd = f64(q)
     scale = 1 / math.sqrt(w.d)
     G = w.n_q // w.n_kv
-    for b in (0, w.batch - 1):
-        for g in (0, 5):
-            Ks, Vs = source_rows(w, b, io, head=g)
+    worst_fmt, worst_kernel = 0.0, 0.0
+    for b in range(w.batch):
+        k, v = w.kv_rows(b, 0, int(w.lengths[b]))
+        kt, vt = torch.from_numpy(k).to(io), torch.from_numpy(v).to(io)
+        del k, v
+        groups = range(w.n_kv) if w.kv_dtype == "bf16" else sorted({0, b % w.n_kv})
+        for g in groups:
+            Ks, Vs = kt[:, g].double().numpy(), vt[:, g].double().numpy()
             heads = list(range(g * G, (g + 1) * G))
             ref_src = np.array([A.attention(qd[b, h][None], Ks, Vs, scale)[0] for h in heads])
             if w.kv_dtype in ("fp8", "int4"):
@@ -170,21 +184,28 @@ def test_llama70b_decode_full_sampled(name):
                 # kernel error: against the oracle on the values the cache holds
                 a, _ = errors(y[b, heads], ref_q, "bf16")
                 assert a <= FP8_ABS_TOL, f"{dt} kernel seq {b} kv {g}: abs {a:.3e}"
-                assert_close(y[b, heads], ref_q, what=f"{dt} kernel seq {b} kv {g}")
+                a, _ = assert_close(y[b, heads], ref_q, what=f"{dt} kernel seq {b} kv {g}")
+                worst_kernel = max(worst_kernel, a)
                 # end to end: never further from the unquantised rows than the
                 # format itself (the oracle on dequantised rows) plus 2e-2
                 fmt = np.abs(ref_q - ref_src)
+                worst_fmt = max(worst_fmt, float(fmt.max()))
                 dev = np.abs(y[b, heads] - ref_src)
                 assert np.all(dev <= fmt + 2e-2 + np.abs(ref_src) * 2.0 ** -8), \
                     f"{dt} end-to-end seq {b} kv {g}: {dev.max():.3e} vs format {fmt.max():.3e}"
             else:
-                assert_close(y[b, heads], ref_src, what=f"seq {b} kv {g}")
+                a, _ = assert_close(y[b, heads], ref_src, what=f"seq {b} kv {g}")
+                worst_kernel = max(worst_kernel, a)
+    # the format's own deviation (oracle on dequantised vs on unquantised
+    # rows) is what rules out the 6e-2 bound against the unquantised rows
+    print(f"{name}: worst kernel abs {worst_kernel:.3e}, "
+          f"worst format deviation {worst_fmt:.3e}")
 
 
-def test_llama8b_prefill_full_sampled_rows():
+def test_llama8b_prefill_full_every_row():
     """4 x 8,192-token causal prefill (the benched call, K/V appended to the
-    cache): sampled rows of sampled heads against the oracle, and the cache
-    rows bit for bit."""
+    cache): first sampled rows and heads, then every row of every head of all
+    four sequences against the oracle, and the cache rows bit for bit."""
     w = prefill_workload()
     qn, kn, vn = w.qkv()
     q, k, v = (torch.from_numpy(a).to(torch.bfloat16).cuda() for a in (qn, kn, vn))
