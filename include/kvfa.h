@@ -327,6 +327,25 @@ int kvc_attn_decode_append(kvc_cache* cache, int32_t layer, int32_t n, const int
                            int32_t num_splits, void* ws_dev, uint64_t ws_bytes,
                            hipStream_t stream);
 
+/* kvc_attn_decode without a caller workspace, for callers that cannot
+ * allocate device memory around the call (code under graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments,
+ * layouts, results and errors as kvc_attn_decode with window 0, except that
+ * the split partials live in a fixed 64 MiB array in device memory owned by
+ * the library: each device it runs on holds one such array from the first
+ * kvc_create on that device until the process ends.  The call allocates
+ * nothing.  A call whose plan needs more than 64 MiB (the bytes
+ * kvc_decode_workspace_bytes reports; about 8,000 (sequence, kv-head group)
+ * segments plus the chip's waves at d_head 128) returns KVC_E_WORKSPACE and
+ * enqueues nothing.  Every call on one device shares that device's array and
+ * nothing in it needs clearing (each call writes every entry it reads before
+ * reading it), so calls that may overlap on one device -- on different
+ * streams, or from different threads -- race and must be serialised by the
+ * caller; calls ordered on one stream are safe. */
+int kvc_attn_decode_noalloc(kvc_cache* cache, int32_t layer, int32_t n, const int32_t* seqs_dev,
+                            const void* q_dev, void* out_dev, float scale, int32_t num_splits,
+                            hipStream_t stream);
+
 /* Block-table gather (kvcache-7e2, PagedAttention section: `physical` maps
  * a logical position p to (table[p / 16], p % 16), and attention gathers K
  * and V from those physical blocks): copy the stored bit patterns of

@@ -85,6 +85,7 @@ _SIGS = {
     "kvc_attn_extend_window": [_P, _I, _I, _P, _I, _P, _P, ctypes.c_float, _I, _I, _P],
     "kvc_attn_decode_append": [_P, _I, _I, _P, _P, _P, _P, _P, ctypes.c_float, _I, _I, _I, _P,
                                ctypes.c_uint64, _P],
+    "kvc_attn_decode_noalloc": [_P, _I, _I, _P, _P, _P, ctypes.c_float, _I, _P],
     "kvc_gather": [_P, _I, _I, _I, _I, _P, _P, _P],
     "kvc_last_error": [],
 }
@@ -347,6 +348,18 @@ class KvCache:
         _check(lib().kvc_attn_decode_append(
             self._h, layer, n, self._seqs(seqs), kp, vp, qp, op, ctypes.c_float(scale), window,
             sinks, num_splits, _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+        return out
+
+    def attn_decode_noalloc(self, layer, seqs, q, scale=None, num_splits=0, out=None):
+        """attn_decode with the partials in the library's own device scratch
+        (no workspace argument; the call allocates nothing)."""
+        n = seqs.numel()
+        scale = 1.0 / math.sqrt(self.d) if scale is None else scale
+        if out is None:
+            out = torch.empty((n, self.n_q, self.d), dtype=self.io_dtype, device=q.device)
+        qp, op = self._io(q, (n, self.n_q, self.d), "q"), self._io(out, (n, self.n_q, self.d), "out")
+        _check(lib().kvc_attn_decode_noalloc(self._h, layer, n, self._seqs(seqs), qp, op,
+                                             ctypes.c_float(scale), num_splits, _stream()))
         return out
 
     def gather(self, layer, seq, start, count):

@@ -45,6 +45,9 @@ struct kvc_cache {
   // call, which may be under graph capture).
   hipStream_t side = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
+  // Device address of the library-owned decode scratch on the device the
+  // handle was created on (kvc_attn_decode_noalloc).
+  void* scratch = nullptr;
   ~kvc_cache() {
     if (fork) (void)hipEventDestroy(fork);
     if (join) (void)hipEventDestroy(join);
@@ -260,7 +263,12 @@ int kvc_create(const kvc_config* cfg, const kvc_buffers* dev, hipStream_t stream
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess &&
         cus > 0)
       c->cu_count = cus;
-    hipError_t e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);
+    hipError_t e = scratch_address(&c->scratch);
+    if (e != hipSuccess) {
+      delete c;
+      return hip_fail(e, "decode scratch address");
+    }
+    e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->fork, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->join, hipEventDisableTiming);
     if (e != hipSuccess) {
@@ -666,6 +674,25 @@ int kvc_attn_decode_append(kvc_cache* c, int32_t layer, int32_t n, const int32_t
   if (!k_new || !v_new) return fail(KVC_E_INVAL, "k_new/v_new is NULL");
   return decode_impl(c, layer, n, seqs, k_new, v_new, q, out, scale, window, sinks, num_splits,
                      ws, ws_bytes, stream);
+}
+
+int kvc_attn_decode_noalloc(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs,
+                            const void* q, void* out, float scale, int32_t num_splits,
+                            hipStream_t stream) {
+  if (!c) return fail(KVC_E_INVAL, "cache is NULL");
+  int r = need_dev(c);
+  if (r) return r;
+  if (n < 0 || num_splits < 0) return fail(KVC_E_INVAL, "negative size");
+  if (n > 0) {
+    DecodePlan p = make_decode_plan(c->view(), n, live_max_len(c), num_splits, c->cu_count);
+    if (p.ws_bytes > kScratchBytes)
+      return fail(KVC_E_WORKSPACE, "the call needs " + std::to_string(p.ws_bytes) +
+                                       " bytes of workspace, more than the library scratch (" +
+                                       std::to_string(kScratchBytes) +
+                                       " bytes): use kvc_attn_decode with a workspace");
+  }
+  return decode_impl(c, layer, n, seqs, nullptr, nullptr, q, out, scale, 0, 0, num_splits,
+                     c->scratch, kScratchBytes, stream);
 }
 
 int kvc_gather(const kvc_cache* c, int32_t layer, int32_t seq, int32_t start, int32_t count,

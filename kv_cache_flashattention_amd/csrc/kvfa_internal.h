@@ -72,6 +72,12 @@ __host__ __device__ inline bool has_scales(int dtype) {
 }
 inline int io_dtype(int dtype) { return has_scales(dtype) ? KVC_BF16 : dtype; }
 
+// Size of the library-owned decode scratch used by kvc_attn_decode_noalloc
+// (one copy per device, alive until the process ends).
+constexpr uint64_t kScratchBytes = 64ull << 20;
+// Device address of the current device's scratch (looked up once per device).
+hipError_t scratch_address(void** addr);
+
 DecodePlan make_decode_plan(const CacheView& cv, int32_t n, int32_t max_len, int32_t num_splits,
                             int32_t cu_count);
 uint64_t work_list_ws_bytes(const CacheView& cv, int32_t nb, int32_t waves);

@@ -214,6 +214,9 @@ def test_host_only_handle_refuses_device_calls():
     rc = L.kvc_attn_decode(c._h, 0, 1, ctypes.c_void_p(16), ctypes.c_void_p(16),
                            ctypes.c_void_p(16), ctypes.c_float(1.0), 0, None, 0, None)
     assert rc == kv.KVC_E_STATE
+    rc = L.kvc_attn_decode_noalloc(c._h, 0, 1, ctypes.c_void_p(16), ctypes.c_void_p(16),
+                                   ctypes.c_void_p(16), ctypes.c_float(1.0), 0, None)
+    assert rc == kv.KVC_E_STATE
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.125, float("nan"), float("inf")])
