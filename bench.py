@@ -102,6 +102,14 @@ def counter_traffic(key):
             + e["write_kib_per_call"] * 1024 * cal["write_factor"])
 
 
+_T0 = time.perf_counter()
+
+
+def log(msg):
+    """Progress line on stderr (the JSON result goes alone to stdout)."""
+    print(f"[bench {time.perf_counter() - _T0:6.1f} s] {msg}", file=sys.stderr, flush=True)
+
+
 def warm_up_clocks(call, torch, seconds=0.05):
     """Repeat `call` (untimed) for at least `seconds` of GPU time.  From idle
     the GPU needs some tens of milliseconds of load before its clocks settle:
@@ -345,15 +353,17 @@ def cpu_decode(w, q, kv_elem, torch, io, budget_s=10.0, prep_budget_s=15.0):
     scale = 1.0 / math.sqrt(w.d)
     G = w.n_q // w.n_kv
     qd = q.detach().cpu().double().numpy()
-    units, prep = [], 0.0
+    units, t_prep = [], time.perf_counter()
     for b in range(w.batch):
+        if time.perf_counter() - t_prep >= prep_budget_s:
+            break
         K, V = source_rows(w, b, torch, io)
+        K32, V32 = K.float().numpy(), V.float().numpy()        # contiguous, exact widening
         for g in range(w.n_kv):
-            if prep >= prep_budget_s:
-                break
-            t0 = time.perf_counter()
-            units.append((b, g, K[:, g:g + 1].double().numpy(), V[:, g:g + 1].double().numpy()))
-            prep += time.perf_counter() - t0
+            units.append((b, g, K32[:, g:g + 1].astype(np.float64),
+                          V32[:, g:g + 1].astype(np.float64)))
+        del K32, V32
+    prep = time.perf_counter() - t_prep
     done_bytes, spent, n_done = 0.0, 0.0, 0
     while spent < budget_s:
         for b, g, Kd, Vd in units:
@@ -372,7 +382,7 @@ def cpu_decode(w, q, kv_elem, torch, io, budget_s=10.0, prep_budget_s=15.0):
     return dict(value=done_bytes / spent / 1e9, unit="GB/s", **cpu_fields(),
                 sample=f"float64 oracle decode of {n_done} (sequence, kv head) units of "
                        f"{w.batch} x {w.n_kv}, passes over the first {len(units)} units, "
-                       f"on {src} ({spent:.1f} s)")
+                       f"on {src} ({spent:.1f} s; inputs prepared in {prep:.1f} s)")
 
 
 # ---------------------------------------------------------------- prefill
@@ -645,6 +655,7 @@ def main():
     with_cpu = not args.no_cpu
 
     if args.workload == "llama8b_extend":
+        log("llama8b_extend")
         ex = bench_extend(args.steps, args.warmup, torch, kv, with_cpu)
         line = {"metric": METRIC, "value": ex["value"], "unit": "TFLOP/s", "n_gpus": 1,
                 "steps": args.steps, "warmup": args.warmup, "ms_per_step": ex["ms_per_step"],
@@ -657,6 +668,7 @@ def main():
         print(json.dumps(line))
         return
     if args.workload == "llama8b_prefill":
+        log("llama8b_prefill")
         pf = bench_prefill(args.steps, args.warmup, torch, kv, with_cpu)
         line = {"metric": METRIC, "value": pf["value"], "unit": "TFLOP/s", "n_gpus": 1,
                 "steps": args.steps, "warmup": args.warmup, "ms_per_step": pf["ms_per_step"],
@@ -668,7 +680,10 @@ def main():
         print(json.dumps(line))
         return
 
+    log(f"{args.workload}: building the cache")
     dec = bench_decode(args.workload, args.steps, args.warmup, torch, kv, with_cpu)
+    log(f"{args.workload}: {dec['roofline']['avg_call_us']:.1f} us per call, "
+        f"frac {dec['roofline']['frac']:.3f}")
     dtype = {"bf16": "bf16", "fp16": "f16", "fp8": "fp8-e4m3 (bf16 q/o)",
              "int4": "int4 (bf16 q/o)"}[dec["shape"]["kv_dtype"]]
     line = {"metric": METRIC, "value": dec["value"], "unit": "GB/s", "n_gpus": 1,
@@ -681,18 +696,23 @@ def main():
     if args.workload == "llama8b_decode" and not args.no_prefill:
         k2 = max(5, args.steps // 2)
         line["decode_window"] = bench_decode_window(k2, torch, kv)
+        log(f"decode_window: frac {line['decode_window']['roofline']['frac']:.3f}")
         drop_rows("llama8b_decode")
         line["prefill"] = bench_prefill(k2, 2, torch, kv, with_cpu)
+        log(f"prefill: frac {line['prefill']['roofline']['frac']:.3f}")
         for key, name in (("decode_llama70b_bf16", "llama70b_decode_bf16"),
                           ("decode_llama70b_fp8", "llama70b_decode_fp8"),
                           ("decode_int4", "llama70b_decode_int4"),
                           ("decode_long_mha", "long_mha_decode")):
             line[key] = bench_decode(name, k2, 2, torch, kv, with_cpu and "int4" not in name)
             line[key]["config"] = DECODE_WORKLOADS[name]
+            log(f"{key}: {line[key]['roofline']['avg_call_us']:.1f} us per call, "
+                f"frac {line[key]['roofline']['frac']:.3f}")
             if name == "llama70b_decode_int4":
                 drop_rows("llama70b_decode")
         drop_rows("long_mha_decode")
         line["extend"] = bench_extend(k2, 2, torch, kv, with_cpu)
+        log(f"extend: frac {line['extend']['roofline']['frac']:.3f}")
         line["prefix_share"] = bench_prefix_share(torch, kv)
     print(json.dumps(line))
 
