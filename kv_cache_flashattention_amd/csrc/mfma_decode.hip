@@ -245,7 +245,9 @@ __device__ __forceinline__ int64_t share(int64_t a, int64_t W, int64_t P) {
 // of the cache (no other wave reads position L-1), and for the first query
 // group of the kv head it also stores the row into the cache.
 // The APPEND variant runs only on 16-bit caches, whose work list uses one
-// workgroup per CU, so it may use the whole register file.
+// workgroup per CU, so it may use the whole register file.  (Giving the
+// plain 16-bit variants the same budget measured 2-3 us slower: the
+// compiler schedules the unit loop differently.)
 template <int KV, int D, bool APPEND>
 __global__ __launch_bounds__(256, APPEND ? 1 : 2) void k_decode_work(CacheView cv, int layer,
                                                         const int32_t* seqs, const uint16_t* q,
@@ -264,6 +266,8 @@ __global__ __launch_bounds__(256, APPEND ? 1 : 2) void k_decode_work(CacheView c
   __shared__ int32_t s_counts[kMaxBatch];
   __shared__ int32_t s_seq[kMaxBatch], s_len[kMaxBatch];   // each entry's sequence and length
   __shared__ int64_t s_wsum[4];
+  constexpr int kLenCache = 4096;
+  __shared__ int32_t s_lenall[kLenCache];               // every sequence's length (small caches)
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   const int G = cv.n_q / cv.n_kv;
@@ -271,16 +275,35 @@ __global__ __launch_bounds__(256, APPEND ? 1 : 2) void k_decode_work(CacheView c
   const int64_t slots = work_slots(nb, nkvg, waves);
   WorkWs W_ = work_ws(ws, slots, D, nb);
 
-  // ---- unit counts and their prefix sums (8 entries per thread, nb <= 2048)
+  // ---- unit counts and their prefix sums (8 entries per thread, nb <= 2048).
+  // The batch's sequence ids and, when the cache has at most kLenCache
+  // sequences, all of their lengths are loaded together, so the lengths do
+  // not wait for the ids.
   {
+    const bool lens_in_lds = cv.max_seqs <= kLenCache;
+    int sqv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int b = tid * 8 + i;
+      sqv[i] = b < nb ? seqs[b] : -1;
+    }
+    if (lens_in_lds)
+      for (int i = tid; i < cv.max_seqs; i += 256) s_lenall[i] = cv.len[i];
+    __syncthreads();
     int64_t loc[8], tsum = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int b = tid * 8 + i;
       int c = 0;
       if (b < nb) {
-        const int sq = seqs[b];
-        const int L = valid_len(cv, sq);
+        const int sq = sqv[i];
+        int L;
+        if (lens_in_lds) {
+          L = sq >= 0 && sq < cv.max_seqs ? s_lenall[sq] : -1;
+          if (L <= 0 || L > cv.max_bps * kBlock) L = -1;
+        } else {
+          L = valid_len(cv, sq);
+        }
         c = L > 0 ? UnitMap(L, window, sinks).count : 0;
         s_counts[b] = c;
         s_seq[b] = sq;
