@@ -314,6 +314,12 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
   // scaled caches: the K and V scales of the tile's four blocks, loaded by
   // group threads 0..3 with the K tile and written to LDS beside it
   float scK = 1.f, scV = 1.f;
+  // Prompt staging: this thread's element offsets within a K or V tile
+  // (row t / KG, granule t % KG; V rows 4 kg, granule dg), computed once;
+  // the other chunks of a tile lie a uniform number of rows further on.
+  const int tg = tid & 255;
+  const int koff = (tg / KG) * (int)kvstride + 8 * (tg % KG);
+  const int voff = 4 * (tg % (BN / 4)) * (int)kvstride + 8 * (tg / (BN / 4));
   auto load_k = [&](int li) {
     const int i = tile_of(li);
     const int lim = L - 1 - BN * i;                    // last valid row of the tile
@@ -344,10 +350,16 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
       }
     } else {
       const uint16_t* tb = kbase + (int64_t)(BN * i) * kvstride;
+      if (lim >= BN - 1) {                             // whole tile: no row clamps
 #pragma unroll
-      for (int c0 = 0; c0 < KCH; ++c0) {
-        const int row = min(t / KG + c0 * (256 / KG), lim);
-        sreg[c0] = *(const u32x4*)(tb + row * kvstride + 8 * (t % KG));
+        for (int c0 = 0; c0 < KCH; ++c0)
+          sreg[c0] = *(const u32x4*)(tb + koff + c0 * (256 / KG) * (int)kvstride);
+      } else {
+#pragma unroll
+        for (int c0 = 0; c0 < KCH; ++c0) {
+          const int row = min(t / KG + c0 * (256 / KG), lim);
+          sreg[c0] = *(const u32x4*)(tb + row * kvstride + 8 * (t % KG));
+        }
       }
     }
   };
@@ -397,10 +409,15 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
       const int kg = t % (BN / 4), dg = t / (BN / 4);
       const uint16_t* tb = vbase + (int64_t)(BN * i) * kvstride;
       const int lim = L - 1 - BN * i;
+      if (lim >= BN - 1) {                             // whole tile: no row clamps
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = min(4 * kg + r, lim);
-        sreg[r] = *(const u32x4*)(tb + row * kvstride + 8 * dg);
+        for (int r = 0; r < 4; ++r) sreg[r] = *(const u32x4*)(tb + voff + r * (int)kvstride);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = min(4 * kg + r, lim);
+          sreg[r] = *(const u32x4*)(tb + row * kvstride + 8 * dg);
+        }
       }
     }
   };
