@@ -131,6 +131,7 @@ __device__ __forceinline__ uint4 interleave_halves(uint4 a) {
   return make_uint4((a.x & 0xFFFFu) | (a.z << 16), (a.x >> 16) | (a.z & 0xFFFF0000u),
                     (a.y & 0xFFFFu) | (a.w << 16), (a.y >> 16) | (a.w & 0xFFFF0000u));
 }
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float sum8_bf16(bf16x8 a) {
   const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
   float s = 0.f;
@@ -478,17 +479,9 @@ __global__ __launch_bounds__(256, APPEND ? 1 : 2) void k_decode_work(CacheView c
         const int x = max(__builtin_amdgcn_readlane(tab, j + i), 0);   // invalid: NaN rows later
         sbase[i] = ((layer_blocks + x) * cv.n_kv + kvh) * SB;
       }
-      if constexpr (SCALED) {
-        const float k0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                             __builtin_bit_cast(int, tks), j));
-        const float k1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                             __builtin_bit_cast(int, tks), j + 1));
-        const float v0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                             __builtin_bit_cast(int, tvs), j));
-        const float v1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                             __builtin_bit_cast(int, tvs), j + 1));
-        B.ksc = (g >> 1) ? k1 : k0;
-        B.vsc = (g >> 1) ? v1 : v0;
+      if constexpr (SCALED) {                         // this lane's block: table lane j + g/2
+        B.ksc = __shfl(tks, j + (g >> 1), 64);
+        B.vsc = __shfl(tvs, j + (g >> 1), 64);
       }
       const uint8_t* krow = kpool + (tok_block(r16) ? sbase[1] : sbase[0]);
       if constexpr (KV == KV_INT4) {
@@ -579,26 +572,34 @@ __global__ __launch_bounds__(256, APPEND ? 1 : 2) void k_decode_work(CacheView c
         vsc = B.vsc;
       }
       const int pos0 = 16 * (g >> 1) + 8 * (g & 1);
-      float p[2][4];
+      // A score enters the exponent as p = s a + b, with a = scale log2(e)
+      // times the block's K scale (kept above zero, so that a hidden
+      // position's -inf stays -inf) and b the int4 offset term.  a and b
+      // belong to the lane's block, so within the lane the map is increasing:
+      // the lane's max is taken on the raw scores s and mapped once, the
+      // lanes' maxima are combined, and exp2(p - m) is exp2(fma(s, a, b - m)).
+      const float a = fmaxf(sl2 * ksc, 1e-30f);
+      const float b = KV == KV_INT4 ? qoff * a : 0.f;
+      float sc[2][4];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          p[t][i] = KV == KV_INT4 ? fmaf(sacc[t][i], sl2 * ksc, qoff * (sl2 * ksc))
-                                  : sacc[t][i] * (sl2 * ksc);
+        for (int i = 0; i < 4; ++i) sc[t][i] = sacc[t][i];
       if (tail || wedge) {                            // wave-uniform: masked units only
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int pos = c * kUnit + pos0 + 4 * t + i;
-            if (pos0 + 4 * t + i >= nvalid || (pos < wlo && pos >= sinks)) p[t][i] = -INFINITY;
+            if (pos0 + 4 * t + i >= nvalid || (pos < wlo && pos >= sinks)) sc[t][i] = -INFINITY;
           }
       }
-      float cmax = fmaxf(fmaxf(fmaxf(p[0][0], p[0][1]), fmaxf(p[0][2], p[0][3])),
-                         fmaxf(fmaxf(p[1][0], p[1][1]), fmaxf(p[1][2], p[1][3])));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+      // (maximum, not fmaxf: no canonicalising of the selected values)
+      const float smax = vmax(vmax(vmax(sc[0][0], sc[0][1]), vmax(sc[0][2], sc[0][3])),
+                              vmax(vmax(sc[1][0], sc[1][1]), vmax(sc[1][2], sc[1][3])));
+      float cmax = fmaf(smax, a, b);
+      cmax = vmax(cmax, __shfl_xor(cmax, 16, 64));
+      cmax = vmax(cmax, __shfl_xor(cmax, 32, 64));
       // Lazy rescale: the running max m moves only when a row's new max
       // exceeds it by more than kStale (log2 units), so most units skip the
       // rescale of O; probabilities stay below 2^kStale.  (m, l, O) remain a
@@ -612,12 +613,13 @@ __global__ __launch_bounds__(256, APPEND ? 1 : 2) void k_decode_work(CacheView c
 #pragma unroll
         for (int i = 0; i < DT; ++i) o[i] *= alpha;
       }
+      const float bm = b - m;
       float psum = 0.f, pv[8];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float e = __builtin_amdgcn_exp2f(p[t][i] - m);
+          const float e = __builtin_amdgcn_exp2f(fmaf(sc[t][i], a, bm));
           psum += e;
           pv[4 * t + i] = e * vsc;
         }
