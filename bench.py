@@ -8,8 +8,7 @@ behind shuffled block tables, context lengths uniform in [512, 4096].  One
 step is one pass of the decode hot path over that batch: grow every sequence
 by one token (host allocator + table update), then kvc_attn_decode_append:
 kv_append of the new K/V rows and attn_decode (work-list partials and their
-(m, l) merge) in one call, the append fused into the decode kernel for 16-bit
-caches.  The headline `value` is the decode's algorithmic HBM bytes per step
+(m, l) merge) in one call.  The headline `value` is the decode's algorithmic HBM bytes per step
 (K/V rows read through the tables, queries, outputs, table entries) divided
 by the wall-clock time per step.
 
@@ -606,7 +605,7 @@ def bench_prefix_share(torch, kv, n_seq=40, prompt=600, n_layers=32):
 DECODE_WORKLOADS = {
     "llama8b_decode": "40 sequences, 32 q / 8 kv heads, d 128, bf16 cache, 16-token blocks, "
                       "shuffled tables, lengths uniform in [512, 4096]; step = grow + "
-                      "kvc_attn_decode_append (kv_append fused into the decode call)",
+                      "kvc_attn_decode_append (kv_append and the decode in one call)",
     "llama70b_decode_bf16": "8 x 32,768-token contexts, 64 q / 8 kv heads, d 128, bf16 cache, "
                             "1% outliers x8",
     "llama70b_decode_fp8": "8 x 32,768-token contexts, 64 q / 8 kv heads, d 128, fp8-e4m3 cache "

@@ -317,9 +317,8 @@ int kvc_attn_extend_window(kvc_cache* cache, int32_t layer, int32_t n, const int
  * (call kvc_seq_grow first; k_new_dev, v_new_dev [n][n_kv_heads][d_head] in
  * the io type, 16-byte aligned) and as kvc_attn_decode_window (window = 0:
  * full attention).  Outputs and cache contents equal those of kvc_append
- * then kvc_attn_decode_window.  For bf16 and f16 caches the row is stored
- * and attended inside the decode kernel (one launch fewer); other caches run
- * the append kernel first.  The workspace is sized by
+ * then kvc_attn_decode_window: the call enqueues the append kernel, then the
+ * decode, on the same stream.  The workspace is sized by
  * kvc_decode_workspace_bytes as for kvc_attn_decode. */
 int kvc_attn_decode_append(kvc_cache* cache, int32_t layer, int32_t n, const int32_t* seqs_dev,
                            const void* k_new_dev, const void* v_new_dev, const void* q_dev,

@@ -259,23 +259,11 @@ __device__ __forceinline__ int64_t share(int64_t a, int64_t W, int64_t P) {
 }
 
 
-// APPEND (16-bit caches): the call also appends each sequence's newest K/V
-// row, knew / vnew [nb][n_kv][D], at position L-1.  The wave that computes a
-// segment's last unit takes that token's operands from knew / vnew instead
-// of the cache (no other wave reads position L-1), and for the first query
-// group of the kv head it also stores the row into the cache.
-// The APPEND variant runs only on 16-bit caches, whose work list uses one
-// workgroup per CU, so it may use the whole register file.  (Giving the
-// plain 16-bit variants the same budget measured 2-3 us slower: the
-// compiler schedules the unit loop differently.)
-template <int KV, int D, bool APPEND>
-__global__ __launch_bounds__(256, APPEND ? 1 : 2) void k_decode_work(CacheView cv, int layer,
+template <int KV, int D>
+__global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
                                                         const int32_t* seqs, const uint16_t* q,
                                                         void* ws, int nb, int qgroups, int waves,
-                                                        float sl2, int window, int sinks,
-                                                        const uint16_t* knew,
-                                                        const uint16_t* vnew) {
-  static_assert(!APPEND || KV == KV_BF16 || KV == KV_F16, "append fusion: 16-bit caches");
+                                                        float sl2, int window, int sinks) {
   typedef typename Op<KV>::T OpT;
   typedef Unit<KV, D> U;
   constexpr int KS = U::KS, DT = U::DT, KL = U::KL;
@@ -392,23 +380,6 @@ __global__ __launch_bounds__(256, APPEND ? 1 : 2) void k_decode_work(CacheView c
     const int seq = uni(s_seq[b]);
     const int L = uni(s_len[b]);                       // > 0: the entry has units
     const UnitMap umap(L, window, sinks);
-    // APPEND: the newest row of this (sequence, kv head), and the last unit
-    // (the one holding position L-1) of the segment's visible units
-    const uint16_t* knew_row = APPEND ? knew + ((int64_t)b * cv.n_kv + kvh) * D : nullptr;
-    const uint16_t* vnew_row = APPEND ? vnew + ((int64_t)b * cv.n_kv + kvh) * D : nullptr;
-    const int cs_last = umap.count - 1;
-    // ... and, when this piece ends with that unit, the newest V row's
-    // elements this lane patches in (column 16 dt + r16, two per register),
-    // loaded now so that the last unit does not wait for them
-    uint32_t vpatch[DT / 2];
-    if constexpr (APPEND) {
-      if (c1 == umap.count) {
-#pragma unroll
-        for (int i = 0; i < DT / 2; ++i)
-          vpatch[i] = (uint32_t)vnew_row[32 * i + r16] | ((uint32_t)vnew_row[32 * i + 16 + r16] << 16);
-      }
-    }
-
     // Query operand (B of S^T = K Q^T): column r16 = query row qg*16 + r16.
     const int qi = qg * 16 + r16;
     const bool qrow = qi < G;
@@ -508,11 +479,6 @@ __global__ __launch_bounds__(256, APPEND ? 1 : 2) void k_decode_work(CacheView c
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const uint8_t* rp = krow + (int64_t)tok_slot(t, r16) * D * EB;
-          if constexpr (APPEND) {
-            if (cs == cs_last &&
-                umap.unit(cs) * kUnit + 16 * tok_block(r16) + tok_slot(t, r16) == L - 1)
-              rp = (const uint8_t*)knew_row;
-          }
 #pragma unroll
           for (int a = 0; a < KL; ++a) {
             const int off = KV == KV_FP8 ? 64 * a + 16 * g : 2 * dmap<KV, D>(a, g);
@@ -659,53 +625,11 @@ __global__ __launch_bounds__(256, APPEND ? 1 : 2) void k_decode_work(CacheView c
             const uint32_t hi = ((dt & 1) ? w4.w : w4.y) & keep[1];
             vop = __builtin_bit_cast(OpT, fp8x8_to_bf16(lo, hi));
           } else {
-            uint4 raw = B.v[dt];
-            if constexpr (APPEND) {
-              // the newest token's V element comes from vnew
-              const int np = L - 1 - (c * kUnit + pos0);
-              if (cs == cs_last && np >= 0 && np < 8) {
-                const uint32_t val = (dt & 1) ? vpatch[dt / 2] >> 16 : vpatch[dt / 2] & 0xFFFFu;
-                const uint32_t lo = (raw.x & 0xFFFF0000u) | val, hi = (raw.x & 0xFFFFu) | (val << 16);
-                const uint32_t lo1 = (raw.y & 0xFFFF0000u) | val, hi1 = (raw.y & 0xFFFFu) | (val << 16);
-                const uint32_t lo2 = (raw.z & 0xFFFF0000u) | val, hi2 = (raw.z & 0xFFFFu) | (val << 16);
-                const uint32_t lo3 = (raw.w & 0xFFFF0000u) | val, hi3 = (raw.w & 0xFFFFu) | (val << 16);
-                raw.x = np == 0 ? lo : np == 1 ? hi : raw.x;
-                raw.y = np == 2 ? lo1 : np == 3 ? hi1 : raw.y;
-                raw.z = np == 4 ? lo2 : np == 5 ? hi2 : raw.z;
-                raw.w = np == 6 ? lo3 : np == 7 ? hi3 : raw.w;
-              }
-            }
+            const uint4 raw = B.v[dt];
             vop = __builtin_bit_cast(OpT, make_uint4(raw.x & keep[0], raw.y & keep[1],
                                                      raw.z & keep[2], raw.w & keep[3]));
           }
           o[dt] = mfma(vop, pop, o[dt]);
-        }
-      }
-      // APPEND: the first query group of the kv head stores the newest row
-      // into the cache (slot (L-1) % 16 of its block; skipped if the table
-      // entry is invalid): K from the operand registers of the lanes that
-      // loaded it, V from the patch values of lane group 0.
-      if constexpr (APPEND) {
-        if (cs == cs_last && qg == 0) {
-          const int x = __builtin_amdgcn_readlane(tab, 2 * (cs - tab0) + (((L - 1) / kBlock) & 1));
-          if (x >= 0) {
-            const int64_t base = ((layer_blocks + x) * cv.n_kv + kvh) * SB;
-            const int r = (L - 1) % kBlock;
-            uint8_t* kdst = (uint8_t*)cv.k + base + (int64_t)r * D * 2;
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-              if (c * kUnit + 16 * tok_block(r16) + tok_slot(t, r16) == L - 1) {
-#pragma unroll
-                for (int a = 0; a < KL; ++a) *(uint4*)(kdst + 2 * dmap<KV, D>(a, g)) = B.k[t][a];
-              }
-            if (g == 0) {
-              uint16_t* vdst = (uint16_t*)((uint8_t*)cv.v + base) + r;
-#pragma unroll
-              for (int dt = 0; dt < DT; ++dt)
-                vdst[(16 * dt + r16) * kBlock] =
-                    (uint16_t)((dt & 1) ? vpatch[dt / 2] >> 16 : vpatch[dt / 2] & 0xFFFFu);
-            }
-          }
         }
       }
     };
@@ -844,10 +768,10 @@ __global__ __launch_bounds__(256) void k_decode_work_merge(CacheView cv, const v
   }
 }
 
-template <int KV, int D, bool APPEND = false>
+template <int KV, int D>
 hipError_t run(const CacheView& cv, int layer, int n, const int32_t* seqs, const void* q,
                void* out, float sl2, const DecodePlan& p, void* ws, int window, int sinks,
-               hipStream_t st, const void* knew = nullptr, const void* vnew = nullptr) {
+               hipStream_t st) {
   const int G = cv.n_q / cv.n_kv;
   const int qgroups = (G + 15) / 16;
   const int grid = (p.waves + 3) / 4;
@@ -855,10 +779,8 @@ hipError_t run(const CacheView& cv, int layer, int n, const int32_t* seqs, const
     const int nb = n - b0 < kMaxBatch ? n - b0 : kMaxBatch;
     const uint16_t* qb = (const uint16_t*)q + (int64_t)b0 * cv.n_q * D;
     uint16_t* ob = (uint16_t*)out + (int64_t)b0 * cv.n_q * D;
-    const uint16_t* kb = APPEND ? (const uint16_t*)knew + (int64_t)b0 * cv.n_kv * D : nullptr;
-    const uint16_t* vb = APPEND ? (const uint16_t*)vnew + (int64_t)b0 * cv.n_kv * D : nullptr;
-    hipLaunchKernelGGL((k_decode_work<KV, D, APPEND>), dim3(grid), dim3(256), 0, st, cv, layer,
-                       seqs + b0, qb, ws, nb, qgroups, p.waves, sl2, window, sinks, kb, vb);
+    hipLaunchKernelGGL((k_decode_work<KV, D>), dim3(grid), dim3(256), 0, st, cv, layer,
+                       seqs + b0, qb, ws, nb, qgroups, p.waves, sl2, window, sinks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_decode_work_merge<KV == KV_F16, D>), dim3(cv.n_q, nb), dim3(256), 0, st,
@@ -875,7 +797,7 @@ int occupancy_waves() {
   if (waves == 0) {
     int blocks = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks,
-                                                     (const void*)k_decode_work<KV, D, false>,
+                                                     (const void*)k_decode_work<KV, D>,
                                                      256, 0) != hipSuccess || blocks < 1)
       blocks = 2;
     waves = 4 * blocks;
@@ -922,27 +844,21 @@ int work_list_waves_per_cu(const CacheView& cv) {
 
 hipError_t launch_decode_mfma(const CacheView& cv, int layer, int n, const int32_t* seqs,
                               const void* q, void* out, float sl2, const DecodePlan& p, void* ws,
-                              int window, int sinks, const void* knew, const void* vnew,
-                              hipStream_t st, bool* handled) {
+                              int window, int sinks, hipStream_t st, bool* handled) {
   *handled = p.work_list != 0;
   if (!*handled) return hipSuccess;
-  const bool fuse = knew != nullptr;
-  if (fuse && cv.dtype != KVC_BF16 && cv.dtype != KVC_F16) return hipErrorInvalidValue;
 #define KVFA_RUN(KVT, DD) run<KVT, DD>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st)
-#define KVFA_RUN_APPEND(KVT, DD) \
-  run<KVT, DD, true>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st, knew, vnew)
   if (cv.d == 128) {
-    if (cv.dtype == KVC_BF16) return fuse ? KVFA_RUN_APPEND(KV_BF16, 128) : KVFA_RUN(KV_BF16, 128);
-    if (cv.dtype == KVC_F16) return fuse ? KVFA_RUN_APPEND(KV_F16, 128) : KVFA_RUN(KV_F16, 128);
+    if (cv.dtype == KVC_BF16) return KVFA_RUN(KV_BF16, 128);
+    if (cv.dtype == KVC_F16) return KVFA_RUN(KV_F16, 128);
     if (cv.dtype == KVC_INT4) return KVFA_RUN(KV_INT4, 128);
     return KVFA_RUN(KV_FP8, 128);
   }
-  if (cv.dtype == KVC_BF16) return fuse ? KVFA_RUN_APPEND(KV_BF16, 64) : KVFA_RUN(KV_BF16, 64);
-  if (cv.dtype == KVC_F16) return fuse ? KVFA_RUN_APPEND(KV_F16, 64) : KVFA_RUN(KV_F16, 64);
+  if (cv.dtype == KVC_BF16) return KVFA_RUN(KV_BF16, 64);
+  if (cv.dtype == KVC_F16) return KVFA_RUN(KV_F16, 64);
   if (cv.dtype == KVC_INT4) return KVFA_RUN(KV_INT4, 64);
   return KVFA_RUN(KV_FP8, 64);
 #undef KVFA_RUN
-#undef KVFA_RUN_APPEND
 }
 
 }  // namespace kvfa

@@ -1,7 +1,6 @@
 """kvc_attn_decode_append (kv_append + attn_decode in one call) against the
 two calls it replaces: identical outputs bit for bit and identical cache
-bytes, for every storage type (fused into the decode kernel for bf16/f16,
-append kernel first otherwise), with windows, several split counts, GQA
+bytes, for every storage type, with windows, several split counts, GQA
 groups wider than 16 query heads, and invalid device entries."""
 import numpy as np
 import pytest
@@ -40,7 +39,7 @@ def _same_pools(a, b):
 @pytest.mark.parametrize("dtype,n_q,n_kv,d", [("bf16", 32, 8, 128), ("fp16", 12, 4, 64),
                                               ("bf16", 32, 1, 128), ("fp8", 64, 8, 128),
                                               ("int4", 16, 4, 64), ("f32", 8, 2, 128)])
-def test_fused_equals_append_then_decode(dtype, n_q, n_kv, d):
+def test_decode_append_equals_append_then_decode(dtype, n_q, n_kv, d):
     w, A, B = _pair(dtype, n_q, n_kv, d, (1, 300))
     io = A.io
     for step in range(3):                              # crosses block boundaries for some
@@ -59,7 +58,7 @@ def bits_t(t):
     return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
 
 
-def test_fused_with_window_and_vs_oracle():
+def test_decode_append_with_window_and_vs_oracle():
     w, A, B = _pair("bf16", 32, 8, 128, (200, 700), tag="dappw")
     k, v, q = _new_rows(w, A.io)
     for X in (A, B):
@@ -80,7 +79,7 @@ def test_fused_with_window_and_vs_oracle():
         assert_close(f64(yb[b]), r, what=f"seq {b}")
 
 
-def test_fused_invalid_entries_match_two_calls():
+def test_decode_append_invalid_entries_match_two_calls():
     w, A, B = _pair("bf16", 32, 8, 128, (5, 90), batch=4, tag="dappi")
     k, v, q = _new_rows(w, A.io)
     seqs = torch.tensor([0, 99, 2, -1], dtype=torch.int32, device="cuda")
@@ -97,7 +96,7 @@ def test_fused_invalid_entries_match_two_calls():
     assert torch.equal(bits_t(ya[ok]), bits_t(yb[ok]))
 
 
-def test_fused_rejects_bad_arguments():
+def test_decode_append_rejects_bad_arguments():
     w, A, _ = _pair("bf16", 8, 2, 64, (3, 20), batch=2, tag="dappe")
     k, v, q = _new_rows(w, A.io)
     rc = kv.lib().kvc_attn_decode_append(A.c._h, 0, 2, A.seqs.data_ptr(), None, None,

@@ -80,7 +80,7 @@ def test_llama8b_decode_full_all_outputs():
     print(f"llama8b decode: worst abs {worst[0]:.2e} rel {worst[1]:.2e}")
 
 
-def test_llama8b_fused_append_decode_full_all_outputs():
+def test_llama8b_append_decode_full_all_outputs():
     """The bench's step at full size: rows 0..L-2 written in bulk, a grow,
     then kvc_attn_decode_append with row L-1 (appended inside the decode
     kernel); every output against the oracle, and the appended rows read

@@ -1,6 +1,6 @@
 """Decode of batches wider than one launch's share (more than 2,048
 sequences are run as consecutive sub-batches): every row against the
-oracle, then a fused append + decode step across the sub-batch boundary."""
+oracle, then an append + decode step (one call) across the sub-batch boundary."""
 import math
 
 import numpy as np
@@ -24,7 +24,7 @@ def test_decode_more_than_2048_sequences():
     for s in range(w.batch):
         K, V = b.m.logical_values(0, s)
         assert_close(y[s], A.decode_attention(qd[s], K, V, scale), what=f"seq {s}")
-    # one fused append + decode step over the same batch
+    # one append + decode step (one call) over the same batch
     rng = np.random.default_rng(3)
     k = torch.from_numpy(rng.standard_normal((w.batch, w.n_kv, w.d), dtype=np.float32)).to(
         torch.bfloat16).cuda()
@@ -38,5 +38,5 @@ def test_decode_more_than_2048_sequences():
         b.m.write_rows(0, s, int(b.m.length[s]) - 1, bits(k[s:s + 1]), bits(v[s:s + 1]))
         if s in checked:
             K, V = b.m.logical_values(0, s)
-            assert_close(y2[s], A.decode_attention(qd[s], K, V, scale), what=f"fused seq {s}")
+            assert_close(y2[s], A.decode_attention(qd[s], K, V, scale), what=f"append+decode seq {s}")
     assert b.pools_equal()
