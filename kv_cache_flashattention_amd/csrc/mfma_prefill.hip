@@ -320,6 +320,32 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
   const int tg = tid & 255;
   const int koff = (tg / KG) * (int)kvstride + 8 * (tg % KG);
   const int voff = 4 * (tg % (BN / 4)) * (int)kvstride + 8 * (tg / (BN / 4));
+  // Paged staging: a tile's block ids are read (ktab / vtab) before the
+  // staging group writes its previous tile into LDS, so the table round
+  // trip overlaps those writes and the data loads (load_k / load_v) start
+  // without waiting for it.  Slab offsets: block id times the slab size,
+  // both below 2^32, as one 32 x 32 -> 64-bit product.
+  int kblk[KCH], sblk = 0, vblk = 0;
+  auto slab_off = [](int e, int64_t n) { return (int64_t)((uint64_t)(uint32_t)e * (uint32_t)n); };
+  auto ktab = [&](int li) {
+    if constexpr (PAGED) {
+      const int i = tile_of(li);
+      const int lim = L - 1 - BN * i;
+      const int t = opaque_tid() & 255;
+#pragma unroll
+      for (int c0 = 0; c0 < KCH; ++c0) kblk[c0] = btab[(BN * i + min(t / KG + c0 * (256 / KG), lim)) >> 4];
+      if constexpr (SC != 0) {
+        if (t < 4) sblk = btab[min(BN * i + kBlock * t, L - 1) >> 4];
+      }
+    }
+  };
+  auto vtab = [&](int li) {
+    if constexpr (PAGED) {
+      const int i = tile_of(li);
+      const int t = opaque_tid() & 255;
+      vblk = btab[min(BN * i + kBlock * ((t >> 1) & 3), L - 1) >> 4];   // block (c / 2) % 4 of every chunk
+    }
+  };
   auto load_k = [&](int li) {
     const int i = tile_of(li);
     const int lim = L - 1 - BN * i;                    // last valid row of the tile
@@ -328,24 +354,23 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
 #pragma unroll
       for (int c0 = 0; c0 < KCH; ++c0) {
         const int kp = BN * i + min(t / KG + c0 * (256 / KG), lim);
-        const int e = btab[kp >> 4];
+        const int e = kblk[c0];
         if constexpr (FP8) {
-          const uint2 x = *(const uint2*)(kpool8 + e * slab8 + (kp & (kBlock - 1)) * D + 8 * (t % KG));
+          const uint2 x = *(const uint2*)(kpool8 + slab_off(e, slab8) + (kp & (kBlock - 1)) * D + 8 * (t % KG));
           sreg[c0] = u32x4{x.x, x.y, 0u, 0u};
         } else if constexpr (I4) {
-          const uint32_t x = *(const uint32_t*)(kpool8 + e * slab8 + (kp & (kBlock - 1)) * (D / 2) +
+          const uint32_t x = *(const uint32_t*)(kpool8 + slab_off(e, slab8) + (kp & (kBlock - 1)) * (D / 2) +
                                                 4 * (t % KG));
           sreg[c0] = u32x4{x, 0u, 0u, 0u};
         } else {
-          const uint16_t* sl = kpool + e * slab;
+          const uint16_t* sl = kpool + slab_off(e, slab);
           sreg[c0] = *(const u32x4*)(sl + (kp & (kBlock - 1)) * D + 8 * (t % KG));
         }
       }
       if constexpr (SC != 0) {
         if (t < 4) {
-          const int e = btab[min(BN * i + kBlock * t, L - 1) >> 4];
-          scK = cv.ks[sc0 + (int64_t)e * n_kv];
-          scV = cv.vs[sc0 + (int64_t)e * n_kv];
+          scK = cv.ks[sc0 + (int64_t)sblk * n_kv];
+          scV = cv.vs[sc0 + (int64_t)sblk * n_kv];
         }
       }
     } else {
@@ -391,17 +416,16 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
     if constexpr (PAGED) {
 #pragma unroll
       for (int c0 = 0; c0 < VCH; ++c0) {
-        const int c = t + 256 * c0, rr = c >> 3, j = (c >> 1) & 3, h = c & 1;
-        const int kb = min(BN * i + kBlock * j, L - 1) >> 4;
-        const int e = btab[kb];
+        const int c = t + 256 * c0, rr = c >> 3, h = c & 1;
+        const int e = vblk;
         if constexpr (FP8) {
-          const uint2 x = *(const uint2*)(vpool8 + e * slab8 + rr * kBlock + 8 * h);
+          const uint2 x = *(const uint2*)(vpool8 + slab_off(e, slab8) + rr * kBlock + 8 * h);
           sreg[c0] = u32x4{x.x, x.y, 0u, 0u};
         } else if constexpr (I4) {
-          const uint32_t x = *(const uint32_t*)(vpool8 + e * slab8 + rr * (kBlock / 2) + 4 * h);
+          const uint32_t x = *(const uint32_t*)(vpool8 + slab_off(e, slab8) + rr * (kBlock / 2) + 4 * h);
           sreg[c0] = u32x4{x, 0u, 0u, 0u};
         } else {
-          const uint16_t* sl = vpool + e * slab;
+          const uint16_t* sl = vpool + slab_off(e, slab);
           sreg[c0] = *(const u32x4*)(sl + rr * kBlock + 8 * h);
         }
       }
@@ -579,10 +603,13 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
 
   // ---- prologue: K_0 into LDS; loads of K_1 (group 1) and V_0 (group 0)
   if (grp == 1) {
+    ktab(0);
     load_k(0);
+    if (1 < nkt) ktab(1);
     store_k(0);
     if (1 < nkt) load_k(1);
   } else {
+    vtab(0);
     load_v(0);
   }
   __syncthreads();
@@ -601,6 +628,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
   // and the other wave's VALU work fills the remaining issue cycles.
   if (grp == 1) {
     if (1 < nkt) {
+      if (2 < nkt) ktab(2);
       store_k(1);
       if (2 < nkt) load_k(2);
     }
@@ -621,10 +649,12 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
     // staging first: its LDS writes drain while the exponentials run
     if (grp == 1) {
       if (i + 2 < nkt) {
+        if (i + 3 < nkt) ktab(i + 3);
         store_k(i & 1);
         if (i + 3 < nkt) load_k(i + 3);
       }
     } else if (i < nkt) {
+      if (i + 1 < nkt) vtab(i + 1);
       store_v(i & 1, i);
       if (i + 1 < nkt) load_v(i + 1);
     }
