@@ -544,7 +544,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
       // belong to the lane's block, so within the lane the map is increasing:
       // the lane's max is taken on the raw scores s and mapped once, the
       // lanes' maxima are combined, and exp2(p - m) is exp2(fma(s, a, b - m)).
-      const float a = fmaxf(sl2 * ksc, 1e-30f);
+      const float a = vmax(sl2 * ksc, 1e-30f);        // (a NaN scale stays NaN)
       const float b = KV == KV_INT4 ? qoff * a : 0.f;
       float sc[2][4];
 #pragma unroll
@@ -570,8 +570,11 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
       // exceeds it by more than kStale (log2 units), so most units skip the
       // rescale of O; probabilities stay below 2^kStale.  (m, l, O) remain a
       // consistent triple for the merge whatever m is.
-      if (__any(cmax > m + kStale)) {
-        const float m_new = fmaxf(m, cmax);
+      // (written so that a NaN max -- NaN scores or scales -- also takes the
+      // branch and makes m NaN: the merge then propagates it instead of
+      // taking the piece for an empty one)
+      if (__any(!(cmax <= m + kStale))) {
+        const float m_new = vmax(m, cmax);
         const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_new);
         m = m_new;
         lpart *= alpha;
@@ -681,7 +684,9 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
 // four waves per (query head, sequence): each wave folds every fourth piece
 // into its own running (M, den, acc) -- the same online rescale, four pieces
 // per step so their loads are in flight together -- and the four waves are
-// combined through LDS.  An entry without units (invalid) gets NaN.
+// combined through LDS.  An entry without units (invalid) gets NaN.  The
+// maxima are taken NaN-propagating, so a piece made NaN by a NaN input (a
+// score or a block scale) makes its row NaN instead of counting as empty.
 template <bool F16, int D>
 __global__ __launch_bounds__(256) void k_decode_work_merge(CacheView cv, const void* ws_,
                                                            uint16_t* out, int nb, int qgroups,
@@ -731,7 +736,7 @@ __global__ __launch_bounds__(256) void k_decode_work_merge(CacheView cv, const v
     }
     float Mn = M;
 #pragma unroll
-    for (int k = 0; k < UN; ++k) Mn = fmaxf(Mn, pm[k]);
+    for (int k = 0; k < UN; ++k) Mn = vmax(Mn, pm[k]);     // a NaN piece makes Mn NaN
     if (Mn == -INFINITY) continue;
     const float a = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
     den *= a;
@@ -753,7 +758,7 @@ __global__ __launch_bounds__(256) void k_decode_work_merge(CacheView cv, const v
 #pragma unroll
   for (int i = 0; i < J; ++i) sAcc[wv][lane + 64 * i] = acc[i];
   __syncthreads();
-  const float Mt = fmaxf(fmaxf(sM[0], sM[1]), fmaxf(sM[2], sM[3]));
+  const float Mt = vmax(vmax(sM[0], sM[1]), vmax(sM[2], sM[3]));
   float f[4], dt = 0.f;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {

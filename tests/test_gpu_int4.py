@@ -190,3 +190,30 @@ def test_prefill_with_scaled_cache_writes_codes_and_attends_in_bf16(dtype):
     for s in range(w.batch):
         K, V = m.logical_values(0, s)
         assert_close(y[s], A.decode_attention(f64(qd[s]), K, V, scale), what=f"decode seq {s}")
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3])
+@pytest.mark.parametrize("which", ["k", "v"])
+@pytest.mark.parametrize("dtype", ["fp8", "int4"])
+def test_decode_nan_block_scale_gives_nan_rows(dtype, which, splits):
+    """The scale arrays are caller memory: a NaN K or V scale in one (block,
+    kv head) makes exactly the query rows of that sequence and kv head NaN
+    (their softmax or weighted sum cannot be evaluated), and every other row
+    still matches the oracle -- under the work list, where the poisoned unit
+    may be the only one of its piece, and under fixed split counts."""
+    n_q, n_kv, d = 8, 2, 128
+    w = DecodeWorkload("nanscale" + dtype, 3, n_q, n_kv, d, dtype, 300)
+    b = Built(w)
+    q = torch.from_numpy(w.q()).to(b.io).cuda()
+    blk = b.c.seq_blocks(1)[2]
+    (b.c.k_scale if which == "k" else b.c.v_scale)[0, blk, 0] = float("nan")
+    torch.cuda.synchronize()
+    y = f64(b.c.attn_decode(0, b.seqs, q, num_splits=splits))
+    G = n_q // n_kv
+    assert np.all(np.isnan(y[1, :G])), "rows of the poisoned (sequence, kv head)"
+    scale = 1 / math.sqrt(d)
+    for s in range(w.batch):
+        K, V = b.m.logical_values(0, s)
+        r = A.decode_attention(f64(q[s]), K, V, scale)
+        rows = slice(G, n_q) if s == 1 else slice(0, n_q)
+        assert_close(y[s, rows], r[rows], what=f"{dtype} sequence {s}")
