@@ -26,10 +26,13 @@ The same JSON line carries one object per other workload, each with its own
   prefix_share          40 sequences sharing a 600-token prompt
 
 `roofline` is measured for the dominant call of each workload with HIP
-events recorded on the stream the library launches on: for decode, the same
-call repeated K times after the timed steps, each launch preceded by a read
-of a separate 1 GiB buffer that evicts the Infinity Cache; for prefill, over
-the timed launches.  `traffic` is the HBM bytes per call that rocprofv3's
+events on the stream the library launches on: for decode, the same call
+repeated K times after the timed steps, each launch preceded by a read of a
+separate 1 GiB buffer that evicts the Infinity Cache, and timed by dispatch
+events attached to the call's first and last kernels (kvc_set_dispatch_events:
+first kernel start to last kernel end, as a kernel trace shows it; the
+stream-marker time around the same calls is reported beside it as
+`avg_call_us_stream_markers`); for prefill, over the timed launches.  `traffic` is the HBM bytes per call that rocprofv3's
 FETCH_SIZE / WRITE_SIZE counters recorded (profiles/counters.json, scaled by
 a copy-kernel calibration), reported only while the kernel sources are
 unchanged since that measurement.  `cpu_baseline` times the float64 oracle
@@ -198,24 +201,36 @@ def window_rows(L, window, sinks):
     return len(pos), len(np.unique(pos // 16))
 
 
-def evict_and_time(call, steps, torch):
-    """Mean HIP-event time (s) of `call` over `steps` launches on the current
-    stream, each launch preceded by a full read of a separate 1 GiB buffer: the
-    read evicts the 256 MB Infinity Cache without leaving dirty lines, so the
-    call's K/V bytes all come from HBM."""
+def evict_and_time(call, steps, torch, cache):
+    """Mean times (s) of `call`, a decode on `cache`, over `steps` launches on
+    the current stream, each launch preceded by a full read of a separate
+    1 GiB buffer: the read evicts the 256 MB Infinity Cache without leaving
+    dirty lines, so the call's K/V bytes all come from HBM.  Two passes: one
+    timed by dispatch events (kvc_set_dispatch_events: from the start of the
+    call's first kernel to the end of its last), one by stream markers
+    recorded before and after the call (the hook unset, since its events add
+    packets of their own to the stream).  Returns (dispatch, markers)."""
     flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     sink = torch.empty((), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for e in ev:
+        for x in e[:2]:
+            x.record(stream)                          # creates the events the hook takes
     torch.cuda.synchronize()
     for i in range(steps):
         torch.sum(flush, dim=0, out=sink)
-        ev[i][0].record(stream)
+        cache.set_dispatch_events(ev[i][0], ev[i][1])
         call()
-        ev[i][1].record(stream)
+    for i in range(steps):
+        torch.sum(flush, dim=0, out=sink)
+        ev[i][2].record(stream)
+        call()
+        ev[i][3].record(stream)
     torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    disp = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) / 1e3
+    mark = float(np.mean([e[2].elapsed_time(e[3]) for e in ev])) / 1e3
+    return disp, mark
 
 
 def bench_decode_window(steps, torch, kv, window=1024, sinks=4):
@@ -236,13 +251,14 @@ def bench_decode_window(steps, torch, kv, window=1024, sinks=4):
     def call():
         c.attn_decode(0, seqs, q, out=out, ws=ws, window=window, sinks=sinks)
     warm_up_clocks(call, torch)
-    call_s = evict_and_time(call, steps, torch)
+    call_s, mark_s = evict_and_time(call, steps, torch, c)
     achieved = per_call / call_s / 1e9
     return {"workload": f"llama8b_decode, window {window} + {sinks} sink rows",
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                          "kernel": "kvc_attn_decode_window (work list + merge)",
                          "avg_call_us": call_s * 1e6, "bytes_per_call": per_call,
+                         "avg_call_us_stream_markers": mark_s * 1e6,
                          "cache_evicted_before_each_call": True},
             "visible_rows": rows, "all_rows": int(np.sum(w.lengths))}
 
@@ -300,7 +316,7 @@ def bench_decode(name, steps, warmup, torch, kv, with_cpu):
     # roofline: the same decode call (state after the timed steps), cold
     lens1 = lens0 + steps
     per_call = decode_bytes(w, lens1, kv_elem)
-    kern_avg_s = evict_and_time(call, steps, torch)
+    kern_avg_s, mark_s = evict_and_time(call, steps, torch, c)
     achieved = per_call / kern_avg_s / 1e9
     res = {
         "workload": name,
@@ -312,6 +328,7 @@ def bench_decode(name, steps, warmup, torch, kv, with_cpu):
                      "traffic": counter_traffic("decode_" + name),
                      "kernel": "kvc_attn_decode (work-list partials + merge)",
                      "avg_call_us": kern_avg_s * 1e6, "bytes_per_call": per_call,
+                     "avg_call_us_stream_markers": mark_s * 1e6,
                      "cache_evicted_before_each_call": True,
                      "avg_call_us_warm_with_append": warm_avg_s * 1e6},
         "shape": {"batch": w.batch, "n_q": w.n_q, "n_kv": w.n_kv, "d": w.d,

@@ -356,6 +356,19 @@ int kvc_attn_decode_noalloc(kvc_cache* cache, int32_t layer, int32_t n, const in
 int kvc_gather(const kvc_cache* cache, int32_t layer, int32_t seq, int32_t start, int32_t count,
                void* k_out_dev, void* v_out_dev, hipStream_t stream);
 
+/* Timing hook for measuring a decode call's kernels alone.  The next decode
+ * call on this cache (kvc_attn_decode, _window, _append or _noalloc) records
+ * start_event when the first kernel it launches begins and stop_event when
+ * the last one ends: the events are attached to those kernels' own
+ * dispatches (hipExtLaunchKernel), so the time between them covers the
+ * call's kernels and the gaps between them, but no stream-marker overhead.
+ * Both are hipEvent_t handles created by the caller with timing enabled on
+ * the cache's device; either may be NULL; the caller keeps ownership.  The
+ * events are used by that one call (whether it launches or fails) and then
+ * forgotten; passing two NULLs clears them.  A call that launches nothing
+ * (n = 0) records neither.  Returns KVC_E_INVAL for a NULL cache. */
+int kvc_set_dispatch_events(kvc_cache* cache, void* start_event, void* stop_event);
+
 /* Message describing the last failure on the calling thread ("" if none). */
 const char* kvc_last_error(void);
 

@@ -507,27 +507,23 @@ hipError_t launch_copy_blocks(const CacheView& cv, const BlockCopy& u, hipStream
 }
 
 hipError_t launch_append(const CacheView& cv, int layer, int n, const int32_t* seqs,
-                         const void* k, const void* v, hipStream_t s) {
+                         const void* k, const void* v, hipStream_t s, hipEvent_t start) {
   dim3 grid(n, cv.n_kv);
   switch (cv.dtype) {
     case KVC_F32:
-      hipLaunchKernelGGL(k_append_copy<uint32_t>, grid, dim3(64), 0, s, cv, layer, seqs,
-                         (const uint32_t*)k, (const uint32_t*)v);
-      break;
+      return launch_ev(k_append_copy<uint32_t>, grid, dim3(64), s, start, nullptr, cv, layer,
+                       seqs, (const uint32_t*)k, (const uint32_t*)v);
     case KVC_F16:
     case KVC_BF16:
-      hipLaunchKernelGGL(k_append_copy<uint16_t>, grid, dim3(64), 0, s, cv, layer, seqs,
-                         (const uint16_t*)k, (const uint16_t*)v);
-      break;
+      return launch_ev(k_append_copy<uint16_t>, grid, dim3(64), s, start, nullptr, cv, layer,
+                       seqs, (const uint16_t*)k, (const uint16_t*)v);
     case KVC_INT4:
-      hipLaunchKernelGGL(k_write_int4, dim3(1, cv.n_kv, n), dim3(256), 0, s, cv, layer, seqs, -1,
-                         1, (const uint16_t*)k, (const uint16_t*)v);
-      break;
+      return launch_ev(k_write_int4, dim3(1, cv.n_kv, n), dim3(256), s, start, nullptr, cv, layer,
+                       seqs, -1, 1, (const uint16_t*)k, (const uint16_t*)v);
     default:
-      hipLaunchKernelGGL(k_append_fp8, grid, dim3(64), 0, s, cv, layer, seqs,
-                         (const uint16_t*)k, (const uint16_t*)v);
+      return launch_ev(k_append_fp8, grid, dim3(64), s, start, nullptr, cv, layer, seqs,
+                       (const uint16_t*)k, (const uint16_t*)v);
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_write(const CacheView& cv, int layer, int n, const int32_t* seqs, int start,

@@ -25,7 +25,8 @@ namespace kvfa {
 
 hipError_t launch_decode_mfma(const CacheView& cv, int layer, int n, const int32_t* seqs,
                               const void* q, void* out, float scale_log2, const DecodePlan& plan,
-                              void* ws, int window, int sinks, hipStream_t s, bool* handled);
+                              void* ws, int window, int sinks, hipStream_t s, DispatchEvents ev,
+                              bool* handled);
 
 DecodePlan make_decode_plan(const CacheView& cv, int32_t n, int32_t max_len, int32_t num_splits,
                             int32_t cu_count) {
@@ -216,27 +217,29 @@ __global__ __launch_bounds__(64) void k_decode_merge(CacheView cv, const int32_t
 
 template <typename E, typename IO, int D>
 hipError_t run_valu(const CacheView& cv, int layer, int n, const int32_t* seqs, const void* q,
-                    void* out, float scale_log2, const DecodePlan& p, void* ws, hipStream_t st) {
-  hipLaunchKernelGGL((k_decode_valu<E, IO, D>), dim3(p.splits, cv.n_q, n), dim3(64), 0, st, cv,
-                     layer, seqs, (const IO*)q, (IO*)out, ws, n, p.splits, p.split_len,
-                     scale_log2);
-  hipError_t e = hipGetLastError();
+                    void* out, float scale_log2, const DecodePlan& p, void* ws, hipStream_t st,
+                    DispatchEvents ev) {
+  hipError_t e = launch_ev(k_decode_valu<E, IO, D>, dim3(p.splits, cv.n_q, n), dim3(64), st,
+                           ev.start, p.splits == 1 ? ev.stop : nullptr, cv, layer, seqs,
+                           (const IO*)q, (IO*)out, ws, n, p.splits, p.split_len, scale_log2);
   if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL((k_decode_merge<IO, D>), dim3(cv.n_q, n), dim3(64), 0, st, cv, seqs,
-                     (IO*)out, (const void*)ws, n, p.splits, p.split_len);
-  return hipGetLastError();
+  return launch_ev(k_decode_merge<IO, D>, dim3(cv.n_q, n), dim3(64), st, nullptr, ev.stop, cv,
+                   seqs, (IO*)out, (const void*)ws, n, p.splits, p.split_len);
 }
 
 template <int D>
 hipError_t run_valu_d(const CacheView& cv, int layer, int n, const int32_t* seqs, const void* q,
-                      void* out, float sl2, const DecodePlan& p, void* ws, hipStream_t st) {
+                      void* out, float sl2, const DecodePlan& p, void* ws, hipStream_t st,
+                      DispatchEvents ev) {
+#define KVFA_RUN(E, IO) run_valu<E, IO, D>(cv, layer, n, seqs, q, out, sl2, p, ws, st, ev)
   switch (cv.dtype) {
-    case KVC_F32: return run_valu<float, float, D>(cv, layer, n, seqs, q, out, sl2, p, ws, st);
-    case KVC_F16: return run_valu<_Float16, _Float16, D>(cv, layer, n, seqs, q, out, sl2, p, ws, st);
-    case KVC_BF16: return run_valu<BF16, BF16, D>(cv, layer, n, seqs, q, out, sl2, p, ws, st);
-    case KVC_FP8_E4M3FN: return run_valu<uint8_t, BF16, D>(cv, layer, n, seqs, q, out, sl2, p, ws, st);
+    case KVC_F32: return KVFA_RUN(float, float);
+    case KVC_F16: return KVFA_RUN(_Float16, _Float16);
+    case KVC_BF16: return KVFA_RUN(BF16, BF16);
+    case KVC_FP8_E4M3FN: return KVFA_RUN(uint8_t, BF16);
     default: return hipErrorInvalidValue;                // int4 runs on the matrix cores only
   }
+#undef KVFA_RUN
 }
 
 }  // namespace
@@ -244,23 +247,24 @@ hipError_t run_valu_d(const CacheView& cv, int layer, int n, const int32_t* seqs
 hipError_t launch_decode(const CacheView& cv, int layer, int n, const int32_t* seqs,
                          const void* q, void* out, float scale, const DecodePlan& plan,
                          void* ws, int window, int sinks, const void* knew, const void* vnew,
-                         hipStream_t s) {
+                         hipStream_t s, DispatchEvents ev) {
   const float sl2 = scale * kLog2e;
   // The newest rows go in by the append kernel, ordered before the decode on
   // the stream.  (A decode kernel that took position L-1 from knew / vnew and
   // stored the row itself saved that launch but ran its unit loop slower:
   // 89.6 against 87.9 us per Llama-8B-shaped decode step.)
   if (knew != nullptr) {
-    hipError_t e = launch_append(cv, layer, n, seqs, knew, vnew, s);
+    hipError_t e = launch_append(cv, layer, n, seqs, knew, vnew, s, ev.start);
     if (e != hipSuccess) return e;
+    ev.start = nullptr;                                 // the append kernel opened the call
   }
   bool handled = false;
   hipError_t e = launch_decode_mfma(cv, layer, n, seqs, q, out, sl2, plan, ws, window, sinks, s,
-                                    &handled);
+                                    ev, &handled);
   if (handled) return e;
   if (window > 0) return hipErrorInvalidValue;          // the VALU kernel has no window
-  if (cv.d == 128) return run_valu_d<128>(cv, layer, n, seqs, q, out, sl2, plan, ws, s);
-  return run_valu_d<64>(cv, layer, n, seqs, q, out, sl2, plan, ws, s);
+  if (cv.d == 128) return run_valu_d<128>(cv, layer, n, seqs, q, out, sl2, plan, ws, s, ev);
+  return run_valu_d<64>(cv, layer, n, seqs, q, out, sl2, plan, ws, s, ev);
 }
 
 }  // namespace kvfa

@@ -48,6 +48,8 @@ struct kvc_cache {
   // Device address of the library-owned decode scratch on the device the
   // handle was created on (kvc_attn_decode_noalloc).
   void* scratch = nullptr;
+  // Dispatch events for the next decode call (kvc_set_dispatch_events).
+  DispatchEvents timing{};
   ~kvc_cache() {
     if (fork) (void)hipEventDestroy(fork);
     if (join) (void)hipEventDestroy(join);
@@ -634,6 +636,8 @@ int decode_impl(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs, con
                 int32_t sinks, int32_t num_splits, void* ws, uint64_t ws_bytes,
                 hipStream_t stream) {
   if (!c) return fail(KVC_E_INVAL, "cache is NULL");
+  const DispatchEvents ev = c->timing;                 // this call's, whatever its outcome
+  c->timing = DispatchEvents{};
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(KVC_E_INVAL, "scale must be finite and positive");
   int rw = check_window(c, window, sinks);
@@ -655,7 +659,7 @@ int decode_impl(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs, con
                                      " bytes");
   if (p.ws_bytes > 0 && !aligned16(ws)) return fail(KVC_E_INVAL, "workspace must be 16-byte aligned");
   hipError_t e = launch_decode(c->view(), layer, n, seqs, q, out, scale, p, ws, window, sinks,
-                               knew, vnew, stream);
+                               knew, vnew, stream, ev);
   return e == hipSuccess ? KVC_OK : hip_fail(e, "decode launch");
 }
 }  // namespace
@@ -671,7 +675,10 @@ int kvc_attn_decode_append(kvc_cache* c, int32_t layer, int32_t n, const int32_t
                            const void* k_new, const void* v_new, const void* q, void* out,
                            float scale, int32_t window, int32_t sinks, int32_t num_splits,
                            void* ws, uint64_t ws_bytes, hipStream_t stream) {
-  if (!k_new || !v_new) return fail(KVC_E_INVAL, "k_new/v_new is NULL");
+  if (!k_new || !v_new) {
+    if (c) c->timing = DispatchEvents{};
+    return fail(KVC_E_INVAL, "k_new/v_new is NULL");
+  }
   return decode_impl(c, layer, n, seqs, k_new, v_new, q, out, scale, window, sinks, num_splits,
                      ws, ws_bytes, stream);
 }
@@ -681,18 +688,29 @@ int kvc_attn_decode_noalloc(kvc_cache* c, int32_t layer, int32_t n, const int32_
                             hipStream_t stream) {
   if (!c) return fail(KVC_E_INVAL, "cache is NULL");
   int r = need_dev(c);
-  if (r) return r;
-  if (n < 0 || num_splits < 0) return fail(KVC_E_INVAL, "negative size");
+  if (r || n < 0 || num_splits < 0) {
+    c->timing = DispatchEvents{};
+    return r ? r : fail(KVC_E_INVAL, "negative size");
+  }
   if (n > 0) {
     DecodePlan p = make_decode_plan(c->view(), n, live_max_len(c), num_splits, c->cu_count);
-    if (p.ws_bytes > kScratchBytes)
+    if (p.ws_bytes > kScratchBytes) {
+      c->timing = DispatchEvents{};
       return fail(KVC_E_WORKSPACE, "the call needs " + std::to_string(p.ws_bytes) +
                                        " bytes of workspace, more than the library scratch (" +
                                        std::to_string(kScratchBytes) +
                                        " bytes): use kvc_attn_decode with a workspace");
+    }
   }
   return decode_impl(c, layer, n, seqs, nullptr, nullptr, q, out, scale, 0, 0, num_splits,
                      c->scratch, kScratchBytes, stream);
+}
+
+int kvc_set_dispatch_events(kvc_cache* c, void* start_event, void* stop_event) {
+  if (!c) return fail(KVC_E_INVAL, "cache is NULL");
+  c->timing.start = (hipEvent_t)start_event;
+  c->timing.stop = (hipEvent_t)stop_event;
+  return KVC_OK;
 }
 
 int kvc_gather(const kvc_cache* c, int32_t layer, int32_t seq, int32_t start, int32_t count,

@@ -3,6 +3,10 @@
 
 #include <stdint.h>
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
+
+#include <tuple>
+#include <utility>
 
 #include "kvfa.h"
 
@@ -83,21 +87,47 @@ DecodePlan make_decode_plan(const CacheView& cv, int32_t n, int32_t max_len, int
 uint64_t work_list_ws_bytes(const CacheView& cv, int32_t nb, int32_t waves);
 int work_list_waves_per_cu(const CacheView& cv);
 
+// Dispatch events of one call (kvc_set_dispatch_events): `start` is recorded
+// as the call's first kernel begins, `stop` as its last kernel ends.
+struct DispatchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+// Launch of kernel k, optionally with dispatch events (hipExtLaunchKernel
+// records them from the kernel's own dispatch, not as separate stream
+// markers).  The arguments are converted to the kernel's parameter types.
+template <typename... P, size_t... I>
+hipError_t launch_args(void (*k)(P...), dim3 grid, dim3 block, hipStream_t s, hipEvent_t start,
+                       hipEvent_t stop, std::tuple<P...>& t, std::index_sequence<I...>) {
+  void* args[] = {(void*)&std::get<I>(t)..., nullptr};
+  if (!start && !stop) return hipLaunchKernel((const void*)k, grid, block, args, 0, s);
+  return hipExtLaunchKernel((const void*)k, grid, block, args, 0, s, start, stop, 0);
+}
+template <typename... P, typename... A>
+hipError_t launch_ev(void (*k)(P...), dim3 grid, dim3 block, hipStream_t s, hipEvent_t start,
+                     hipEvent_t stop, A... a) {
+  std::tuple<P...> t(a...);
+  return launch_args(k, grid, block, s, start, stop, t, std::index_sequence_for<P...>{});
+}
+
 // Launchers: return hipSuccess or the launch error.
 hipError_t launch_fill_tables(const CacheView& cv, hipStream_t s);
 hipError_t launch_table_update(const CacheView& cv, const TableUpdate& u, hipStream_t s);
 hipError_t launch_copy_blocks(const CacheView& cv, const BlockCopy& u, hipStream_t s);
+// start: dispatch event recorded as the append kernel begins (or null).
 hipError_t launch_append(const CacheView& cv, int layer, int n, const int32_t* seqs,
-                         const void* k, const void* v, hipStream_t s);
+                         const void* k, const void* v, hipStream_t s,
+                         hipEvent_t start = nullptr);
 hipError_t launch_write(const CacheView& cv, int layer, int n, const int32_t* seqs, int start,
                         int T, const void* k, const void* v, hipStream_t s);
 hipError_t launch_gather(const CacheView& cv, int layer, int seq, int start, int count,
                          void* k_out, void* v_out, hipStream_t s);
 // knew / vnew non-null: append those rows (kv_append) as part of the call.
+// ev: dispatch events of the call's first and last kernels (or nulls).
 hipError_t launch_decode(const CacheView& cv, int layer, int n, const int32_t* seqs,
                          const void* q, void* out, float scale, const DecodePlan& plan,
                          void* ws, int window, int sinks, const void* knew, const void* vnew,
-                         hipStream_t s);
+                         hipStream_t s, DispatchEvents ev = {});
 // window > 0: key j visible to position p iff p - window < j <= p or
 // j < sinks; window = 0: full causal attention.
 hipError_t launch_prefill(const CacheView& cv, int n, int T, const void* q, const void* k,

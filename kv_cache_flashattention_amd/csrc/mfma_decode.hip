@@ -776,7 +776,7 @@ __global__ __launch_bounds__(256) void k_decode_work_merge(CacheView cv, const v
 template <int KV, int D>
 hipError_t run(const CacheView& cv, int layer, int n, const int32_t* seqs, const void* q,
                void* out, float sl2, const DecodePlan& p, void* ws, int window, int sinks,
-               hipStream_t st) {
+               hipStream_t st, DispatchEvents ev) {
   const int G = cv.n_q / cv.n_kv;
   const int qgroups = (G + 15) / 16;
   const int grid = (p.waves + 3) / 4;
@@ -784,13 +784,13 @@ hipError_t run(const CacheView& cv, int layer, int n, const int32_t* seqs, const
     const int nb = n - b0 < kMaxBatch ? n - b0 : kMaxBatch;
     const uint16_t* qb = (const uint16_t*)q + (int64_t)b0 * cv.n_q * D;
     uint16_t* ob = (uint16_t*)out + (int64_t)b0 * cv.n_q * D;
-    hipLaunchKernelGGL((k_decode_work<KV, D>), dim3(grid), dim3(256), 0, st, cv, layer,
-                       seqs + b0, qb, ws, nb, qgroups, p.waves, sl2, window, sinks);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_ev(k_decode_work<KV, D>, dim3(grid), dim3(256), st,
+                             b0 == 0 ? ev.start : nullptr, nullptr, cv, layer, seqs + b0, qb, ws,
+                             nb, qgroups, p.waves, sl2, window, sinks);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_decode_work_merge<KV == KV_F16, D>), dim3(cv.n_q, nb), dim3(256), 0, st,
-                       cv, (const void*)ws, ob, nb, qgroups, p.waves);
-    e = hipGetLastError();
+    e = launch_ev(k_decode_work_merge<KV == KV_F16, D>, dim3(cv.n_q, nb), dim3(256), st, nullptr,
+                  b0 + nb == n ? ev.stop : nullptr, cv, (const void*)ws, ob, nb, qgroups,
+                  p.waves);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -849,10 +849,11 @@ int work_list_waves_per_cu(const CacheView& cv) {
 
 hipError_t launch_decode_mfma(const CacheView& cv, int layer, int n, const int32_t* seqs,
                               const void* q, void* out, float sl2, const DecodePlan& p, void* ws,
-                              int window, int sinks, hipStream_t st, bool* handled) {
+                              int window, int sinks, hipStream_t st, DispatchEvents ev,
+                              bool* handled) {
   *handled = p.work_list != 0;
   if (!*handled) return hipSuccess;
-#define KVFA_RUN(KVT, DD) run<KVT, DD>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st)
+#define KVFA_RUN(KVT, DD) run<KVT, DD>(cv, layer, n, seqs, q, out, sl2, p, ws, window, sinks, st, ev)
   if (cv.d == 128) {
     if (cv.dtype == KVC_BF16) return KVFA_RUN(KV_BF16, 128);
     if (cv.dtype == KVC_F16) return KVFA_RUN(KV_F16, 128);
