@@ -255,6 +255,10 @@ __device__ __forceinline__ int64_t uni64(int64_t x) {
 
 // floor(a * W / P) without overflow: W = qP + r.
 __device__ __forceinline__ int64_t share(int64_t a, int64_t W, int64_t P) {
+  if ((W >> 31) == 0 && (P >> 16) == 0) {              // the common sizes: 32-bit divisions
+    const uint32_t w = (uint32_t)W, p = (uint32_t)P, x = (uint32_t)a;
+    return (int64_t)(x * (w / p) + (x * (w % p)) / p);
+  }
   return a * (W / P) + (a * (W % P)) / P;
 }
 
@@ -283,31 +287,37 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
   const int64_t slots = work_slots(nb, nkvg, waves);
   WorkWs W_ = work_ws(ws, slots, D, nb);
 
-  // ---- unit counts and their prefix sums (8 entries per thread, nb <= 2048).
-  // The batch's sequence ids and, when the cache has at most kLenCache
-  // sequences, all of their lengths are loaded together, so the lengths do
-  // not wait for the ids.
+  // ---- unit counts and their prefix sums: up to 8 contiguous entries per
+  // thread (nb <= 2048), one per thread when nb <= 256 so that no wave works
+  // through the entries alone.  The batch's sequence ids and, when the cache
+  // has at most kLenCache sequences, all of their lengths are loaded
+  // together, so the lengths do not wait for the ids.
   {
     const bool lens_in_lds = cv.max_seqs <= kLenCache;
+    const int per = nb <= 256 ? 1 : 8;                   // wave-uniform
     int sqv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int b = tid * 8 + i;
-      sqv[i] = b < nb ? seqs[b] : -1;
+      const int b = tid * per + i;
+      sqv[i] = i < per && b < nb ? seqs[b] : -1;
     }
     if (lens_in_lds)
       for (int i = tid; i < cv.max_seqs; i += 256) s_lenall[i] = cv.len[i];
     __syncthreads();
     int64_t loc[8], tsum = 0;
+    int lv[8];                                          // LDS lengths, read before any branch
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      lv[i] = lens_in_lds ? s_lenall[sqv[i] >= 0 && sqv[i] < cv.max_seqs ? sqv[i] : 0] : 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int b = tid * 8 + i;
+      const int b = tid * per + i;
       int c = 0;
-      if (b < nb) {
+      if (i < per && b < nb) {
         const int sq = sqv[i];
         int L;
         if (lens_in_lds) {
-          L = sq >= 0 && sq < cv.max_seqs ? s_lenall[sq] : -1;
+          L = sq >= 0 && sq < cv.max_seqs ? lv[i] : -1;
           if (L <= 0 || L > cv.max_bps * kBlock) L = -1;
         } else {
           L = valid_len(cv, sq);
@@ -320,11 +330,24 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
       loc[i] = (int64_t)c * nkvg;
       tsum += loc[i];
     }
+    // inclusive scan of the threads' sums over the wave: 32-bit when the
+    // batch's unit count is bounded below 2^31 (each segment holds at most
+    // max_bps / 2 + 1 units)
     int64_t x = tsum;
+    if ((int64_t)nb * (cv.max_bps / 2 + 1) * nkvg < (1ll << 31)) {
+      int32_t x32 = (int32_t)tsum;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int64_t y = __shfl_up(x, o, 64);
-      if (lane >= o) x += y;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int32_t y = __shfl_up(x32, o, 64);
+        if (lane >= o) x32 += y;
+      }
+      x = x32;
+    } else {
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int64_t y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
     }
     if (lane == 63) s_wsum[tid >> 6] = x;
     __syncthreads();
@@ -332,8 +355,8 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
     for (int i = 0; i < (tid >> 6); ++i) ex += s_wsum[i];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int b = tid * 8 + i;
-      if (b < nb) s_units[b] = ex;
+      const int b = tid * per + i;
+      if (i < per && b < nb) s_units[b] = ex;
       ex += loc[i];
     }
     if (tid == 0) s_units[nb] = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
@@ -351,15 +374,19 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
   const int64_t u1 = share(gw + 1, Wt, waves);
 
   // entry holding unit u: the last b with s_units[b] <= u (entries without
-  // units share their offset with the next entry and are skipped this way)
+  // units share their offset with the next entry and are skipped this way).
+  // The offsets do not decrease, so the entries at or below u are a prefix:
+  // count them 64 at a time with one LDS read and a ballot per chunk.
   int b = 0;
   {
-    int lo = 0, hi = nb - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_units[mid] <= u) lo = mid; else hi = mid - 1;
+    int k = 0;
+    for (int c0 = 0; c0 < nb; c0 += 64) {              // wave-uniform
+      const int e = c0 + lane;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(e < nb && s_units[e < nb ? e : 0] <= u);
+      k += __builtin_popcountll(m);
+      if (m != ~0ull) break;
     }
-    b = uni(lo);
+    b = uni(k - 1);                                     // s_units[0] = 0 <= u: k >= 1
   }
 
   const uint8_t* kpool = (const uint8_t*)cv.k;
@@ -371,8 +398,14 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
     const int cb = uni(s_counts[b]);
     const int64_t sb = uni64(s_units[b]);
     const int64_t rem = u - sb;
-    const int kvg = (int)(rem / cb);
-    const int c0 = (int)(rem % cb);
+    int kvg, c0;
+    if ((rem >> 31) == 0) {                             // the common sizes: 32-bit division
+      kvg = (int)((uint32_t)rem / (uint32_t)cb);
+      c0 = (int)((uint32_t)rem - (uint32_t)kvg * (uint32_t)cb);
+    } else {
+      kvg = (int)(rem / cb);
+      c0 = (int)(rem % cb);
+    }
     const int64_t segend = sb + (int64_t)(kvg + 1) * cb;
     const int64_t pend = u1 < segend ? u1 : segend;
     const int c1 = c0 + (int)(pend - u);

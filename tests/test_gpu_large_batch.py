@@ -40,3 +40,21 @@ def test_decode_more_than_2048_sequences():
             K, V = b.m.logical_values(0, s)
             assert_close(y2[s], A.decode_attention(qd[s], K, V, scale), what=f"append+decode seq {s}")
     assert b.pools_equal()
+
+
+@pytest.mark.parametrize("batch", [64, 65, 256, 257, 700])
+def test_decode_batches_around_the_prologue_layouts(batch):
+    """The work list's prologue gives each thread one batch entry up to 256
+    entries and eight contiguous ones above; the wave's first entry is found
+    64 entries at a time.  Every row against the oracle on both sides of
+    those edges."""
+    print(f"batch {batch}", flush=True)
+    w = DecodeWorkload(f"edge{batch}", batch, 8, 2, 64, "bf16", (1, 200))
+    b = Built(w)
+    q = torch.from_numpy(w.q()).to(torch.bfloat16).cuda()
+    y = f64(b.c.attn_decode(0, b.seqs, q))
+    scale = 1 / math.sqrt(w.d)
+    qd = f64(q)
+    for s in range(w.batch):
+        K, V = b.m.logical_values(0, s)
+        assert_close(y[s], A.decode_attention(qd[s], K, V, scale), what=f"batch {batch}, seq {s}")
