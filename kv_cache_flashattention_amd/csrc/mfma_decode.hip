@@ -483,10 +483,6 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
         const int x = max(__builtin_amdgcn_readlane(tab, j + i), 0);   // invalid: NaN rows later
         sbase[i] = ((layer_blocks + x) * cv.n_kv + kvh) * SB;
       }
-      if constexpr (SCALED) {                         // this lane's block: table lane j + g/2
-        B.ksc = __shfl(tks, j + (g >> 1), 64);
-        B.vsc = __shfl(tvs, j + (g >> 1), 64);
-      }
       const uint8_t* krow = kpool + (tok_block(r16) ? sbase[1] : sbase[0]);
       if constexpr (KV == KV_INT4) {
 #pragma unroll
@@ -531,6 +527,12 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
           for (int dt = 0; dt < DT; ++dt)
             B.v[dt] = ld_stream4(vslab + 2 * (16 * dt + r16) * kBlock);
         }
+      }
+      // The block scales come from loads that wait for the block ids, so they
+      // are read after the K/V loads have gone out.
+      if constexpr (SCALED) {                         // this lane's block: table lane j + g/2
+        B.ksc = __shfl(tks, j + (g >> 1), 64);
+        B.vsc = __shfl(tvs, j + (g >> 1), 64);
       }
     };
 
