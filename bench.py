@@ -25,14 +25,18 @@ The same JSON line carries one object per other workload, each with its own
   decode_window         the headline batch under a 1,024-row window + 4 sinks
   prefix_share          40 sequences sharing a 600-token prompt
 
-`roofline` is measured for the dominant call of each workload with HIP
-events on the stream the library launches on: for decode, the same call
-repeated K times after the timed steps, each launch preceded by a read of a
-separate 1 GiB buffer that evicts the Infinity Cache, and timed by dispatch
-events attached to the call's first and last kernels (kvc_set_dispatch_events:
-first kernel start to last kernel end, as a kernel trace shows it; the
-stream-marker time around the same calls is reported beside it as
-`avg_call_us_stream_markers`); for prefill, over the timed launches.  `traffic` is the HBM bytes per call that rocprofv3's
+`roofline` is the dominant kernel of each workload: its algorithmic bytes
+(or FLOPs) over its duration, timed by HIP dispatch events attached to that
+kernel (kvc_set_dispatch_events), as a kernel trace times it.  Decode: the
+work-list kernel of the same call repeated K times after the timed steps,
+each launch preceded by a read of a separate 1 GiB buffer that evicts the
+Infinity Cache.  Prefill and extend: the attention kernel.  Beside it,
+`roofline.call` gives the whole library call: for decode the work-list
+kernel, the merge and the gap between them (first kernel start to last
+kernel end) and the same calls timed by stream markers; for prefill and
+extend the stream-marker time of the timed calls.  `traffic` is the HBM
+bytes per launch of the dominant kernel (in `call`: of every kernel of the
+call) that rocprofv3's
 FETCH_SIZE / WRITE_SIZE counters recorded (profiles/counters.json, scaled by
 a copy-kernel calibration), reported only while the kernel sources are
 unchanged since that measurement.  `cpu_baseline` times the float64 oracle
@@ -87,10 +91,11 @@ def kernel_source_digest():
     return h.hexdigest()
 
 
-def counter_traffic(key):
+def counter_traffic(key, kernel=None):
     """HBM bytes per call from rocprofv3 FETCH_SIZE / WRITE_SIZE runs recorded
-    in profiles/counters.json, scaled by the copy-kernel calibration factors;
-    None unless the kernels are byte-identical in source to those measured."""
+    in profiles/counters.json, scaled by the copy-kernel calibration factors
+    (with `kernel`: only the kernels whose names start with it); None unless
+    the kernels are byte-identical in source to those measured."""
     try:
         with open(COUNTERS) as fh:
             rec = json.load(fh)
@@ -100,8 +105,14 @@ def counter_traffic(key):
     if e is None or rec.get("kernel_source_sha256") != kernel_source_digest():
         return None
     cal = rec["calibration"]
-    return (e["fetch_kib_per_call"] * 1024 * cal["fetch_factor"]
-            + e["write_kib_per_call"] * 1024 * cal["write_factor"])
+    if kernel is None:
+        fetch, write = e["fetch_kib_per_call"], e["write_kib_per_call"]
+    else:
+        ks = [v for n, v in e["kernels"].items() if n.startswith(kernel)]
+        if not ks:
+            return None
+        fetch, write = sum(v["fetch_kib"] for v in ks), sum(v["write_kib"] for v in ks)
+    return fetch * 1024 * cal["fetch_factor"] + write * 1024 * cal["write_factor"]
 
 
 _T0 = time.perf_counter()
@@ -205,32 +216,69 @@ def evict_and_time(call, steps, torch, cache):
     """Mean times (s) of `call`, a decode on `cache`, over `steps` launches on
     the current stream, each launch preceded by a full read of a separate
     1 GiB buffer: the read evicts the 256 MB Infinity Cache without leaving
-    dirty lines, so the call's K/V bytes all come from HBM.  Two passes: one
-    timed by dispatch events (kvc_set_dispatch_events: from the start of the
-    call's first kernel to the end of its last), one by stream markers
-    recorded before and after the call (the hook unset, since its events add
-    packets of their own to the stream).  Returns (dispatch, markers)."""
+    dirty lines, so the call's K/V bytes all come from HBM.  Three passes:
+    dispatch events on the call's main kernel (the work-list kernel), dispatch
+    events from the call's first kernel's start to its last kernel's end
+    (kvc_set_dispatch_events), and stream markers recorded before and after
+    the call with the hook unset (its events add packets of their own to the
+    stream).  Returns (kernel, call, markers)."""
     flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     sink = torch.empty((), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
     for e in ev:
-        for x in e[:2]:
+        for x in e[:4]:
             x.record(stream)                          # creates the events the hook takes
     torch.cuda.synchronize()
+    for main, (i0, i1) in ((True, (0, 1)), (False, (2, 3))):
+        for i in range(steps):
+            torch.sum(flush, dim=0, out=sink)
+            cache.set_dispatch_events(ev[i][i0], ev[i][i1], main_kernel=main)
+            call()
     for i in range(steps):
         torch.sum(flush, dim=0, out=sink)
-        cache.set_dispatch_events(ev[i][0], ev[i][1])
+        ev[i][4].record(stream)
         call()
-    for i in range(steps):
-        torch.sum(flush, dim=0, out=sink)
-        ev[i][2].record(stream)
-        call()
-        ev[i][3].record(stream)
+        ev[i][5].record(stream)
     torch.cuda.synchronize()
-    disp = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) / 1e3
-    mark = float(np.mean([e[2].elapsed_time(e[3]) for e in ev])) / 1e3
-    return disp, mark
+    return tuple(float(np.mean([e[i0].elapsed_time(e[i0 + 1]) for e in ev])) / 1e3
+                 for i0 in (0, 2, 4))
+
+
+def dispatch_time(call, steps, torch, cache):
+    """Mean time (s) of the main kernel of `call` (an attention call on
+    `cache`) over `steps` launches, by dispatch events on that kernel."""
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in ev:
+        for x in e:
+            x.record(stream)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        cache.set_dispatch_events(ev[i][0], ev[i][1], main_kernel=True)
+        call()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+
+
+def decode_roofline(per_call, kern_s, call_s, mark_s, key, extra=None):
+    """The decode `roofline` object: algorithmic bytes over the work-list
+    kernel's time (the dominant kernel, as a kernel trace times it), with the
+    whole call (work list, merge and the gap between them) beside it."""
+    r = {"bound": "hbm", "achieved": per_call / kern_s / 1e9, "peak": HBM_PEAK_GBS,
+         "unit": "GB/s", "frac": per_call / kern_s / 1e9 / HBM_PEAK_GBS,
+         "traffic": counter_traffic(key, "k_decode_work<") if key else None,
+         "kernel": "k_decode_work (the work-list kernel; dispatch events on it)",
+         "avg_kernel_us": kern_s * 1e6, "bytes_per_call": per_call,
+         "cache_evicted_before_each_call": True,
+         "call": {"what": "kvc_attn_decode: work-list kernel, merge kernel and the gap "
+                          "between them (first kernel start to last kernel end)",
+                  "avg_us": call_s * 1e6, "achieved": per_call / call_s / 1e9,
+                  "frac": per_call / call_s / 1e9 / HBM_PEAK_GBS,
+                  "avg_us_stream_markers": mark_s * 1e6,
+                  "traffic": counter_traffic(key) if key else None}}
+    r.update(extra or {})
+    return r
 
 
 def bench_decode_window(steps, torch, kv, window=1024, sinks=4):
@@ -251,15 +299,9 @@ def bench_decode_window(steps, torch, kv, window=1024, sinks=4):
     def call():
         c.attn_decode(0, seqs, q, out=out, ws=ws, window=window, sinks=sinks)
     warm_up_clocks(call, torch)
-    call_s, mark_s = evict_and_time(call, steps, torch, c)
-    achieved = per_call / call_s / 1e9
+    kern_s, call_s, mark_s = evict_and_time(call, steps, torch, c)
     return {"workload": f"llama8b_decode, window {window} + {sinks} sink rows",
-            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                         "kernel": "kvc_attn_decode_window (work list + merge)",
-                         "avg_call_us": call_s * 1e6, "bytes_per_call": per_call,
-                         "avg_call_us_stream_markers": mark_s * 1e6,
-                         "cache_evicted_before_each_call": True},
+            "roofline": decode_roofline(per_call, kern_s, call_s, mark_s, None),
             "visible_rows": rows, "all_rows": int(np.sum(w.lengths))}
 
 
@@ -316,21 +358,14 @@ def bench_decode(name, steps, warmup, torch, kv, with_cpu):
     # roofline: the same decode call (state after the timed steps), cold
     lens1 = lens0 + steps
     per_call = decode_bytes(w, lens1, kv_elem)
-    kern_avg_s, mark_s = evict_and_time(call, steps, torch, c)
-    achieved = per_call / kern_avg_s / 1e9
+    kern_s, call_s, mark_s = evict_and_time(call, steps, torch, c)
     res = {
         "workload": name,
         "value": total_bytes / wall / 1e9,
         "unit": "GB/s",
         "ms_per_step": wall / steps * 1e3,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": counter_traffic("decode_" + name),
-                     "kernel": "kvc_attn_decode (work-list partials + merge)",
-                     "avg_call_us": kern_avg_s * 1e6, "bytes_per_call": per_call,
-                     "avg_call_us_stream_markers": mark_s * 1e6,
-                     "cache_evicted_before_each_call": True,
-                     "avg_call_us_warm_with_append": warm_avg_s * 1e6},
+        "roofline": decode_roofline(per_call, kern_s, call_s, mark_s, "decode_" + name,
+                                    {"avg_call_us_warm_with_append": warm_avg_s * 1e6}),
         "shape": {"batch": w.batch, "n_q": w.n_q, "n_kv": w.n_kv, "d": w.d,
                   "kv_dtype": w.kv_dtype, "mean_len": float(np.mean(lens0 + 1))},
     }
@@ -435,16 +470,23 @@ def bench_prefill(steps, warmup, torch, kv, with_cpu, small=False):
     wall = time.perf_counter() - t0
     flops = prefill_flops(w.batch, w.T, w.n_q, w.d)
     call_s = float(np.mean([a.elapsed_time(b) for a, b in events])) / 1e3
-    achieved = flops / call_s / 1e12
+    kern_s = dispatch_time(lambda: c.attn_prefill(0, q, k, v, seqs=seqs, out=out), steps, torch, c)
+    achieved = flops / kern_s / 1e12
     res = {
         "workload": "llama8b_prefill" if not small else "llama8b_prefill_small",
         "value": flops * steps / wall / 1e12, "unit": "TFLOP/s",
         "ms_per_step": wall / steps * 1e3,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
-                     "traffic": counter_traffic("prefill_llama8b_prefill"),
-                     "kernel": "kvc_attn_prefill (K/V append + causal attention)",
-                     "avg_call_us": call_s * 1e6, "flops_per_call": flops},
+                     "traffic": counter_traffic("prefill_llama8b_prefill", "k_prefill_mfma<"),
+                     "kernel": "k_prefill_mfma (the attention kernel; dispatch events on it)",
+                     "avg_kernel_us": kern_s * 1e6, "flops_per_call": flops,
+                     "call": {"what": "kvc_attn_prefill: attention kernel with the K/V cache "
+                                      "write beside it on the side stream (stream markers)",
+                              "avg_us_stream_markers": call_s * 1e6,
+                              "achieved": flops / call_s / 1e12,
+                              "frac": flops / call_s / 1e12 / BF16_PEAK_TFLOPS,
+                              "traffic": counter_traffic("prefill_llama8b_prefill")}},
         "shape": {"batch": w.batch, "T": w.T, "n_q": w.n_q, "n_kv": w.n_kv, "d": w.d},
     }
     if with_cpu:
@@ -532,16 +574,25 @@ def bench_extend(steps, warmup, torch, kv, with_cpu):
     wall = time.perf_counter() - t0
     flops = extend_flops(w.batch, ctx, EXTEND_CHUNK, w.n_q, w.d)
     call_s = float(np.mean([a.elapsed_time(b) for a, b in events])) / 1e3
-    achieved = flops / call_s / 1e12
+
+    def step_timed():
+        c.write(0, seqs, ctx, kc, vc)
+        c.attn_extend(0, seqs, q, out=out)
+    kern_s = dispatch_time(step_timed, steps, torch, c)
+    achieved = flops / kern_s / 1e12
     res = {
         "workload": "llama8b_extend",
         "value": flops * steps / wall / 1e12, "unit": "TFLOP/s",
         "ms_per_step": wall / steps * 1e3,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
-                     "traffic": counter_traffic("extend_llama8b_extend"),
-                     "kernel": "kvc_attn_extend (paged causal chunk attention)",
-                     "avg_call_us": call_s * 1e6, "flops_per_call": flops},
+                     "traffic": counter_traffic("extend_llama8b_extend", "k_prefill_mfma<"),
+                     "kernel": "k_prefill_mfma, paged (dispatch events on it)",
+                     "avg_kernel_us": kern_s * 1e6, "flops_per_call": flops,
+                     "call": {"what": "kvc_attn_extend (stream markers)",
+                              "avg_us_stream_markers": call_s * 1e6,
+                              "achieved": flops / call_s / 1e12,
+                              "frac": flops / call_s / 1e12 / BF16_PEAK_TFLOPS}},
         "shape": {"batch": w.batch, "context": ctx, "chunk": EXTEND_CHUNK, "n_q": w.n_q,
                   "n_kv": w.n_kv, "d": w.d},
     }
@@ -698,7 +749,7 @@ def main():
 
     log(f"{args.workload}: building the cache")
     dec = bench_decode(args.workload, args.steps, args.warmup, torch, kv, with_cpu)
-    log(f"{args.workload}: {dec['roofline']['avg_call_us']:.1f} us per call, "
+    log(f"{args.workload}: {dec['roofline']['avg_kernel_us']:.1f} us per work kernel, "
         f"frac {dec['roofline']['frac']:.3f}")
     dtype = {"bf16": "bf16", "fp16": "f16", "fp8": "fp8-e4m3 (bf16 q/o)",
              "int4": "int4 (bf16 q/o)"}[dec["shape"]["kv_dtype"]]
@@ -722,7 +773,7 @@ def main():
                           ("decode_long_mha", "long_mha_decode")):
             line[key] = bench_decode(name, k2, 2, torch, kv, with_cpu and "int4" not in name)
             line[key]["config"] = DECODE_WORKLOADS[name]
-            log(f"{key}: {line[key]['roofline']['avg_call_us']:.1f} us per call, "
+            log(f"{key}: {line[key]['roofline']['avg_kernel_us']:.1f} us per work kernel, "
                 f"frac {line[key]['roofline']['frac']:.3f}")
             if name == "llama70b_decode_int4":
                 drop_rows("llama70b_decode")

@@ -356,18 +356,33 @@ int kvc_attn_decode_noalloc(kvc_cache* cache, int32_t layer, int32_t n, const in
 int kvc_gather(const kvc_cache* cache, int32_t layer, int32_t seq, int32_t start, int32_t count,
                void* k_out_dev, void* v_out_dev, hipStream_t stream);
 
-/* Timing hook for measuring a decode call's kernels alone.  The next decode
- * call on this cache (kvc_attn_decode, _window, _append or _noalloc) records
- * start_event when the first kernel it launches begins and stop_event when
- * the last one ends: the events are attached to those kernels' own
- * dispatches (hipExtLaunchKernel), so the time between them covers the
- * call's kernels and the gaps between them, but no stream-marker overhead.
- * Both are hipEvent_t handles created by the caller with timing enabled on
- * the cache's device; either may be NULL; the caller keeps ownership.  The
- * events are used by that one call (whether it launches or fails) and then
- * forgotten; passing two NULLs clears them.  A call that launches nothing
- * (n = 0) records neither.  Returns KVC_E_INVAL for a NULL cache. */
-int kvc_set_dispatch_events(kvc_cache* cache, void* start_event, void* stop_event);
+/* Scopes of kvc_set_dispatch_events. */
+enum {
+  KVC_TIME_CALL = 0,          /* first kernel's start to last kernel's end */
+  KVC_TIME_MAIN_KERNEL = 1    /* the call's main kernel only */
+};
+
+/* Timing hook for measuring a call's kernels without stream-marker
+ * overhead.  The next attention call on this cache (kvc_attn_decode,
+ * _window, _append, _noalloc, kvc_attn_prefill, _window, kvc_attn_extend,
+ * _window) attaches start_event and stop_event to kernel dispatches of its
+ * own (hipExtLaunchKernel records them as those kernels begin and end):
+ *   KVC_TIME_CALL: start at the call's first kernel, stop at its last;
+ *   KVC_TIME_MAIN_KERNEL: both at the call's main kernel, the one that reads
+ *     the cache or the prompt (decode: the work-list kernel, or the split
+ *     kernel of an f32 cache, from its first to its last launch when a large
+ *     batch runs in sub-batches; the merge and the append kernel stay
+ *     outside).
+ * Prefill and extend time their attention kernel in both scopes (a prompt's
+ * cache write runs beside it on the handle's side stream, outside the
+ * events).  Both handles are hipEvent_t created by the caller with timing
+ * enabled on the cache's device; either may be NULL; the caller keeps
+ * ownership.  The events are used by that one call, whether it launches or
+ * fails, and then forgotten; two NULLs clear them.  A call that launches
+ * nothing (n = 0 or T = 0) records neither.  KVC_E_INVAL for a NULL cache or
+ * an unknown scope (which also clears them). */
+int kvc_set_dispatch_events(kvc_cache* cache, void* start_event, void* stop_event,
+                            int32_t scope);
 
 /* Message describing the last failure on the calling thread ("" if none). */
 const char* kvc_last_error(void);

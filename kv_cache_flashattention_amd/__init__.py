@@ -87,7 +87,7 @@ _SIGS = {
                                ctypes.c_uint64, _P],
     "kvc_attn_decode_noalloc": [_P, _I, _I, _P, _P, _P, ctypes.c_float, _I, _P],
     "kvc_gather": [_P, _I, _I, _I, _I, _P, _P, _P],
-    "kvc_set_dispatch_events": [_P, _P, _P],
+    "kvc_set_dispatch_events": [_P, _P, _P, _I],
     "kvc_last_error": [],
 }
 
@@ -363,19 +363,21 @@ class KvCache:
                                              ctypes.c_float(scale), num_splits, _stream()))
         return out
 
-    def set_dispatch_events(self, start=None, stop=None):
-        """Timing hook: the next decode call on this cache records `start` as
-        its first kernel begins and `stop` as its last kernel ends (events
-        attached to the kernels' dispatches).  Each is a torch.cuda.Event
-        made with enable_timing=True and recorded once already (torch creates
-        the underlying event at its first record), or None."""
+    def set_dispatch_events(self, start=None, stop=None, main_kernel=False):
+        """Timing hook: the next attention call on this cache records `start`
+        as its first kernel begins and `stop` as its last kernel ends, or,
+        with main_kernel, both on its main kernel (events attached to the
+        kernels' own dispatches).  Each is a torch.cuda.Event made with
+        enable_timing=True and recorded once already (torch creates the
+        underlying event at its first record), or None."""
         def handle(e):
             if e is None:
                 return None
             if not e.cuda_event:
                 raise ValueError("record the event once before using it as a dispatch event")
             return e.cuda_event
-        _check(lib().kvc_set_dispatch_events(self._h, handle(start), handle(stop)))
+        _check(lib().kvc_set_dispatch_events(self._h, handle(start), handle(stop),
+                                             1 if main_kernel else 0))
 
     def gather(self, layer, seq, start, count):
         st = STORAGE_TORCH[self.kv_dtype]

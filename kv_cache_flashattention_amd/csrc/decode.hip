@@ -220,11 +220,12 @@ hipError_t run_valu(const CacheView& cv, int layer, int n, const int32_t* seqs, 
                     void* out, float scale_log2, const DecodePlan& p, void* ws, hipStream_t st,
                     DispatchEvents ev) {
   hipError_t e = launch_ev(k_decode_valu<E, IO, D>, dim3(p.splits, cv.n_q, n), dim3(64), st,
-                           ev.start, p.splits == 1 ? ev.stop : nullptr, cv, layer, seqs,
-                           (const IO*)q, (IO*)out, ws, n, p.splits, p.split_len, scale_log2);
+                           ev.start, p.splits == 1 || ev.main_only ? ev.stop : nullptr, cv, layer,
+                           seqs, (const IO*)q, (IO*)out, ws, n, p.splits, p.split_len, scale_log2);
   if (e != hipSuccess || p.splits == 1) return e;
-  return launch_ev(k_decode_merge<IO, D>, dim3(cv.n_q, n), dim3(64), st, nullptr, ev.stop, cv,
-                   seqs, (IO*)out, (const void*)ws, n, p.splits, p.split_len);
+  return launch_ev(k_decode_merge<IO, D>, dim3(cv.n_q, n), dim3(64), st, nullptr,
+                   ev.main_only ? nullptr : ev.stop, cv, seqs, (IO*)out, (const void*)ws, n,
+                   p.splits, p.split_len);
 }
 
 template <int D>
@@ -254,9 +255,10 @@ hipError_t launch_decode(const CacheView& cv, int layer, int n, const int32_t* s
   // stored the row itself saved that launch but ran its unit loop slower:
   // 89.6 against 87.9 us per Llama-8B-shaped decode step.)
   if (knew != nullptr) {
-    hipError_t e = launch_append(cv, layer, n, seqs, knew, vnew, s, ev.start);
+    hipError_t e = launch_append(cv, layer, n, seqs, knew, vnew, s,
+                                 ev.main_only ? nullptr : ev.start);
     if (e != hipSuccess) return e;
-    ev.start = nullptr;                                 // the append kernel opened the call
+    if (!ev.main_only) ev.start = nullptr;              // the append kernel opened the call
   }
   bool handled = false;
   hipError_t e = launch_decode_mfma(cv, layer, n, seqs, q, out, sl2, plan, ws, window, sinks, s,

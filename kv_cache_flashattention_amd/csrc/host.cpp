@@ -545,6 +545,8 @@ int kvc_attn_prefill_window(kvc_cache* c, int32_t layer, int32_t n, const int32_
                             int32_t T, const void* q, const void* k, const void* v, void* out,
                             float scale, int32_t window, int32_t sinks, hipStream_t stream) {
   if (!c) return fail(KVC_E_INVAL, "cache is NULL");
+  const DispatchEvents ev = c->timing;                 // this call's, whatever its outcome
+  c->timing = DispatchEvents{};
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(KVC_E_INVAL, "scale must be finite and positive");
   int rw = check_window(c, window, sinks);
@@ -573,7 +575,8 @@ int kvc_attn_prefill_window(kvc_cache* c, int32_t layer, int32_t n, const int32_
       e = launch_write(c->view(), layer, n, seqs, 0, T, k, v, c->side);
     }
   }
-  if (e == hipSuccess) e = launch_prefill(c->view(), n, T, q, k, v, out, scale, window, sinks, stream);
+  if (e == hipSuccess)
+    e = launch_prefill(c->view(), n, T, q, k, v, out, scale, window, sinks, stream, ev);
   if (forked) {
     // Whatever failed above, the caller's stream waits for everything enqueued
     // on the side stream, which may still read k and v.
@@ -594,6 +597,8 @@ int kvc_attn_extend_window(kvc_cache* c, int32_t layer, int32_t n, const int32_t
                            int32_t T, const void* q, void* out, float scale, int32_t window,
                            int32_t sinks, hipStream_t stream) {
   if (!c) return fail(KVC_E_INVAL, "cache is NULL");
+  const DispatchEvents ev = c->timing;                 // this call's, whatever its outcome
+  c->timing = DispatchEvents{};
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(KVC_E_INVAL, "scale must be finite and positive");
   if (window < 0 || sinks < 0) return fail(KVC_E_INVAL, "window and sinks must be >= 0");
@@ -610,7 +615,7 @@ int kvc_attn_extend_window(kvc_cache* c, int32_t layer, int32_t n, const int32_t
   if (!aligned16(q) || !aligned16(out)) return fail(KVC_E_INVAL, "q/out must be 16-byte aligned");
   bool handled = false;
   hipError_t e = launch_extend(c->view(), layer, n, seqs, T, q, out, scale, window, sinks, stream,
-                               &handled);
+                               &handled, ev);
   if (e == hipSuccess && !handled) return fail(KVC_E_UNSUPPORTED, "no extend kernel for this shape");
   return e == hipSuccess ? KVC_OK : hip_fail(e, "extend launch");
 }
@@ -706,10 +711,15 @@ int kvc_attn_decode_noalloc(kvc_cache* c, int32_t layer, int32_t n, const int32_
                      c->scratch, kScratchBytes, stream);
 }
 
-int kvc_set_dispatch_events(kvc_cache* c, void* start_event, void* stop_event) {
+int kvc_set_dispatch_events(kvc_cache* c, void* start_event, void* stop_event, int32_t scope) {
   if (!c) return fail(KVC_E_INVAL, "cache is NULL");
+  if (scope != KVC_TIME_CALL && scope != KVC_TIME_MAIN_KERNEL) {
+    c->timing = DispatchEvents{};
+    return fail(KVC_E_INVAL, "scope must be KVC_TIME_CALL or KVC_TIME_MAIN_KERNEL");
+  }
   c->timing.start = (hipEvent_t)start_event;
   c->timing.stop = (hipEvent_t)stop_event;
+  c->timing.main_only = scope == KVC_TIME_MAIN_KERNEL;
   return KVC_OK;
 }
 

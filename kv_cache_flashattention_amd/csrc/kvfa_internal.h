@@ -88,9 +88,12 @@ uint64_t work_list_ws_bytes(const CacheView& cv, int32_t nb, int32_t waves);
 int work_list_waves_per_cu(const CacheView& cv);
 
 // Dispatch events of one call (kvc_set_dispatch_events): `start` is recorded
-// as the call's first kernel begins, `stop` as its last kernel ends.
+// as the call's first kernel begins and `stop` as its last kernel ends, or,
+// with main_only, both on the call's main kernel (decode: the work-list or
+// VALU kernel; prefill and extend: the attention kernel in either case).
 struct DispatchEvents {
   hipEvent_t start = nullptr, stop = nullptr;
+  bool main_only = false;
 };
 
 // Launch of kernel k, optionally with dispatch events (hipExtLaunchKernel
@@ -132,11 +135,11 @@ hipError_t launch_decode(const CacheView& cv, int layer, int n, const int32_t* s
 // j < sinks; window = 0: full causal attention.
 hipError_t launch_prefill(const CacheView& cv, int n, int T, const void* q, const void* k,
                           const void* v, void* out, float scale, int window, int sinks,
-                          hipStream_t s);
+                          hipStream_t s, DispatchEvents ev = {});
 // T query rows per sequence against the paged cache (bf16 / f16 caches);
 // *handled = false when the cache type has no such kernel.
 hipError_t launch_extend(const CacheView& cv, int layer, int n, const int32_t* seqs, int T,
                          const void* q, void* out, float scale, int window, int sinks,
-                         hipStream_t s, bool* handled);
+                         hipStream_t s, bool* handled, DispatchEvents ev = {});
 
 }  // namespace kvfa

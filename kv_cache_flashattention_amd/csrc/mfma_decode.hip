@@ -819,12 +819,14 @@ hipError_t run(const CacheView& cv, int layer, int n, const int32_t* seqs, const
     const int nb = n - b0 < kMaxBatch ? n - b0 : kMaxBatch;
     const uint16_t* qb = (const uint16_t*)q + (int64_t)b0 * cv.n_q * D;
     uint16_t* ob = (uint16_t*)out + (int64_t)b0 * cv.n_q * D;
+    const bool last = b0 + nb == n;
     hipError_t e = launch_ev(k_decode_work<KV, D>, dim3(grid), dim3(256), st,
-                             b0 == 0 ? ev.start : nullptr, nullptr, cv, layer, seqs + b0, qb, ws,
-                             nb, qgroups, p.waves, sl2, window, sinks);
+                             b0 == 0 ? ev.start : nullptr, last && ev.main_only ? ev.stop : nullptr,
+                             cv, layer, seqs + b0, qb, ws, nb, qgroups, p.waves, sl2, window,
+                             sinks);
     if (e != hipSuccess) return e;
     e = launch_ev(k_decode_work_merge<KV == KV_F16, D>, dim3(cv.n_q, nb), dim3(256), st, nullptr,
-                  b0 + nb == n ? ev.stop : nullptr, cv, (const void*)ws, ob, nb, qgroups,
+                  last && !ev.main_only ? ev.stop : nullptr, cv, (const void*)ws, ob, nb, qgroups,
                   p.waves);
     if (e != hipSuccess) return e;
   }

@@ -690,42 +690,40 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
 template <int D, bool F16, bool PAGED, int SC = 0>
 hipError_t run(const CacheView& cv, int layer, int n, const int32_t* seqs, int T, const void* q,
                const void* k, const void* v, void* out, float sl2, int window, int sinks,
-               hipStream_t s) {
+               hipStream_t s, DispatchEvents ev) {
   const int ntiles = (T + BM - 1) / BM;
   const int64_t units = (int64_t)cv.n_q * n * ntiles;
   if (units > INT32_MAX) return hipErrorInvalidValue;
   const int xcd_split = units % 8 == 0 ? 1 : 0;
+  const dim3 grid((uint32_t)units), block(512);
   if (window > 0)
-    hipLaunchKernelGGL((k_prefill_mfma<D, F16, PAGED, true, SC>), dim3((uint32_t)units), dim3(512), 0,
-                       s, cv.n_q, cv.n_kv, T, (const uint16_t*)q, (const uint16_t*)k,
-                       (const uint16_t*)v, (uint16_t*)out, sl2, ntiles, n, (int)units, xcd_split,
-                       cv, layer, seqs, window, sinks);
-  else
-    hipLaunchKernelGGL((k_prefill_mfma<D, F16, PAGED, false, SC>), dim3((uint32_t)units), dim3(512),
-                       0, s, cv.n_q, cv.n_kv, T, (const uint16_t*)q, (const uint16_t*)k,
-                       (const uint16_t*)v, (uint16_t*)out, sl2, ntiles, n, (int)units, xcd_split,
-                       cv, layer, seqs, 0, 0);
-  return hipGetLastError();
+    return launch_ev(k_prefill_mfma<D, F16, PAGED, true, SC>, grid, block, s, ev.start, ev.stop,
+                     cv.n_q, cv.n_kv, T, (const uint16_t*)q, (const uint16_t*)k,
+                     (const uint16_t*)v, (uint16_t*)out, sl2, ntiles, n, (int)units, xcd_split,
+                     cv, layer, seqs, window, sinks);
+  return launch_ev(k_prefill_mfma<D, F16, PAGED, false, SC>, grid, block, s, ev.start, ev.stop,
+                   cv.n_q, cv.n_kv, T, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                   (uint16_t*)out, sl2, ntiles, n, (int)units, xcd_split, cv, layer, seqs, 0, 0);
 }
 
 template <bool PAGED>
 hipError_t dispatch(const CacheView& cv, int layer, int n, const int32_t* seqs, int T,
                     const void* q, const void* k, const void* v, void* out, float sl2,
-                    int window, int sinks, hipStream_t s, bool* handled) {
+                    int window, int sinks, hipStream_t s, DispatchEvents ev, bool* handled) {
   *handled = true;
   const int io = io_dtype(cv.dtype);
   if (io == KVC_BF16 && (!PAGED || cv.dtype == KVC_BF16)) {
-    if (cv.d == 128) return run<128, false, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);
-    if (cv.d == 64) return run<64, false, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);
+    if (cv.d == 128) return run<128, false, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s, ev);
+    if (cv.d == 64) return run<64, false, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s, ev);
   } else if (PAGED && cv.dtype == KVC_FP8_E4M3FN) {
-    if (cv.d == 128) return run<128, false, true, KVC_FP8_E4M3FN>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);
-    if (cv.d == 64) return run<64, false, true, KVC_FP8_E4M3FN>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);
+    if (cv.d == 128) return run<128, false, true, KVC_FP8_E4M3FN>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s, ev);
+    if (cv.d == 64) return run<64, false, true, KVC_FP8_E4M3FN>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s, ev);
   } else if (PAGED && cv.dtype == KVC_INT4) {
-    if (cv.d == 128) return run<128, false, true, KVC_INT4>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);
-    if (cv.d == 64) return run<64, false, true, KVC_INT4>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);
+    if (cv.d == 128) return run<128, false, true, KVC_INT4>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s, ev);
+    if (cv.d == 64) return run<64, false, true, KVC_INT4>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s, ev);
   } else if (io == KVC_F16) {
-    if (cv.d == 128) return run<128, true, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);
-    if (cv.d == 64) return run<64, true, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s);
+    if (cv.d == 128) return run<128, true, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s, ev);
+    if (cv.d == 64) return run<64, true, PAGED>(cv, layer, n, seqs, T, q, k, v, out, sl2, window, sinks, s, ev);
   }
   *handled = false;
   return hipSuccess;
@@ -735,15 +733,15 @@ hipError_t dispatch(const CacheView& cv, int layer, int n, const int32_t* seqs, 
 
 hipError_t launch_prefill_mfma(const CacheView& cv, int n, int T, const void* q, const void* k,
                                const void* v, void* out, float sl2, int window, int sinks,
-                               hipStream_t s, bool* handled) {
-  return dispatch<false>(cv, 0, n, nullptr, T, q, k, v, out, sl2, window, sinks, s, handled);
+                               hipStream_t s, DispatchEvents ev, bool* handled) {
+  return dispatch<false>(cv, 0, n, nullptr, T, q, k, v, out, sl2, window, sinks, s, ev, handled);
 }
 
 hipError_t launch_extend_mfma(const CacheView& cv, int layer, int n, const int32_t* seqs, int T,
                               const void* q, void* out, float sl2, int window, int sinks,
-                              hipStream_t s, bool* handled) {
+                              hipStream_t s, DispatchEvents ev, bool* handled) {
   return dispatch<true>(cv, layer, n, seqs, T, q, nullptr, nullptr, out, sl2, window, sinks, s,
-                        handled);
+                        ev, handled);
 }
 
 }  // namespace kvfa

@@ -15,10 +15,10 @@ namespace kvfa {
 
 hipError_t launch_prefill_mfma(const CacheView& cv, int n, int T, const void* q, const void* k,
                                const void* v, void* out, float scale_log2, int window, int sinks,
-                               hipStream_t s, bool* handled);
+                               hipStream_t s, DispatchEvents ev, bool* handled);
 hipError_t launch_extend_mfma(const CacheView& cv, int layer, int n, const int32_t* seqs, int T,
                               const void* q, void* out, float scale_log2, int window, int sinks,
-                              hipStream_t s, bool* handled);
+                              hipStream_t s, DispatchEvents ev, bool* handled);
 
 namespace {
 
@@ -98,38 +98,36 @@ __global__ __launch_bounds__(64) void k_prefill_valu(int n_q, int n_kv, int T, c
 
 template <typename IO>
 hipError_t run_valu(const CacheView& cv, int n, int T, const void* q, const void* k,
-                    const void* v, void* out, float sl2, hipStream_t s) {
+                    const void* v, void* out, float sl2, hipStream_t s, DispatchEvents ev) {
   dim3 grid((T + 63) / 64, cv.n_q, n);
   if (cv.d == 128)
-    hipLaunchKernelGGL((k_prefill_valu<IO, 128>), grid, dim3(64), 0, s, cv.n_q, cv.n_kv, T,
-                       (const IO*)q, (const IO*)k, (const IO*)v, (IO*)out, sl2);
-  else
-    hipLaunchKernelGGL((k_prefill_valu<IO, 64>), grid, dim3(64), 0, s, cv.n_q, cv.n_kv, T,
-                       (const IO*)q, (const IO*)k, (const IO*)v, (IO*)out, sl2);
-  return hipGetLastError();
+    return launch_ev(k_prefill_valu<IO, 128>, grid, dim3(64), s, ev.start, ev.stop, cv.n_q,
+                     cv.n_kv, T, (const IO*)q, (const IO*)k, (const IO*)v, (IO*)out, sl2);
+  return launch_ev(k_prefill_valu<IO, 64>, grid, dim3(64), s, ev.start, ev.stop, cv.n_q, cv.n_kv,
+                   T, (const IO*)q, (const IO*)k, (const IO*)v, (IO*)out, sl2);
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const CacheView& cv, int n, int T, const void* q, const void* k,
                           const void* v, void* out, float scale, int window, int sinks,
-                          hipStream_t s) {
+                          hipStream_t s, DispatchEvents ev) {
   const float sl2 = scale * kLog2e;
   bool handled = false;
-  hipError_t e = launch_prefill_mfma(cv, n, T, q, k, v, out, sl2, window, sinks, s, &handled);
+  hipError_t e = launch_prefill_mfma(cv, n, T, q, k, v, out, sl2, window, sinks, s, ev, &handled);
   if (handled) return e;
   if (window > 0) return hipErrorInvalidValue;          // the VALU kernel has no window
   switch (io_dtype(cv.dtype)) {
-    case KVC_F32: return run_valu<float>(cv, n, T, q, k, v, out, sl2, s);
-    case KVC_F16: return run_valu<_Float16>(cv, n, T, q, k, v, out, sl2, s);
-    default: return run_valu<BF16>(cv, n, T, q, k, v, out, sl2, s);
+    case KVC_F32: return run_valu<float>(cv, n, T, q, k, v, out, sl2, s, ev);
+    case KVC_F16: return run_valu<_Float16>(cv, n, T, q, k, v, out, sl2, s, ev);
+    default: return run_valu<BF16>(cv, n, T, q, k, v, out, sl2, s, ev);
   }
 }
 
 hipError_t launch_extend(const CacheView& cv, int layer, int n, const int32_t* seqs, int T,
                          const void* q, void* out, float scale, int window, int sinks,
-                         hipStream_t s, bool* handled) {
-  return launch_extend_mfma(cv, layer, n, seqs, T, q, out, scale * kLog2e, window, sinks, s,
+                         hipStream_t s, bool* handled, DispatchEvents ev) {
+  return launch_extend_mfma(cv, layer, n, seqs, T, q, out, scale * kLog2e, window, sinks, s, ev,
                             handled);
 }
 
