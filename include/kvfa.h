@@ -362,8 +362,10 @@ enum {
   KVC_TIME_MAIN_KERNEL = 1    /* the call's main kernel only */
 };
 
-/* Timing hook for measuring a call's kernels without stream-marker
- * overhead.  The next attention call on this cache (kvc_attn_decode,
+/* Timing hook, for callers that measure the kernels against their roofline
+ * (a profiler-free benchmark, a serving loop's own telemetry); no page
+ * defines it.  It times a call's kernels without stream-marker overhead.
+ * The next attention call on this cache (kvc_attn_decode,
  * _window, _append, _noalloc, kvc_attn_prefill, _window, kvc_attn_extend,
  * _window) attaches start_event and stop_event to kernel dispatches of its
  * own (hipExtLaunchKernel records them as those kernels begin and end):
