@@ -413,29 +413,12 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
     const int seq = uni(s_seq[b]);
     const int L = uni(s_len[b]);                       // > 0: the entry has units
     const UnitMap umap(L, window, sinks);
-    // Query operand (B of S^T = K Q^T): column r16 = query row qg*16 + r16.
+    // Query operand (B of S^T = K Q^T): column r16 = query row qg*16 + r16,
+    // loaded after the piece's first block-table load (below).
     const int qi = qg * 16 + r16;
     const bool qrow = qi < G;
     OpT qop[KS];
-    {
-      const uint16_t* qr = q + ((int64_t)b * cv.n_q + kvh * G + (qrow ? qi : 0)) * D;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        uint4 raw = qrow ? *(const uint4*)(qr + dmap<KV, D>(ks, g)) : make_uint4(0, 0, 0, 0);
-        if (KV == KV_INT4) raw = interleave_halves(raw);
-        qop[ks] = __builtin_bit_cast(OpT, raw);
-      }
-    }
-    // int4: -136 * sum of the query row's values (the K operands' offset)
-    float qoff = 0.f;
-    if (KV == KV_INT4) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qoff += sum8_bf16(__builtin_bit_cast(bf16x8, qop[ks]));
-      qoff += __shfl_xor(qoff, 16, 64);
-      qoff += __shfl_xor(qoff, 32, 64);
-      qoff *= -kInt4Offset;
-    }
-
+    float qoff = 0.f;                                 // int4: -136 * sum of the query row
     f32x4 o[DT];
 #pragma unroll
     for (int i = 0; i < DT; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -472,6 +455,24 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
       }
     };
     load_tab(c0);
+    {
+      const uint16_t* qr = q + ((int64_t)b * cv.n_q + kvh * G + (qrow ? qi : 0)) * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 raw = qrow ? *(const uint4*)(qr + dmap<KV, D>(ks, g)) : make_uint4(0, 0, 0, 0);
+        if (KV == KV_INT4) raw = interleave_halves(raw);
+        qop[ks] = __builtin_bit_cast(OpT, raw);
+      }
+    }
+    // int4: -136 * sum of the query row's values (the K operands' offset)
+    if (KV == KV_INT4) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qoff += sum8_bf16(__builtin_bit_cast(bf16x8, qop[ks]));
+      qoff += __shfl_xor(qoff, 16, 64);
+      qoff += __shfl_xor(qoff, 32, 64);
+      qoff *= -kInt4Offset;
+    }
+
 
     // Issue every load of unit cs into buffer B.
     auto issue = [&](U& B, int cs) {
