@@ -186,6 +186,7 @@ template <int KV, int D> struct Unit {
   uint4 k[2][KL];
   uint4 v[VL];
   float ksc, vsc;                                      // fp8/int4: this lane's block scales
+  int sj;                                              // the lane's slot in its table chunk
 };
 
 // Units a wave keeps loaded (ring depth).  Deeper rings cost registers and
@@ -272,6 +273,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
   typedef Unit<KV, D> U;
   constexpr int KS = U::KS, DT = U::DT, KL = U::KL;
   constexpr int NB = DecodeDepth<KV>::value;
+  static_assert(NB == 2, "the block-scale shuffles assume one unit in flight");
   constexpr int EB = KV == KV_FP8 ? 1 : 2;            // bytes per element (not int4)
   constexpr int64_t SB = KV == KV_INT4 ? kBlock * D / 2 : kBlock * D * EB;   // slab bytes
   __shared__ int64_t s_units[kMaxBatch + 1];
@@ -464,14 +466,6 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
         qop[ks] = __builtin_bit_cast(OpT, raw);
       }
     }
-    // int4: -136 * sum of the query row's values (the K operands' offset)
-    if (KV == KV_INT4) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qoff += sum8_bf16(__builtin_bit_cast(bf16x8, qop[ks]));
-      qoff += __shfl_xor(qoff, 16, 64);
-      qoff += __shfl_xor(qoff, 32, 64);
-      qoff *= -kInt4Offset;
-    }
 
 
     // Issue every load of unit cs into buffer B.
@@ -529,11 +523,16 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
             B.v[dt] = ld_stream4(vslab + 2 * (16 * dt + r16) * kBlock);
         }
       }
-      // The block scales come from loads that wait for the block ids, so they
-      // are read after the K/V loads have gone out.
-      if constexpr (SCALED) {                         // this lane's block: table lane j + g/2
-        B.ksc = __shfl(tks, j + (g >> 1), 64);
-        B.vsc = __shfl(tvs, j + (g >> 1), 64);
+      B.sj = j + (g >> 1);                            // this lane's block: table lane
+    };
+    // The unit's block scales, read from the table chunk it was issued from:
+    // called before the next issue, which may load the next chunk.  Their
+    // loads are then older than the unit's own K/V loads, so the shuffles do
+    // not wait on the loads in flight.
+    auto scales = [&](U& B) {
+      if constexpr (SCALED) {
+        B.ksc = __shfl(tks, B.sj, 64);
+        B.vsc = __shfl(tvs, B.sj, 64);
       }
     };
 
@@ -676,15 +675,44 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
     // NB register buffers in a ring: the loads of unit c+NB-1 go out before
     // unit c is computed, so NB-1 units are in flight while the wave computes.
     U buf[NB];
+    issue(buf[0], c0);
+    // The query rows were loaded before the first unit's loads: wait for them
+    // here, once, so that the unit loop below never waits on them (and with
+    // them on every load issued since).
 #pragma unroll
-    for (int j = 0; j < NB - 1; ++j)
-      if (c0 + j < c1) issue(buf[j], c0 + j);
-    for (int c = c0; c < c1; c += NB) {
+    for (int ks = 0; ks < KS; ++ks) {
+      ntu4 x = __builtin_bit_cast(ntu4, qop[ks]);
+      asm volatile("" : "+v"(x));
+      qop[ks] = __builtin_bit_cast(OpT, x);
+    }
+    // int4: -136 * sum of the query row's values (the K operands' offset)
+    if (KV == KV_INT4) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        if (c + j + NB - 1 < c1) issue(buf[(j + NB - 1) % NB], c + j + NB - 1);
-        if (c + j < c1) compute(buf[j], c + j);
-      }
+      for (int ks = 0; ks < KS; ++ks) qoff += sum8_bf16(__builtin_bit_cast(bf16x8, qop[ks]));
+      qoff += __shfl_xor(qoff, 16, 64);
+      qoff += __shfl_xor(qoff, 32, 64);
+      qoff *= -kInt4Offset;
+    }
+    // Two units per step with no conditions in the steady state, so that the
+    // compiler's wait counts see one fixed order of loads: unit c+1's loads
+    // go out while unit c is computed.  A piece holds at least one unit.
+    int c = c0;
+    for (; c + 2 < c1; c += 2) {
+      scales(buf[0]);
+      issue(buf[1], c + 1);
+      compute(buf[0], c);
+      scales(buf[1]);
+      issue(buf[0], c + 2);
+      compute(buf[1], c + 1);
+    }
+    scales(buf[0]);
+    if (c + 1 < c1) {
+      issue(buf[1], c + 1);
+      compute(buf[0], c);
+      scales(buf[1]);
+      compute(buf[1], c + 1);
+    } else {
+      compute(buf[0], c);
     }
 
     // ---- piece done: (m, l, O) of this wave's query rows to slot (segment + wave)
@@ -851,11 +879,11 @@ int occupancy_waves() {
 }  // namespace
 
 // Waves per CU the work list is cut for, by storage type (at most the
-// kernel's occupancy).  A 16-bit unit carries 16 KiB of K/V, so one wave per
-// SIMD keeps enough bytes in flight, and fewer waves mean fewer pieces to
-// start and merge (Llama-8B-shaped decode 90.5 -> 84.9 us against eight
-// waves); fp8 and int4 units are 8 and 4 KiB and need more waves.
-constexpr int kWaves16 = 4, kWavesFp8 = 8, kWavesInt4 = 8;
+// kernel's occupancy).  With two units in flight per wave, one wave per SIMD
+// keeps enough bytes in flight for 16 KiB (16-bit) and 8 KiB (fp8) units, and
+// fewer waves mean fewer pieces to start and merge; int4's 4 KiB units run at
+// the same speed with four or eight waves.
+constexpr int kWaves16 = 4, kWavesFp8 = 4, kWavesInt4 = 8;
 
 uint64_t work_list_ws_bytes(const CacheView& cv, int32_t nb, int32_t waves) {
   const int nkvg = cv.n_kv * ((cv.n_q / cv.n_kv + 15) / 16);
