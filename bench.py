@@ -6,9 +6,10 @@ Default workload (the headline): the Llama-3-8B-shaped decode step -- 40
 sequences, 32 query and 8 kv heads of 128, bf16 cache in 16-token blocks
 behind shuffled block tables, context lengths uniform in [512, 4096].  One
 step is one pass of the decode hot path over that batch: grow every sequence
-by one token (host allocator + table update), then kvc_attn_decode_append:
-kv_append of the new K/V rows and attn_decode (work-list partials and their
-(m, l) merge) in one call.  The headline `value` is the decode's algorithmic HBM bytes per step
+by one token and append its new K/V rows (kvc_seq_grow_append: the host
+allocator places each row, one launch writes the rows and the table and
+length updates), then kvc_attn_decode (work-list partials and their (m, l)
+merge).  The headline `value` is the decode's algorithmic HBM bytes per step
 (K/V rows read through the tables, queries, outputs, table entries) divided
 by the wall-clock time per step.
 
@@ -307,10 +308,10 @@ def bench_decode_window(steps, torch, kv, window=1024, sinks=4):
 
 def bench_decode(name, steps, warmup, torch, kv, with_cpu):
     """One workload of the decode path.  A step grows every sequence by one
-    token (host allocator + table update) and runs kvc_attn_decode_append
-    (kv_append of the new rows, then the decode); `value` is the decode's
-    algorithmic bytes per step over the wall-clock time of the K steps.  The
-    roofline times kvc_attn_decode alone after an Infinity-Cache eviction."""
+    token and appends its new rows (kvc_seq_grow_append), then runs
+    kvc_attn_decode; `value` is the decode's algorithmic bytes per step over
+    the wall-clock time of the K steps.  The roofline times kvc_attn_decode
+    alone after an Infinity-Cache eviction."""
     w, c, io = build_decode(name, torch, kv)
     kv_elem = KV_ELEM_BYTES[w.kv_dtype]
     seqs_host = list(range(w.batch))
@@ -327,10 +328,10 @@ def bench_decode(name, steps, warmup, torch, kv, with_cpu):
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
-        c.seq_grow(seqs_host)
         if ev is not None:
             ev[0].record(stream)
-        c.attn_decode_append(0, seqs, knew, vnew, q, out=out, ws=ws)
+        c.seq_grow_append(0, seqs_host, knew, vnew)
+        c.attn_decode(0, seqs, q, out=out, ws=ws)
         if ev is not None:
             ev[1].record(stream)
 
@@ -365,7 +366,7 @@ def bench_decode(name, steps, warmup, torch, kv, with_cpu):
         "unit": "GB/s",
         "ms_per_step": wall / steps * 1e3,
         "roofline": decode_roofline(per_call, kern_s, call_s, mark_s, "decode_" + name,
-                                    {"avg_call_us_warm_with_append": warm_avg_s * 1e6}),
+                                    {"avg_step_us_warm": warm_avg_s * 1e6}),
         "shape": {"batch": w.batch, "n_q": w.n_q, "n_kv": w.n_kv, "d": w.d,
                   "kv_dtype": w.kv_dtype, "mean_len": float(np.mean(lens0 + 1))},
     }

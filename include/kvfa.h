@@ -213,6 +213,22 @@ int kvc_free_blocks(const kvc_cache* cache, int32_t* out);
 int kvc_append(kvc_cache* cache, int32_t layer, int32_t n, const int32_t* seqs_dev,
                const void* k_dev, const void* v_dev, hipStream_t stream);
 
+/* kvc_seq_grow followed by kvc_append of the grown rows of one layer, in one
+ * launch (the same two steps of a decoded token: the block manager places
+ * the new position, kvcache-7e2 PagedAttention section, `append_token`; its
+ * K and V rows are stored there, KV cache section).  The host's block
+ * manager already knows where each new row goes, so the launch carries each
+ * entry's block and slot along with the grow's table and length writes, and
+ * the kernel reads no table or length.  seqs_host: n distinct live sequence
+ * ids; k_dev, v_dev: [n][n_kv_heads][d_head] in the io type, row i for
+ * seqs_host[i].  The resulting pools, tables and lengths equal those of
+ * kvc_seq_grow then kvc_append.  Checks as kvc_seq_grow (all-or-nothing:
+ * nothing changes on an error it reports), plus the layer range and
+ * non-NULL k_dev, v_dev.  Copy-on-write block copies run first, as in
+ * kvc_seq_grow.  Batches above 96 entries take one launch per 96. */
+int kvc_seq_grow_append(kvc_cache* cache, int32_t layer, int32_t n, const int32_t* seqs_host,
+                        const void* k_dev, const void* v_dev, hipStream_t stream);
+
 /* Bulk store of T consecutive rows per sequence (prefill, population):
  * positions start .. start+T-1 of each of n sequences, which must all lie
  * below the sequence's length.  k_dev, v_dev: [n][T][n_kv_heads][d_head] in

@@ -74,6 +74,7 @@ _SIGS = {
     "kvc_seq_blocks": [_P, _I, ctypes.POINTER(_I), _I, ctypes.POINTER(_I)],
     "kvc_free_blocks": [_P, ctypes.POINTER(_I)],
     "kvc_append": [_P, _I, _I, _P, _P, _P, _P],
+    "kvc_seq_grow_append": [_P, _I, _I, ctypes.POINTER(_I), _P, _P, _P],
     "kvc_write": [_P, _I, _I, _P, _I, _I, _P, _P, _P],
     "kvc_attn_prefill": [_P, _I, _I, _P, _I, _P, _P, _P, _P, ctypes.c_float, _P],
     "kvc_attn_extend": [_P, _I, _I, _P, _I, _P, _P, ctypes.c_float, _P],
@@ -262,6 +263,15 @@ class KvCache:
         shape = (n, self.n_kv, self.d)
         _check(lib().kvc_append(self._h, layer, n, self._seqs(seqs), self._io(k, shape, "k"),
                                 self._io(v, shape, "v"), _stream()))
+
+    def seq_grow_append(self, layer, seqs, k, v):
+        """seq_grow of the host ids `seqs`, then append of their new rows
+        k, v [n, n_kv, d] to `layer`, in one launch."""
+        n = len(seqs)
+        arr = (_I * n)(*[int(s) for s in seqs])
+        shape = (n, self.n_kv, self.d)
+        _check(lib().kvc_seq_grow_append(self._h, layer, n, arr, self._io(k, shape, "k"),
+                                         self._io(v, shape, "v"), _stream()))
 
     def write(self, layer, seqs, start, k, v):
         n, T = seqs.numel(), k.shape[1]

@@ -59,16 +59,20 @@ __global__ void k_fill_tables(CacheView cv) {
     cv.len[i] = 0;
 }
 
-__global__ void k_table_update(CacheView cv, TableUpdate u) {
-  int i = threadIdx.x;
-  if (i >= u.n) return;
-  int32_t idx = u.idx[i];
+// One table or length write: idx >= 0 is block_table[idx], idx < 0 is
+// seq_len[-idx - 1]; indices outside the tables are dropped.
+__device__ __forceinline__ void table_write(const CacheView& cv, int32_t idx, int32_t val) {
   if (idx >= 0) {
-    if ((int64_t)idx < (int64_t)cv.max_seqs * cv.max_bps) cv.bt[idx] = u.val[i];
+    if ((int64_t)idx < (int64_t)cv.max_seqs * cv.max_bps) cv.bt[idx] = val;
   } else {
-    int32_t s = -idx - 1;
-    if (s < cv.max_seqs) cv.len[s] = u.val[i];
+    const int32_t s = -idx - 1;
+    if (s < cv.max_seqs) cv.len[s] = val;
   }
+}
+
+__global__ void k_table_update(CacheView cv, TableUpdate u) {
+  const int i = threadIdx.x;
+  if (i < u.n) table_write(cv, u.idx[i], u.val[i]);
 }
 
 // ---------------------------------------------------------------- block copy
@@ -123,16 +127,9 @@ __global__ __launch_bounds__(256) void k_copy_blocks(CacheView cv, BlockCopy u) 
 // One wave per (sequence, kv head): the new row goes to slot (L-1) % 16 of
 // block table[(L-1) / 16].  16/32-bit storage copies the bits.
 template <typename E>
-__global__ __launch_bounds__(64) void k_append_copy(CacheView cv, int layer, const int32_t* seqs,
-                                                    const E* knew, const E* vnew) {
-  const int b = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
-  const int seq = seqs[b];
-  const int L = seq_length(cv, seq);
-  if (L < 0) return;
-  const int pos = L - 1, slot = pos % kBlock;
-  const int blk = block_of(cv, seq, pos);
-  if (blk < 0) return;
-  const int d = cv.d;
+__device__ void append_row_copy(const CacheView& cv, int layer, int b, int h, int blk, int slot,
+                                const E* knew, const E* vnew) {
+  const int d = cv.d, lane = threadIdx.x;
   const int64_t base = slab_elems(cv, layer, blk, h);
   E* K = (E*)cv.k + base;
   E* V = (E*)cv.v + base;
@@ -142,6 +139,19 @@ __global__ __launch_bounds__(64) void k_append_copy(CacheView cv, int layer, con
     K[slot * d + j] = kr[j];
     V[j * kBlock + slot] = vr[j];
   }
+}
+
+template <typename E>
+__global__ __launch_bounds__(64) void k_append_copy(CacheView cv, int layer, const int32_t* seqs,
+                                                    const E* knew, const E* vnew) {
+  const int b = blockIdx.x, h = blockIdx.y;
+  const int seq = seqs[b];
+  const int L = seq_length(cv, seq);
+  if (L < 0) return;
+  const int pos = L - 1;
+  const int blk = block_of(cv, seq, pos);
+  if (blk < 0) return;
+  append_row_copy(cv, layer, b, h, blk, pos % kBlock, knew, vnew);
 }
 
 // fp8 append of one slab column set.  Every lane owns the head-dimension
@@ -180,21 +190,26 @@ __device__ void fp8_append_slab(uint8_t* slab, float* scale, int slot, int d, in
   if (lane == 0) *scale = s;
 }
 
-__global__ __launch_bounds__(64) void k_append_fp8(CacheView cv, int layer, const int32_t* seqs,
-                                                   const uint16_t* knew, const uint16_t* vnew) {
-  const int b = blockIdx.x, h = blockIdx.y;
-  const int seq = seqs[b];
-  const int L = seq_length(cv, seq);
-  if (L < 0) return;
-  const int pos = L - 1, slot = pos % kBlock;
-  const int blk = block_of(cv, seq, pos);
-  if (blk < 0) return;
+__device__ void append_row_fp8(const CacheView& cv, int layer, int b, int h, int blk, int slot,
+                               const uint16_t* knew, const uint16_t* vnew) {
   const int d = cv.d;
   const int64_t base = slab_elems(cv, layer, blk, h);
   const int64_t si = scale_idx(cv, layer, blk, h);
   const int64_t row = ((int64_t)b * cv.n_kv + h) * d;
   fp8_append_slab((uint8_t*)cv.k + base, cv.ks + si, slot, d, d, 1, knew + row);
   fp8_append_slab((uint8_t*)cv.v + base, cv.vs + si, slot, d, 1, kBlock, vnew + row);
+}
+
+__global__ __launch_bounds__(64) void k_append_fp8(CacheView cv, int layer, const int32_t* seqs,
+                                                   const uint16_t* knew, const uint16_t* vnew) {
+  const int b = blockIdx.x, h = blockIdx.y;
+  const int seq = seqs[b];
+  const int L = seq_length(cv, seq);
+  if (L < 0) return;
+  const int pos = L - 1;
+  const int blk = block_of(cv, seq, pos);
+  if (blk < 0) return;
+  append_row_fp8(cv, layer, b, h, blk, pos % kBlock, knew, vnew);
 }
 
 // ---------------------------------------------------------------- bulk write
@@ -356,25 +371,12 @@ __device__ __forceinline__ uint32_t int4_update(uint32_t old, int r, int r0, int
 // bulk writes above; start < 0 selects append mode: one row per sequence,
 // at position seq_len - 1, inputs [n][n_kv][d].  Every thread owns whole
 // bytes, so the two nibbles of a byte are written together.
-__global__ __launch_bounds__(256) void k_write_int4(CacheView cv, int layer, const int32_t* seqs,
-                                                    int start, int T, const uint16_t* kin,
-                                                    const uint16_t* vin) {
+// Rows [start, start + T) of batch entry b that fall in logical block lb
+// (physical block blk), kv head h; input rows are [n][T][n_kv][d].  Called
+// by whole workgroups of 256 threads.
+__device__ void int4_write_rows(const CacheView& cv, int layer, int b, int h, int blk, int lb,
+                                int start, int T, const uint16_t* kin, const uint16_t* vin) {
   __shared__ float red[2][4];
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int seq = seqs[b];
-  const int L = seq_length(cv, seq);
-  if (L < 0) return;
-  int lb;
-  if (start < 0) {
-    start = L - 1;
-    T = 1;
-    lb = start / kBlock;
-  } else {
-    if (start + T > L) return;
-    lb = start / kBlock + blockIdx.x;
-  }
-  const int blk = block_of(cv, seq, lb * kBlock);
-  if (blk < 0) return;
   const int d = cv.d, hb = d / 2;
   const int p0 = max(start, lb * kBlock), p1 = min(start + T, lb * kBlock + kBlock);
   const int r0 = p0 - lb * kBlock, nnew = p1 - p0;
@@ -441,6 +443,64 @@ __global__ __launch_bounds__(256) void k_write_int4(CacheView cv, int layer, con
     cv.ks[si] = sk;
     cv.vs[si] = sv;
   }
+}
+
+__global__ __launch_bounds__(256) void k_write_int4(CacheView cv, int layer, const int32_t* seqs,
+                                                    int start, int T, const uint16_t* kin,
+                                                    const uint16_t* vin) {
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int seq = seqs[b];
+  const int L = seq_length(cv, seq);
+  if (L < 0) return;
+  int lb;
+  if (start < 0) {
+    start = L - 1;
+    T = 1;
+    lb = start / kBlock;
+  } else {
+    if (start + T > L) return;
+    lb = start / kBlock + blockIdx.x;
+  }
+  const int blk = block_of(cv, seq, lb * kBlock);
+  if (blk < 0) return;
+  int4_write_rows(cv, layer, b, h, blk, lb, start, T, kin, vin);
+}
+
+// ---------------------------------------------------------------- grow + append
+// The grow's table and length writes, by workgroup (0, 0, 0) of a launch.
+__device__ __forceinline__ void grown_tables(const CacheView& cv, const GrownRows& g) {
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+    for (int i = threadIdx.x; i < g.nup; i += blockDim.x) table_write(cv, g.idx[i], g.val[i]);
+}
+
+// One wave per (entry, kv head), as the append above, with the row's place
+// taken from the launch.
+template <typename E>
+__global__ __launch_bounds__(64) void k_grow_append_copy(CacheView cv, int layer, GrownRows g,
+                                                         const E* knew, const E* vnew) {
+  grown_tables(cv, g);
+  const int i = blockIdx.x;
+  if (i >= g.n) return;
+  append_row_copy(cv, layer, g.first + i, blockIdx.y, g.blk[i], g.pos[i] % kBlock, knew, vnew);
+}
+
+__global__ __launch_bounds__(64) void k_grow_append_fp8(CacheView cv, int layer, GrownRows g,
+                                                        const uint16_t* knew,
+                                                        const uint16_t* vnew) {
+  grown_tables(cv, g);
+  const int i = blockIdx.x;
+  if (i >= g.n) return;
+  append_row_fp8(cv, layer, g.first + i, blockIdx.y, g.blk[i], g.pos[i] % kBlock, knew, vnew);
+}
+
+__global__ __launch_bounds__(256) void k_grow_append_int4(CacheView cv, int layer, GrownRows g,
+                                                         const uint16_t* knew,
+                                                         const uint16_t* vnew) {
+  grown_tables(cv, g);
+  const int i = blockIdx.z;
+  if (i >= g.n) return;
+  const int pos = g.pos[i];
+  int4_write_rows(cv, layer, g.first + i, blockIdx.y, g.blk[i], pos / kBlock, pos, 1, knew, vnew);
 }
 
 // Gather of an int4 cache: K and V rows [count][n_kv][d/2] bytes, codes
@@ -522,6 +582,28 @@ hipError_t launch_append(const CacheView& cv, int layer, int n, const int32_t* s
                        seqs, -1, 1, (const uint16_t*)k, (const uint16_t*)v);
     default:
       return launch_ev(k_append_fp8, grid, dim3(64), s, start, nullptr, cv, layer, seqs,
+                       (const uint16_t*)k, (const uint16_t*)v);
+  }
+}
+
+hipError_t launch_grow_append(const CacheView& cv, int layer, const GrownRows& g, const void* k,
+                              const void* v, hipStream_t s, hipEvent_t start) {
+  if (g.n <= 0 && g.nup <= 0) return hipSuccess;
+  const int n = g.n > 0 ? g.n : 1;                     // table writes alone: one workgroup row
+  dim3 grid(n, cv.n_kv);
+  switch (cv.dtype) {
+    case KVC_F32:
+      return launch_ev(k_grow_append_copy<uint32_t>, grid, dim3(64), s, start, nullptr, cv, layer,
+                       g, (const uint32_t*)k, (const uint32_t*)v);
+    case KVC_F16:
+    case KVC_BF16:
+      return launch_ev(k_grow_append_copy<uint16_t>, grid, dim3(64), s, start, nullptr, cv, layer,
+                       g, (const uint16_t*)k, (const uint16_t*)v);
+    case KVC_INT4:
+      return launch_ev(k_grow_append_int4, dim3(1, cv.n_kv, n), dim3(256), s, start, nullptr, cv,
+                       layer, g, (const uint16_t*)k, (const uint16_t*)v);
+    default:
+      return launch_ev(k_grow_append_fp8, grid, dim3(64), s, start, nullptr, cv, layer, g,
                        (const uint16_t*)k, (const uint16_t*)v);
   }
 }

@@ -111,15 +111,21 @@ uint64_t pool_bytes(const kvc_config* c) {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Collects (index, value) writes and flushes them in launches of at most
-// kTableUpdateMax entries each.
+// kTableUpdateMax entries each -- or, with a sink, only collects them for a
+// launch that carries them with other work.
 struct Uploader {
   kvc_cache* c;
   hipStream_t s;
   TableUpdate u{};
   hipError_t err = hipSuccess;
+  std::vector<std::pair<int32_t, int32_t>>* sink = nullptr;
   Uploader(kvc_cache* c_, hipStream_t s_) : c(c_), s(s_) {}
   void put(int32_t idx, int32_t val) {
     if (!c->has_dev) return;
+    if (sink) {
+      sink->emplace_back(idx, val);
+      return;
+    }
     u.idx[u.n] = idx;
     u.val[u.n] = val;
     if (++u.n == kTableUpdateMax) flush();
@@ -315,8 +321,9 @@ int kvc_seq_alloc(kvc_cache* c, int32_t seq, int32_t n_tokens, hipStream_t strea
   return up.finish();
 }
 
-int kvc_seq_grow(kvc_cache* c, int32_t n, const int32_t* seqs, hipStream_t stream) {
-  if (!c) return fail(KVC_E_INVAL, "cache is NULL");
+namespace {
+// Everything kvc_seq_grow checks before it changes any state.
+int check_grow(const kvc_cache* c, int32_t n, const int32_t* seqs) {
   if (n < 0 || (n > 0 && !seqs)) return fail(KVC_E_INVAL, "bad sequence list");
   std::vector<uint8_t> seen(c->cfg.max_seqs, 0);
   int64_t need = 0;
@@ -332,23 +339,82 @@ int kvc_seq_grow(kvc_cache* c, int32_t n, const int32_t* seqs, hipStream_t strea
     if (c->len[s] % kBlock == 0 || needs_copy(c, s)) ++need;
   }
   if (need > (int64_t)c->free_list.size()) return fail(KVC_E_NO_BLOCKS, "free list exhausted");
+  return KVC_OK;
+}
+
+// One more row for sequence s: a fresh block when the row starts one, a
+// private copy of a shared partly filled last block, then the length.
+void grow_one(kvc_cache* c, int32_t s, Copier& cp, Uploader& up) {
+  if (c->len[s] % kBlock == 0) {
+    int32_t b = take_block(c);
+    up.bt(s, (int32_t)c->table[s].size(), b);
+    c->table[s].push_back(b);
+  } else {
+    unshare_last(c, s, cp, up);
+  }
+  c->len[s] += 1;
+  up.len(s, c->len[s]);
+}
+}  // namespace
+
+int kvc_seq_grow(kvc_cache* c, int32_t n, const int32_t* seqs, hipStream_t stream) {
+  if (!c) return fail(KVC_E_INVAL, "cache is NULL");
+  int r = check_grow(c, n, seqs);
+  if (r) return r;
   Copier cp(c, stream);
   Uploader up(c, stream);
-  for (int32_t i = 0; i < n; ++i) {
-    int32_t s = seqs[i];
-    if (c->len[s] % kBlock == 0) {
-      int32_t b = take_block(c);
-      up.bt(s, (int32_t)c->table[s].size(), b);
-      c->table[s].push_back(b);
-    } else {
-      unshare_last(c, s, cp, up);
-    }
-    c->len[s] += 1;
-    up.len(s, c->len[s]);
-  }
+  for (int32_t i = 0; i < n; ++i) grow_one(c, seqs[i], cp, up);
   int rc = cp.finish();
   int ru = up.finish();
   return rc ? rc : ru;
+}
+
+int kvc_seq_grow_append(kvc_cache* c, int32_t layer, int32_t n, const int32_t* seqs,
+                        const void* k, const void* v, hipStream_t stream) {
+  if (!c) return fail(KVC_E_INVAL, "cache is NULL");
+  int r = need_dev(c);
+  if (r) return r;
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(KVC_E_STATE, "layer out of range");
+  r = check_grow(c, n, seqs);
+  if (r) return r;
+  if (n == 0) return KVC_OK;
+  if (!k || !v) return fail(KVC_E_INVAL, "NULL device pointer");
+  // Bookkeeping first, exactly as kvc_seq_grow; the table and length writes
+  // are kept to ride with the appends.  Copy-on-write block copies are
+  // launched before them, so the appended rows land on the copies.
+  Copier cp(c, stream);
+  Uploader up(c, stream);
+  std::vector<std::pair<int32_t, int32_t>> writes;
+  writes.reserve(2 * (size_t)n);
+  up.sink = &writes;
+  std::vector<int32_t> wend(n);                        // writes made up to entry i
+  for (int32_t i = 0; i < n; ++i) {
+    grow_one(c, seqs[i], cp, up);
+    wend[i] = (int32_t)writes.size();
+  }
+  int rc = cp.finish();
+  if (rc) return rc;
+  hipError_t e = hipSuccess;
+  const CacheView cv = c->view();
+  for (int32_t i0 = 0; i0 < n && e == hipSuccess; i0 += kGrowAppendMax) {
+    const int32_t m = std::min<int32_t>(kGrowAppendMax, n - i0);
+    GrownRows g{};
+    g.n = m;
+    g.first = i0;
+    const int32_t w0 = i0 == 0 ? 0 : wend[i0 - 1], w1 = wend[i0 + m - 1];
+    g.nup = w1 - w0;                                   // at most two per entry
+    for (int32_t j = 0; j < g.nup; ++j) {
+      g.idx[j] = writes[w0 + j].first;
+      g.val[j] = writes[w0 + j].second;
+    }
+    for (int32_t j = 0; j < m; ++j) {
+      const int32_t s = seqs[i0 + j], pos = c->len[s] - 1;
+      g.pos[j] = pos;
+      g.blk[j] = c->table[s][pos / kBlock];
+    }
+    e = launch_grow_append(cv, layer, g, k, v, stream);
+  }
+  return e == hipSuccess ? KVC_OK : hip_fail(e, "grow + append launch");
 }
 
 int kvc_seq_grow_by(kvc_cache* c, int32_t seq, int32_t n_tokens, hipStream_t stream) {

@@ -36,6 +36,22 @@ struct TableUpdate {
   int32_t val[kTableUpdateMax];
 };
 
+// One launch of a grow followed by the append of the grown rows.  The host's
+// block manager has just placed each entry's new row, so the launch carries
+// where it goes (its position in the sequence and the block holding it); the
+// kernel reads no table or length for it.  The grow's table and length writes
+// (TableUpdate form, at most two per entry) ride in the same launch.
+constexpr int kGrowAppendMax = 96;
+struct GrownRows {
+  int32_t n;                        // entries in this launch
+  int32_t first;                    // batch index of entry 0 (its row in k_new / v_new)
+  int32_t nup;                      // table / length writes
+  int32_t pos[kGrowAppendMax];      // position of the entry's new row
+  int32_t blk[kGrowAppendMax];      // block holding that position
+  int32_t idx[2 * kGrowAppendMax];  // as TableUpdate
+  int32_t val[2 * kGrowAppendMax];
+};
+
 // Copy-on-write block copies: block src -> dst, every layer, K and V slabs of
 // all kv heads and (fp8, int4) their scales.
 constexpr int kCopyMax = 120;
@@ -121,6 +137,8 @@ hipError_t launch_copy_blocks(const CacheView& cv, const BlockCopy& u, hipStream
 hipError_t launch_append(const CacheView& cv, int layer, int n, const int32_t* seqs,
                          const void* k, const void* v, hipStream_t s,
                          hipEvent_t start = nullptr);
+hipError_t launch_grow_append(const CacheView& cv, int layer, const GrownRows& g, const void* k,
+                              const void* v, hipStream_t s, hipEvent_t start = nullptr);
 hipError_t launch_write(const CacheView& cv, int layer, int n, const int32_t* seqs, int start,
                         int T, const void* k, const void* v, hipStream_t s);
 hipError_t launch_gather(const CacheView& cv, int layer, int seq, int start, int count,

@@ -80,11 +80,14 @@ def test_llama8b_decode_full_all_outputs():
     print(f"llama8b decode: worst abs {worst[0]:.2e} rel {worst[1]:.2e}")
 
 
-def test_llama8b_append_decode_full_all_outputs():
-    """The bench's step at full size: rows 0..L-2 written in bulk, a grow,
-    then kvc_attn_decode_append with row L-1 (appended inside the decode
-    kernel); every output against the oracle, and the appended rows read
-    back through the gather bit for bit."""
+@pytest.mark.parametrize("form", ["decode_append", "grow_append"])
+def test_llama8b_append_decode_full_all_outputs(form):
+    """The decode step at full size: rows 0..L-2 written in bulk, then row
+    L-1 added and attended -- either a grow followed by
+    kvc_attn_decode_append, or kvc_seq_grow_append (grow and append in one
+    launch, the bench's step) followed by kvc_attn_decode.  Every output
+    against the oracle, and the appended rows read back through the gather
+    bit for bit."""
     w = decode_workload("llama8b_decode")
     io = torch.bfloat16
     max_bps = int(w.blocks_per_seq.max()) + 1
@@ -101,16 +104,20 @@ def test_llama8b_append_decode_full_all_outputs():
                     torch.from_numpy(v[:L - 1]).to(io).cuda()[None])
         last_k.append(torch.from_numpy(k[L - 1]).to(io).cuda())
         last_v.append(torch.from_numpy(v[L - 1]).to(io).cuda())
-    c.seq_grow(list(range(w.batch)))
     seqs = torch.arange(w.batch, dtype=torch.int32, device="cuda")
     kn, vn = torch.stack(last_k).contiguous(), torch.stack(last_v).contiguous()
     q = torch.from_numpy(w.q()).to(io).cuda()
-    y = f64(c.attn_decode_append(0, seqs, kn, vn, q))
+    if form == "decode_append":
+        c.seq_grow(list(range(w.batch)))
+        y = f64(c.attn_decode_append(0, seqs, kn, vn, q))
+    else:
+        c.seq_grow_append(0, list(range(w.batch)), kn, vn)
+        y = f64(c.attn_decode(0, seqs, q))
     scale = 1 / math.sqrt(w.d)
     qd = f64(q)
     for b in range(w.batch):
         K, V = source_rows(w, b, io)
-        assert_close(y[b], A.decode_attention(qd[b], K, V, scale), what=f"seq {b}")
+        assert_close(y[b], A.decode_attention(qd[b], K, V, scale), what=f"{form}, seq {b}")
         L = int(w.lengths[b])
         gk, gv = c.gather(0, b, L - 1, 1)
         assert torch.equal(gk[0].view(torch.int16), kn[b].view(torch.int16))
