@@ -35,7 +35,9 @@ Infinity Cache.  Prefill and extend: the attention kernel.  Beside it,
 `roofline.call` gives the whole library call: for decode the work-list
 kernel, the merge and the gap between them (first kernel start to last
 kernel end) and the same calls timed by stream markers; for prefill and
-extend the stream-marker time of the timed calls.  `traffic` is the HBM
+extend the stream-marker time of up to 10 single calls after the timed ones.
+The K timed steps carry no markers of their own (a marker in the stream
+leaves a gap beside the kernels it brackets).  `traffic` is the HBM
 bytes per launch of the dominant kernel (in `call`: of every kernel of the
 call) that rocprofv3's
 FETCH_SIZE / WRITE_SIZE counters recorded (profiles/counters.json, scaled by
@@ -165,13 +167,16 @@ def drop_rows(tag):
         del _ROWS[key]
 
 
-def build_decode(name, torch, kv):
+def build_decode(name, torch, kv, grow=112):
+    """The workload's cache, with room for every sequence to grow by `grow`
+    more tokens."""
     from workloads import decode_workload
     w = decode_workload(name)
     dt = {"bf16": "bf16", "fp16": "f16", "fp8": "fp8", "int4": "int4"}[w.kv_dtype]
     io = kv.IO_TORCH[dt]
-    spare = w.batch * 8                                     # room to grow during the run
-    max_bps = int(w.blocks_per_seq.max()) + 8
+    room = -(-grow // 16) + 1                              # blocks per sequence to grow into
+    spare = w.batch * room
+    max_bps = int(w.blocks_per_seq.max()) + room
     c = kv.KvCache(1, w.n_q, w.n_kv, w.d, w.n_blocks + spare, w.batch, max_bps, dt)
     tables = w.block_tables()
     for b in range(w.batch):
@@ -312,7 +317,8 @@ def bench_decode(name, steps, warmup, torch, kv, with_cpu):
     kvc_attn_decode; `value` is the decode's algorithmic bytes per step over
     the wall-clock time of the K steps.  The roofline times kvc_attn_decode
     alone after an Infinity-Cache eviction."""
-    w, c, io = build_decode(name, torch, kv)
+    diag = min(steps, 10)                                  # steps timed one by one, after
+    w, c, io = build_decode(name, torch, kv, grow=warmup + steps + diag)
     kv_elem = KV_ELEM_BYTES[w.kv_dtype]
     seqs_host = list(range(w.batch))
     seqs = torch.arange(w.batch, dtype=torch.int32, device="cuda")
@@ -345,19 +351,24 @@ def bench_decode(name, steps, warmup, torch, kv, with_cpu):
         step()
     torch.cuda.synchronize()
     lens0 = np.array([c.seq_len(b) for b in range(w.batch)])
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(events[i])
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # algorithmic bytes of each timed decode: lengths lens0+1 .. lens0+steps
     total_bytes = sum(decode_bytes(w, lens0 + i + 1, kv_elem) for i in range(steps))
+    # device time of single steps, outside the timed region: event records in
+    # the stream leave gaps of their own between the steps they bracket
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(diag)]
+    for i in range(diag):
+        step(events[i])
+    torch.cuda.synchronize()
     warm_avg_s = float(np.mean([a.elapsed_time(b) for a, b in events])) / 1e3
-    # roofline: the same decode call (state after the timed steps), cold
-    lens1 = lens0 + steps
+    # roofline: the same decode call (state after those steps), cold
+    lens1 = lens0 + steps + diag
     per_call = decode_bytes(w, lens1, kv_elem)
     kern_s, call_s, mark_s = evict_and_time(call, steps, torch, c)
     res = {
@@ -460,16 +471,21 @@ def bench_prefill(steps, warmup, torch, kv, with_cpu, small=False):
     for _ in range(warmup):
         c.attn_prefill(0, q, k, v, seqs=seqs, out=out)
     warm_up_clocks(lambda: c.attn_prefill(0, q, k, v, seqs=seqs, out=out), torch)
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        events[i][0].record(stream)
         c.attn_prefill(0, q, k, v, seqs=seqs, out=out)
-        events[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     flops = prefill_flops(w.batch, w.T, w.n_q, w.d)
+    # stream markers around single calls, outside the timed region
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(min(steps, 10))]
+    for e0, e1 in events:
+        e0.record(stream)
+        c.attn_prefill(0, q, k, v, seqs=seqs, out=out)
+        e1.record(stream)
+    torch.cuda.synchronize()
     call_s = float(np.mean([a.elapsed_time(b) for a, b in events])) / 1e3
     kern_s = dispatch_time(lambda: c.attn_prefill(0, q, k, v, seqs=seqs, out=out), steps, torch, c)
     achieved = flops / kern_s / 1e12
@@ -566,14 +582,19 @@ def bench_extend(steps, warmup, torch, kv, with_cpu):
     for _ in range(warmup):
         step()
     warm_up_clocks(step, torch)
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(events[i])
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     flops = extend_flops(w.batch, ctx, EXTEND_CHUNK, w.n_q, w.d)
+    # stream markers around single calls, outside the timed region
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(min(steps, 10))]
+    for ev in events:
+        step(ev)
+    torch.cuda.synchronize()
     call_s = float(np.mean([a.elapsed_time(b) for a, b in events])) / 1e3
 
     def step_timed():
