@@ -279,6 +279,9 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
   __shared__ int64_t s_units[kMaxBatch + 1];
   __shared__ int32_t s_counts[kMaxBatch];
   __shared__ int32_t s_seq[kMaxBatch], s_len[kMaxBatch];   // each entry's sequence and length
+  // batches of at most 64 entries: each wave's own copy of the four arrays
+  __shared__ int64_t w_units[4][65];
+  __shared__ int32_t w_counts[4][64], w_seq[4][64], w_len[4][64];
   __shared__ int64_t s_wsum[4];
   constexpr int kLenCache = 4096;
   __shared__ int32_t s_lenall[kLenCache];               // every sequence's length (small caches)
@@ -291,16 +294,25 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
 
   // ---- unit counts and their prefix sums: up to 8 contiguous entries per
   // thread (nb <= 2048), one per thread when nb <= 256 so that no wave works
-  // through the entries alone.  The batch's sequence ids and, when the cache
-  // has at most kLenCache sequences, all of their lengths are loaded
-  // together, so the lengths do not wait for the ids.
+  // through the entries alone.  Batches of at most 64 entries are scanned by
+  // every wave on its own (lane b: entry b) into its own copy of the arrays,
+  // which takes no barrier after the lengths are in.  The batch's sequence
+  // ids and, when the cache has at most kLenCache sequences, all of their
+  // lengths are loaded together, so the lengths do not wait for the ids.
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool small = nb <= 64;                           // the same for every wave
+  int64_t* const su = small ? w_units[wv] : s_units;
+  int32_t* const sc = small ? w_counts[wv] : s_counts;
+  int32_t* const ss = small ? w_seq[wv] : s_seq;
+  int32_t* const sl = small ? w_len[wv] : s_len;
   {
     const bool lens_in_lds = cv.max_seqs <= kLenCache;
     const int per = nb <= 256 ? 1 : 8;                   // wave-uniform
+    const int first = small ? lane : tid * per;          // this thread's first entry
     int sqv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int b = tid * per + i;
+      const int b = first + i;
       sqv[i] = i < per && b < nb ? seqs[b] : -1;
     }
     if (lens_in_lds)
@@ -313,7 +325,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
       lv[i] = lens_in_lds ? s_lenall[sqv[i] >= 0 && sqv[i] < cv.max_seqs ? sqv[i] : 0] : 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int b = tid * per + i;
+      const int b = first + i;
       int c = 0;
       if (i < per && b < nb) {
         const int sq = sqv[i];
@@ -325,9 +337,9 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
           L = valid_len(cv, sq);
         }
         c = L > 0 ? UnitMap(L, window, sinks).count : 0;
-        s_counts[b] = c;
-        s_seq[b] = sq;
-        s_len[b] = L;
+        sc[b] = c;
+        ss[b] = sq;
+        sl[b] = L;
       }
       loc[i] = (int64_t)c * nkvg;
       tsum += loc[i];
@@ -351,31 +363,46 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
         if (lane >= o) x += y;
       }
     }
-    if (lane == 63) s_wsum[tid >> 6] = x;
-    __syncthreads();
-    int64_t ex = x - tsum;
-    for (int i = 0; i < (tid >> 6); ++i) ex += s_wsum[i];
+    if (small) {
+      // lanes nb.. hold no units: lane 63 holds the batch's total
+      const int64_t ex = x - tsum;
+      const int64_t total = uni64(__shfl(x, 63, 64));
+      if (lane < nb) su[lane] = ex;
+      if (lane == 0) su[nb] = total;
+      if (blockIdx.x == 0 && wv == 0) {
+        if (lane < nb) {
+          W_.units[lane] = ex;
+          W_.counts[lane] = sc[lane];
+        }
+        if (lane == 0) W_.units[nb] = total;
+      }
+    } else {
+      if (lane == 63) s_wsum[tid >> 6] = x;
+      __syncthreads();
+      int64_t ex = x - tsum;
+      for (int i = 0; i < (tid >> 6); ++i) ex += s_wsum[i];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int b = tid * per + i;
-      if (i < per && b < nb) s_units[b] = ex;
-      ex += loc[i];
-    }
-    if (tid == 0) s_units[nb] = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
-    __syncthreads();
-    if (blockIdx.x == 0) {
-      for (int b = tid; b <= nb; b += 256) W_.units[b] = s_units[b];
-      for (int b = tid; b < nb; b += 256) W_.counts[b] = s_counts[b];
+      for (int i = 0; i < 8; ++i) {
+        const int b = tid * per + i;
+        if (i < per && b < nb) s_units[b] = ex;
+        ex += loc[i];
+      }
+      if (tid == 0) s_units[nb] = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+      __syncthreads();
+      if (blockIdx.x == 0) {
+        for (int b = tid; b <= nb; b += 256) W_.units[b] = s_units[b];
+        for (int b = tid; b < nb; b += 256) W_.counts[b] = s_counts[b];
+      }
     }
   }
 
-  const int gw = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t Wt = s_units[nb];
+  const int gw = blockIdx.x * 4 + wv;
+  const int64_t Wt = su[nb];
   if (gw >= waves || Wt == 0) return;
   int64_t u = share(gw, Wt, waves);
   const int64_t u1 = share(gw + 1, Wt, waves);
 
-  // entry holding unit u: the last b with s_units[b] <= u (entries without
+  // entry holding unit u: the last b with su[b] <= u (entries without
   // units share their offset with the next entry and are skipped this way).
   // The offsets do not decrease, so the entries at or below u are a prefix:
   // count them 64 at a time with one LDS read and a ballot per chunk.
@@ -384,11 +411,11 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
     int k = 0;
     for (int c0 = 0; c0 < nb; c0 += 64) {              // wave-uniform
       const int e = c0 + lane;
-      const uint64_t m = __builtin_amdgcn_ballot_w64(e < nb && s_units[e < nb ? e : 0] <= u);
+      const uint64_t m = __builtin_amdgcn_ballot_w64(e < nb && su[e < nb ? e : 0] <= u);
       k += __builtin_popcountll(m);
       if (m != ~0ull) break;
     }
-    b = uni(k - 1);                                     // s_units[0] = 0 <= u: k >= 1
+    b = uni(k - 1);                                     // su[0] = 0 <= u: k >= 1
   }
 
   const uint8_t* kpool = (const uint8_t*)cv.k;
@@ -396,9 +423,9 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
   const int64_t layer_blocks = (int64_t)layer * cv.n_blocks;
 
   while (u < u1) {
-    while (uni64(s_units[b + 1]) <= u) ++b;           // skip to the entry holding u
-    const int cb = uni(s_counts[b]);
-    const int64_t sb = uni64(s_units[b]);
+    while (uni64(su[b + 1]) <= u) ++b;                // skip to the entry holding u
+    const int cb = uni(sc[b]);
+    const int64_t sb = uni64(su[b]);
     const int64_t rem = u - sb;
     int kvg, c0;
     if ((rem >> 31) == 0) {                             // the common sizes: 32-bit division
@@ -412,8 +439,8 @@ __global__ __launch_bounds__(256, 2) void k_decode_work(CacheView cv, int layer,
     const int64_t pend = u1 < segend ? u1 : segend;
     const int c1 = c0 + (int)(pend - u);
     const int kvh = kvg / qgroups, qg = kvg % qgroups;
-    const int seq = uni(s_seq[b]);
-    const int L = uni(s_len[b]);                       // > 0: the entry has units
+    const int seq = uni(ss[b]);
+    const int L = uni(sl[b]);                          // > 0: the entry has units
     const UnitMap umap(L, window, sinks);
     // Query operand (B of S^T = K Q^T): column r16 = query row qg*16 + r16,
     // loaded after the piece's first block-table load (below).
