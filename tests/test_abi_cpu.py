@@ -217,6 +217,11 @@ def test_host_only_handle_refuses_device_calls():
     rc = L.kvc_attn_decode_noalloc(c._h, 0, 1, ctypes.c_void_p(16), ctypes.c_void_p(16),
                                    ctypes.c_void_p(16), ctypes.c_float(1.0), 0, None)
     assert rc == kv.KVC_E_STATE
+    # grow + append in one launch: refused before any bookkeeping changes
+    ids = (ctypes.c_int32 * 1)(0)
+    rc = L.kvc_seq_grow_append(c._h, 0, 1, ids, ctypes.c_void_p(16), ctypes.c_void_p(16), None)
+    assert rc == kv.KVC_E_STATE
+    assert c.seq_len(0) == 4
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.125, float("nan"), float("inf")])
