@@ -13,13 +13,17 @@
 // The score tile never leaves registers; only O / l is written.
 //
 // Two wave groups per SIMD, offset by half a tile ("ping-pong").  Waves w and
-// w+4 share a SIMD.  The kernel runs in slots separated by workgroup
-// barriers; in each slot one group issues its matrix-core work (the PV
-// product of tile i-1, S of tile i, and the short VALU work that needs S:
-// row max and rescale) while the other group computes the exponentials of
-// its last score tile and stages the next K or V tile into LDS.  The matrix
-// core of each SIMD stays busy while the VALU serves the other wave.  Group 1 stages K tiles, group 0 stages V tiles, each in
-// its own exponent slot, through registers (loads issued two slots ahead).
+// w+4 share a SIMD.  The kernel runs in slots of half a tile; in each slot
+// one group issues its matrix-core work (the PV product of tile i-1, S of
+// tile i, and the short VALU work that needs S: row max and rescale) while
+// the other group computes the exponentials of its last score tile and
+// stages the next K or V tile into LDS.  The matrix core of each SIMD stays
+// busy while the VALU serves the other wave.  Group 1 stages K tiles, group
+// 0 stages V tiles, each in its own exponent slot, through registers (loads
+// issued two slots ahead).  Every LDS write and the reads it must follow or
+// precede lie on either side of the barrier at the end of every second
+// slot, so whole-prompt tiles take that one barrier per tile; paged tiles
+// keep a barrier at the end of every slot, which measured faster there.
 //
 // Running max.  The rescale factor exp(m_old - m_new) is applied only when
 // the row max has grown by more than 8 (base-2 units) since the last
@@ -626,13 +630,18 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
   // more slots later.  Loads are issued two slots before their LDS write.
   // The matrix phase runs at a raised wave priority: its MFMAs issue first
   // and the other wave's VALU work fills the remaining issue cycles.
+  // Whole prompts: one barrier per tile (every LDS write and read it orders
+  // lies on either side of the barrier that ends a group's matrix phase for
+  // group 1 and its exponent phase for group 0); the groups offset each
+  // other by half a tile.  Paged tiles: a barrier after each phase.
+  constexpr bool ONE = !PAGED;
   if (grp == 1) {
     if (1 < nkt) {
       if (2 < nkt) ktab(2);
       store_k(1);
       if (2 < nkt) load_k(2);
     }
-    __syncthreads();
+    if (!ONE) __syncthreads();
   }
   for (int i = 0; i <= nkt; ++i) {
     __builtin_amdgcn_sched_barrier(0);
@@ -644,7 +653,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
     }
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
-    __syncthreads();
+    if (!ONE || grp == 1) __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     // staging first: its LDS writes drain while the exponentials run
     if (grp == 1) {
@@ -660,9 +669,9 @@ __global__ __launch_bounds__(512, 1) void k_prefill_mfma(int n_q, int n_kv, int 
     }
     if (need(i)) expo(i);
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+    if (!ONE || grp == 0) __syncthreads();
   }
-  if (grp == 0) __syncthreads();                     // same barrier count for both groups
+  if (!ONE && grp == 0) __syncthreads();             // same barrier count for both groups
 
   // ---- epilogue: O / l for this lane's query column
   if (rq0 >= T || qrow >= T) return;
