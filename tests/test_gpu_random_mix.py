@@ -85,7 +85,7 @@ def _draw_decode(seed):
     return rng, dtype, d, n_kv * G, n_kv, lengths, window, sinks, splits
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(128))
 def test_random_decode(seed):
     rng, dtype, d, n_q, n_kv, lengths, window, sinks, splits = _draw_decode(seed)
     what = (f"seed {seed}: {dtype} d={d} n_q={n_q} n_kv={n_kv} lengths={lengths} "
@@ -104,7 +104,7 @@ def test_random_decode(seed):
         assert_close(f64(out[b]), ref, io=io, what=f"{what}, sequence {b}")
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(32))
 def test_random_prefill_writes_and_attends(seed):
     rng = np.random.default_rng([202, seed])
     dtype = ("bf16", "f16")[seed % 2]
@@ -138,7 +138,7 @@ def test_random_prefill_writes_and_attends(seed):
             f"{what}: cache rows of sequence {s}"
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(32))
 def test_random_extend(seed):
     rng = np.random.default_rng([303, seed])
     dtype = DTYPES[seed % 4]
