@@ -42,12 +42,14 @@ def test_decode_more_than_2048_sequences():
     assert b.pools_equal()
 
 
-@pytest.mark.parametrize("batch", [64, 65, 256, 257, 700])
+@pytest.mark.parametrize("batch", [1, 64, 65, 256, 257, 700, 2048 + 40])
 def test_decode_batches_around_the_prologue_layouts(batch):
-    """The work list's prologue gives each thread one batch entry up to 256
-    entries and eight contiguous ones above; the wave's first entry is found
-    64 entries at a time.  Every row against the oracle on both sides of
-    those edges."""
+    """The work list's prologue lets every wave scan a batch of up to 64
+    entries on its own, gives each thread one batch entry up to 256 entries
+    and eight contiguous ones above; the wave's first entry is found 64
+    entries at a time; 2,088 sequences run as a 2,048-entry sub-batch and a
+    40-entry one.  Every row against the oracle on both sides of those
+    edges."""
     print(f"batch {batch}", flush=True)
     w = DecodeWorkload(f"edge{batch}", batch, 8, 2, 64, "bf16", (1, 200))
     b = Built(w)
