@@ -1,8 +1,8 @@
 """CPU oracle for paged-KV-cache causal attention.
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the library's product path may import,
-call, link or execute anything in this package: only the tests, the graft
-entry point's smoke check and the bench's CPU-baseline leg use it.  It shares
+call, link or execute anything in this package: only the tests,
+``__graft_entry__.smoke()`` and the bench's CPU-baseline leg use it.  It shares
 no code with the HIP library (no kernels, headers, helpers, tables or
 constant generators) and imports nothing from it.
 
